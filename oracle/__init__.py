@@ -1,0 +1,195 @@
+"""fp64 CPU oracle for the fused softmax / LayerNorm row reductions.
+
+TEST INFRASTRUCTURE ONLY. The product package (``layernorm_reduction_amd``) never imports
+this module. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may use it. It shares no code with the HIP path.
+
+The arithmetic lives in ``lnr_oracle.c`` (plain loops, double precision, two-pass
+statistics). This wrapper only converts numpy arrays: every input is widened to float64,
+which is exact for values stored as fp16 or fp32, and every output is float64, never
+rounded to a storage type.
+
+Citations (page titles and sections; see ``lnr_oracle.c`` for the formulas):
+  * softmax forward: "CMU 11-868 HW4: Softmax and LayerNorm as fused CUDA kernels",
+    "Problem structure and scoring" (attention mask added, future tokens set to -inf,
+    a max then a sum of exponentials) and "Faster than what?" (softmax(inp + mask));
+    "CMU 11-868 L10 ...", "Technique 2" (two reductions).
+  * softmax backward: named in the HW4 page's table; formula = textbook softmax Jacobian.
+  * LayerNorm forward/backward: L10 "Technique 2" (mu(x), mu(x^2); the two backward sums),
+    HW4 "Problem structure and scoring" (eps = 1e-8 inside the root; dgamma/dbeta summed
+    across rows).
+  * RMSNorm: "FastTransformer: Breaking the Compiler Ceiling ...", section 5.4.
+
+Every function is pinned by tests in ``tests/test_oracle_*.py`` against closed forms,
+invariants, finite differences and independent fp64 library routines.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblnr_oracle.so")
+SRC_PATH = os.path.join(_HERE, "lnr_oracle.c")
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile lnr_oracle.c with gcc (IEEE double, no FMA contraction, OpenMP)."""
+    import subprocess
+
+    cmd = [
+        "gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+        "-ffp-contract=off", "-fno-fast-math", "-fvisibility=hidden",
+        SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    d = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.lnr_oracle_softmax_fw.argtypes = [d, d, i64, i64, i64, i64, ctypes.c_int, d]
+    lib.lnr_oracle_softmax_fw_rows.argtypes = [d, d, ctypes.POINTER(i64), i64, i64, ctypes.c_int, d]
+    lib.lnr_oracle_softmax_bw.argtypes = [d, d, i64, i64, d]
+    lib.lnr_oracle_layernorm_fw.argtypes = [d, d, d, i64, i64, ctypes.c_double, d, d, d]
+    lib.lnr_oracle_layernorm_bw_dx.argtypes = [d, d, d, i64, i64, ctypes.c_double, d]
+    lib.lnr_oracle_layernorm_bw_dgamma_dbeta.argtypes = [d, d, i64, i64, ctypes.c_double, d, d, d, d]
+    lib.lnr_oracle_rmsnorm_fw.argtypes = [d, d, i64, i64, ctypes.c_double, d, d]
+    lib.lnr_oracle_rmsnorm_bw.argtypes = [d, d, d, i64, i64, ctypes.c_double, d, d]
+    for f in (lib.lnr_oracle_softmax_fw, lib.lnr_oracle_softmax_fw_rows, lib.lnr_oracle_softmax_bw,
+              lib.lnr_oracle_layernorm_fw, lib.lnr_oracle_layernorm_bw_dx,
+              lib.lnr_oracle_layernorm_bw_dgamma_dbeta, lib.lnr_oracle_rmsnorm_fw,
+              lib.lnr_oracle_rmsnorm_bw):
+        f.restype = None
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    """Widen to a C-contiguous float64 array (exact for fp16 / fp32 stored values)."""
+    if hasattr(a, "detach"):  # a CPU torch tensor
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def softmax_fw(x, mask=None, causal: bool = False) -> np.ndarray:
+    """x: [B, H, Tq, Tk]; mask: additive [B, Tk] or None. Returns y as float64."""
+    x = _f64(x)
+    B, H, Tq, Tk = x.shape
+    if causal and Tq != Tk:
+        raise ValueError("causal softmax needs Tq == Tk")
+    m = None if mask is None else _f64(mask).reshape(B, Tk)
+    y = np.empty_like(x)
+    _load().lnr_oracle_softmax_fw(_p(x), _p(m), B, H, Tq, Tk, int(bool(causal)), _p(y))
+    return y
+
+
+def softmax_fw_rows(x_rows, mask_rows, qidx, causal: bool = False) -> np.ndarray:
+    """Selected rows: x_rows [n, Tk]; mask_rows [n, Tk] or None; qidx [n] query positions."""
+    x = _f64(x_rows)
+    n, Tk = x.shape
+    m = None if mask_rows is None else _f64(mask_rows).reshape(n, Tk)
+    q = np.ascontiguousarray(np.asarray(qidx, dtype=np.int64).reshape(n))
+    y = np.empty_like(x)
+    _load().lnr_oracle_softmax_fw_rows(
+        _p(x), _p(m), q.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, Tk,
+        int(bool(causal)), _p(y))
+    return y
+
+
+def softmax_bw(y, dy) -> np.ndarray:
+    """y, dy: [..., Tk] (y = forward output). Returns dx as float64 with the same shape."""
+    y = _f64(y)
+    dy = _f64(dy)
+    if y.shape != dy.shape:
+        raise ValueError("y and dy shapes differ")
+    Tk = y.shape[-1]
+    rows = y.size // Tk if Tk else 0
+    dx = np.empty_like(y)
+    _load().lnr_oracle_softmax_bw(_p(y), _p(dy), rows, Tk, _p(dx))
+    return dx
+
+
+def layernorm_fw(x, gamma, beta, eps: float = 1e-8):
+    """x: [N, C]; gamma, beta: [C]. Returns (y, mean, rstd) as float64."""
+    x = _f64(x)
+    N, C = x.shape
+    g = _f64(gamma).reshape(C)
+    b = _f64(beta).reshape(C)
+    y = np.empty_like(x)
+    mean = np.empty(N, np.float64)
+    rstd = np.empty(N, np.float64)
+    _load().lnr_oracle_layernorm_fw(_p(x), _p(g), _p(b), N, C, float(eps), _p(y), _p(mean), _p(rstd))
+    return y, mean, rstd
+
+
+def layernorm_bw_dx(x, dy, gamma, eps: float = 1e-8) -> np.ndarray:
+    x = _f64(x)
+    dy = _f64(dy)
+    N, C = x.shape
+    g = _f64(gamma).reshape(C)
+    dx = np.empty_like(x)
+    _load().lnr_oracle_layernorm_bw_dx(_p(x), _p(dy), _p(g), N, C, float(eps), _p(dx))
+    return dx
+
+
+def layernorm_bw_dgamma_dbeta(x, dy, eps: float = 1e-8):
+    x = _f64(x)
+    dy = _f64(dy)
+    N, C = x.shape
+    mu = np.empty(N, np.float64)
+    sg = np.empty(N, np.float64)
+    dg = np.empty(C, np.float64)
+    db = np.empty(C, np.float64)
+    _load().lnr_oracle_layernorm_bw_dgamma_dbeta(_p(x), _p(dy), N, C, float(eps), _p(mu), _p(sg), _p(dg), _p(db))
+    return dg, db
+
+
+def layernorm_bw(x, dy, gamma, eps: float = 1e-8):
+    """Returns (dx, dgamma, dbeta) as float64."""
+    dx = layernorm_bw_dx(x, dy, gamma, eps)
+    dg, db = layernorm_bw_dgamma_dbeta(x, dy, eps)
+    return dx, dg, db
+
+
+def rmsnorm_fw(x, gamma, eps: float = 1e-6):
+    """Returns (y, rrms) as float64."""
+    x = _f64(x)
+    N, C = x.shape
+    g = _f64(gamma).reshape(C)
+    y = np.empty_like(x)
+    r = np.empty(N, np.float64)
+    _load().lnr_oracle_rmsnorm_fw(_p(x), _p(g), N, C, float(eps), _p(y), _p(r))
+    return y, r
+
+
+def rmsnorm_bw(x, dy, gamma, eps: float = 1e-6):
+    """Returns (dx, dgamma) as float64."""
+    x = _f64(x)
+    dy = _f64(dy)
+    N, C = x.shape
+    g = _f64(gamma).reshape(C)
+    dx = np.empty_like(x)
+    dg = np.empty(C, np.float64)
+    _load().lnr_oracle_rmsnorm_bw(_p(x), _p(dy), _p(g), N, C, float(eps), _p(dx), _p(dg))
+    return dx, dg

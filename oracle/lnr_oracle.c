@@ -1,0 +1,291 @@
+/*
+ * lnr_oracle.c -- fp64 CPU oracle for masked/causal attention softmax and LayerNorm,
+ * forward and backward.
+ *
+ * TEST INFRASTRUCTURE ONLY. The product library never links, loads or calls this file.
+ * Only the test suite, the smoke check and the CPU-baseline leg of the benchmark use it,
+ * through oracle/__init__.py.
+ *
+ * Every function below is the plain textbook definition written with ordinary loops:
+ *   - all arithmetic and all accumulation in double precision;
+ *   - two-pass statistics (mean first, then the centred second moment), NOT the one-pass
+ *     rewrite that the GPU kernels use, so the rewrite itself is under test;
+ *   - inputs are double arrays holding the stored values exactly (fp16 and fp32 both widen
+ *     to double without rounding); outputs are double and never rounded to a storage type.
+ * OpenMP spreads independent rows (or independent column blocks) over threads. Each output
+ * element is still produced by one thread summing in the natural index order, so the thread
+ * count never changes a result.
+ *
+ * Sources (the pages this oracle follows):
+ *   [L10]  "CMU 11-868 L10: Accelerating Transformers on GPUs, and Where LightSeq Finds the
+ *          Time", section "Technique 2: rewrite the formula, drop a synchronization".
+ *   [HW4]  "CMU 11-868 HW4: Softmax and LayerNorm as fused CUDA kernels", section
+ *          "Problem structure and scoring" (softmax with attention mask and future-token
+ *          mask; LayerNorm with epsilon inside the square root; LayerNorm backward as dinp
+ *          plus dgamma/dbeta summed across rows) and section "Faster than what?" (the
+ *          softmax(inp + mask) baseline, i.e. an additive mask).
+ *   [FT]   "FastTransformer: Breaking the Compiler Ceiling via Architectural Co-Design",
+ *          section 5.4 "Vectorized Pre-RMSNorm" (RMSNorm: no mean, one sum of squares).
+ * The softmax backward formula is never printed on the pages; it is the textbook Jacobian
+ * of softmax (diag(y) - y y^T) applied to dy, and it is pinned by finite differences.
+ */
+#include <math.h>
+#include <stdint.h>
+
+#define ORACLE_API __attribute__((visibility("default")))
+
+/* ---------------------------------------------------------------------------------------
+ * Attention softmax, forward. [HW4 "Problem structure and scoring"; L10 "Technique 2"]
+ * One row r = (b, h, i) of the score tensor [B, H, Tq, Tk]:
+ *   z_j = x_j + m_j           (additive attention mask, key-padding positions hold -inf)
+ *   z_j = -inf  for j > i     (future tokens, when causal)
+ *   M   = max_j z_j           (the first reduction: keeps exp from overflowing)
+ *   e_j = exp(z_j - M),  S = sum_j e_j   (the second reduction)
+ *   y_j = e_j / S
+ * A row whose every position is masked (M = -inf) has no defined softmax; this oracle
+ * returns zeros for it (the reading taken where the pages are silent).
+ * ------------------------------------------------------------------------------------- */
+static double masked_score(const double *x, const double *mrow, int64_t j, int64_t qi,
+                           int causal)
+{
+    if (causal && j > qi)
+        return -INFINITY;
+    double z = x[j];
+    if (mrow)
+        z += mrow[j];
+    return z;
+}
+
+static void softmax_fw_row(const double *x, const double *mrow, int64_t Tk, int64_t qi,
+                           int causal, double *y)
+{
+    double M = -INFINITY;
+    for (int64_t j = 0; j < Tk; ++j) {
+        double z = masked_score(x, mrow, j, qi, causal);
+        if (z > M)
+            M = z;
+    }
+    if (M == -INFINITY) {
+        for (int64_t j = 0; j < Tk; ++j)
+            y[j] = 0.0;
+        return;
+    }
+    double S = 0.0;
+    for (int64_t j = 0; j < Tk; ++j) {
+        double z = masked_score(x, mrow, j, qi, causal);
+        double e = (z == -INFINITY) ? 0.0 : exp(z - M);
+        y[j] = e;
+        S += e;
+    }
+    for (int64_t j = 0; j < Tk; ++j)
+        y[j] = y[j] / S;
+}
+
+/* Whole tensor: x, y are [B, H, Tq, Tk]; mask is [B, Tk] (broadcast over H and Tq) or NULL. */
+ORACLE_API void lnr_oracle_softmax_fw(const double *x, const double *mask, int64_t B,
+                                      int64_t H, int64_t Tq, int64_t Tk, int causal, double *y)
+{
+    const int64_t rows = B * H * Tq;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t b = r / (H * Tq);
+        const int64_t i = r % Tq;
+        softmax_fw_row(x + r * Tk, mask ? mask + b * Tk : 0, Tk, i, causal, y + r * Tk);
+    }
+}
+
+/* Selected rows: x, y are [nrows, Tk]; mask_rows is [nrows, Tk] (the mask row of each
+ * selected row's batch) or NULL; qidx[r] is the query position i of selected row r. */
+ORACLE_API void lnr_oracle_softmax_fw_rows(const double *x, const double *mask_rows,
+                                           const int64_t *qidx, int64_t nrows, int64_t Tk,
+                                           int causal, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r)
+        softmax_fw_row(x + r * Tk, mask_rows ? mask_rows + r * Tk : 0, Tk, qidx[r], causal,
+                       y + r * Tk);
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Attention softmax, backward. [HW4 "Problem structure and scoring" names the kernel]
+ * For one row with forward output y and upstream gradient dy:
+ *   t    = sum_j y_j * dy_j
+ *   dx_j = y_j * (dy_j - t)
+ * i.e. (diag(y) - y y^T) dy. Masked positions have y_j = 0 and therefore dx_j = 0.
+ * y, dy, dx are [rows, Tk].
+ * ------------------------------------------------------------------------------------- */
+ORACLE_API void lnr_oracle_softmax_bw(const double *y, const double *dy, int64_t rows,
+                                      int64_t Tk, double *dx)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *yr = y + r * Tk, *dyr = dy + r * Tk;
+        double t = 0.0;
+        for (int64_t j = 0; j < Tk; ++j)
+            t += yr[j] * dyr[j];
+        for (int64_t j = 0; j < Tk; ++j)
+            dx[r * Tk + j] = yr[j] * (dyr[j] - t);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * LayerNorm statistics of one row, two-pass definition. [L10 "Technique 2"; HW4]
+ *   mu    = (1/C) sum_j x_j
+ *   var   = (1/C) sum_j (x_j - mu)^2          (biased: a mean, as mu(x^2) is a mean)
+ *   sigma = sqrt(var + eps)                    (eps inside the root, as on the HW4 page)
+ * ------------------------------------------------------------------------------------- */
+static void row_stats(const double *x, int64_t C, double eps, double *mu_out,
+                      double *sigma_out)
+{
+    double s = 0.0;
+    for (int64_t j = 0; j < C; ++j)
+        s += x[j];
+    const double mu = s / (double)C;
+    double q = 0.0;
+    for (int64_t j = 0; j < C; ++j) {
+        const double d = x[j] - mu;
+        q += d * d;
+    }
+    const double var = q / (double)C;
+    *mu_out = mu;
+    *sigma_out = sqrt(var + eps);
+}
+
+/* LayerNorm forward: y = gamma * (x - mu) / sigma + beta. x, y: [N, C]; gamma, beta: [C].
+ * Also returns mu and 1/sigma per row (mean, rstd: [N]). */
+ORACLE_API void lnr_oracle_layernorm_fw(const double *x, const double *gamma,
+                                        const double *beta, int64_t N, int64_t C, double eps,
+                                        double *y, double *mean, double *rstd)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        const double *xr = x + i * C;
+        double mu, sigma;
+        row_stats(xr, C, eps, &mu, &sigma);
+        for (int64_t j = 0; j < C; ++j)
+            y[i * C + j] = gamma[j] * ((xr[j] - mu) / sigma) + beta[j];
+        mean[i] = mu;
+        rstd[i] = 1.0 / sigma;
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * LayerNorm backward, input gradient. [L10 "Technique 2"; HW4 "Problem structure"]
+ * With xhat_j = (x_j - mu)/sigma and g_j = gamma_j * dy_j, differentiating
+ * y_j = gamma_j xhat_j + beta_j through mu and sigma (eps inside sigma) gives
+ *   dx_j = (1/sigma) * ( g_j - (1/C) sum_k g_k - xhat_j * (1/C) sum_k g_k xhat_k ),
+ * the two row sums that the L10 lecture rearranges to run in parallel. The statistics are
+ * recomputed here from x in double, so the saved-statistics format cannot affect parity.
+ * x, dy, dx: [N, C]; gamma: [C].
+ * ------------------------------------------------------------------------------------- */
+ORACLE_API void lnr_oracle_layernorm_bw_dx(const double *x, const double *dy,
+                                           const double *gamma, int64_t N, int64_t C,
+                                           double eps, double *dx)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        const double *xr = x + i * C, *dyr = dy + i * C;
+        double mu, sigma;
+        row_stats(xr, C, eps, &mu, &sigma);
+        double sum_g = 0.0, sum_gx = 0.0;
+        for (int64_t j = 0; j < C; ++j) {
+            const double xhat = (xr[j] - mu) / sigma;
+            const double g = gamma[j] * dyr[j];
+            sum_g += g;
+            sum_gx += g * xhat;
+        }
+        const double a = sum_g / (double)C, b = sum_gx / (double)C;
+        for (int64_t j = 0; j < C; ++j) {
+            const double xhat = (xr[j] - mu) / sigma;
+            const double g = gamma[j] * dyr[j];
+            dx[i * C + j] = (g - a - xhat * b) / sigma;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * LayerNorm backward, parameter gradients: sums across rows. [HW4 "Problem structure"]
+ *   dgamma_j = sum_i dy_ij * xhat_ij,   dbeta_j = sum_i dy_ij
+ * Every column is summed over i = 0..N-1 in that order. Threads own disjoint blocks of
+ * columns; that only chooses which thread does a column, not the order of its sum.
+ * x, dy: [N, C]; dgamma, dbeta: [C]. mu/sigma per row are recomputed from x first.
+ * ------------------------------------------------------------------------------------- */
+ORACLE_API void lnr_oracle_layernorm_bw_dgamma_dbeta(const double *x, const double *dy,
+                                                     int64_t N, int64_t C, double eps,
+                                                     double *mu_ws, double *sigma_ws,
+                                                     double *dgamma, double *dbeta)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i)
+        row_stats(x + i * C, C, eps, &mu_ws[i], &sigma_ws[i]);
+
+    const int64_t blk = 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t jb = 0; jb < C; jb += blk) {
+        const int64_t je = (jb + blk < C) ? jb + blk : C;
+        for (int64_t j = jb; j < je; ++j) {
+            dgamma[j] = 0.0;
+            dbeta[j] = 0.0;
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t j = jb; j < je; ++j) {
+                const double xhat = (x[i * C + j] - mu_ws[i]) / sigma_ws[i];
+                dgamma[j] += dy[i * C + j] * xhat;
+                dbeta[j] += dy[i * C + j];
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * RMSNorm (forward and input gradient). [FT section 5.4]
+ *   rms = sqrt((1/C) sum_j x_j^2 + eps),  y_j = gamma_j * x_j / rms
+ *   dx_j = (1/rms) * ( g_j - xhat_j * (1/C) sum_k g_k xhat_k ),  g = gamma*dy, xhat = x/rms
+ *   dgamma_j = sum_i dy_ij * xhat_ij
+ * ------------------------------------------------------------------------------------- */
+ORACLE_API void lnr_oracle_rmsnorm_fw(const double *x, const double *gamma, int64_t N,
+                                      int64_t C, double eps, double *y, double *rrms)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        const double *xr = x + i * C;
+        double q = 0.0;
+        for (int64_t j = 0; j < C; ++j)
+            q += xr[j] * xr[j];
+        const double rms = sqrt(q / (double)C + eps);
+        for (int64_t j = 0; j < C; ++j)
+            y[i * C + j] = gamma[j] * (xr[j] / rms);
+        rrms[i] = 1.0 / rms;
+    }
+}
+
+ORACLE_API void lnr_oracle_rmsnorm_bw(const double *x, const double *dy, const double *gamma,
+                                      int64_t N, int64_t C, double eps, double *dx,
+                                      double *dgamma)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        const double *xr = x + i * C, *dyr = dy + i * C;
+        double q = 0.0;
+        for (int64_t j = 0; j < C; ++j)
+            q += xr[j] * xr[j];
+        const double rms = sqrt(q / (double)C + eps);
+        double sum_gx = 0.0;
+        for (int64_t j = 0; j < C; ++j)
+            sum_gx += gamma[j] * dyr[j] * (xr[j] / rms);
+        const double b = sum_gx / (double)C;
+        for (int64_t j = 0; j < C; ++j)
+            dx[i * C + j] = (gamma[j] * dyr[j] - (xr[j] / rms) * b) / rms;
+    }
+    for (int64_t j = 0; j < C; ++j)
+        dgamma[j] = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+        const double *xr = x + i * C;
+        double q = 0.0;
+        for (int64_t j = 0; j < C; ++j)
+            q += xr[j] * xr[j];
+        const double rms = sqrt(q / (double)C + eps);
+        for (int64_t j = 0; j < C; ++j)
+            dgamma[j] += dy[i * C + j] * (xr[j] / rms);
+    }
+}
