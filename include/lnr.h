@@ -1,0 +1,197 @@
+/*
+ * lnr.h -- C ABI of liblnr: fused attention-softmax and LayerNorm row reductions for
+ * AMD Instinct MI355X (gfx950, CDNA4), hand-written HIP kernels.
+ *
+ * The operations are the reduce kernels of a Transformer layer as the LightSeq line of work
+ * describes them:
+ *   - "CMU 11-868 L10: Accelerating Transformers on GPUs, and Where LightSeq Finds the Time",
+ *     sections "Technique 1: kernel fusion" (LayerNorm and softmax become custom reduce
+ *     kernels) and "Technique 2: rewrite the formula, drop a synchronization" (one fused
+ *     pass for mu(x) and mu(x^2); the LayerNorm backward as two sums computed together;
+ *     softmax as a max then a sum of exponentials; FP32 compute with FP16 storage).
+ *   - "CMU 11-868 HW4: Softmax and LayerNorm as fused CUDA kernels", section "Problem
+ *     structure and scoring" (masked softmax forward and backward, LayerNorm forward with
+ *     eps inside the square root, LayerNorm input gradient and gamma/beta gradients summed
+ *     across rows, row-length templates up to 2048) and section "Faster than what?"
+ *     (the mask is added to the scores: softmax(inp + mask)).
+ *
+ * Conventions shared by every entry point
+ *   - Storage dtype is LNR_F32 (IEEE binary32) or LNR_F16 (IEEE binary16); all arithmetic
+ *     is binary32. fp16 results are rounded to nearest even.
+ *   - Tensors are dense, row-major, C-contiguous device buffers (hipMalloc'd or any
+ *     device-accessible memory). The caller owns every buffer; the library allocates and
+ *     frees nothing and keeps no state between calls, so calls are re-entrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL means the default stream). Every call
+ *     only enqueues work on that stream and returns; nothing synchronises.
+ *   - Every argument is checked before anything is enqueued. A failed check returns a
+ *     nonzero lnr_status and enqueues nothing. A launch the HIP runtime rejects returns
+ *     LNR_ERR_HIP. Faults inside a kernel surface at the caller's next synchronisation.
+ *     No C++ exception crosses this interface.
+ *   - Results are bitwise reproducible: no floating-point atomics; every reduction has a
+ *     fixed order that depends only on the shape.
+ *   - Sizes of zero are legal and enqueue nothing (except layernorm_bw, which still writes
+ *     zero gradients for gamma and beta when N == 0).
+ *   - Any buffer may start at any address aligned to its element size. Rows whose byte
+ *     length is a multiple of 16 and buffers aligned to 16 bytes take the 128-bit vector
+ *     kernels; anything else takes a slower element-wise kernel with identical results
+ *     up to rounding order.
+ */
+#ifndef LNR_H
+#define LNR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point below is exported from liblnr.so; nothing else is. */
+#define LNR_API __attribute__((visibility("default")))
+
+typedef enum { LNR_F32 = 0, LNR_F16 = 1 } lnr_dtype;
+
+typedef enum {
+    LNR_OK = 0,
+    LNR_ERR_NULL = 1,        /* a required pointer is NULL */
+    LNR_ERR_SHAPE = 2,       /* a size is negative / zero where it may not be, or causal with Tq != Tk */
+    LNR_ERR_UNSUPPORTED = 3, /* row length beyond LNR_SOFTMAX_MAX_TK or LNR_LAYERNORM_MAX_C */
+    LNR_ERR_DTYPE = 4,       /* dtype is not an lnr_dtype value */
+    LNR_ERR_ALIGN = 5,       /* a pointer is not aligned to its element size */
+    LNR_ERR_ALIAS = 6,       /* buffers overlap in a way the operation forbids */
+    LNR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than layernorm_bw_workspace_bytes() */
+    LNR_ERR_HIP = 8          /* the HIP runtime rejected a launch */
+} lnr_status;
+
+#define LNR_SOFTMAX_MAX_TK 2048  /* longest row in the HW4 page's row-length template list */
+#define LNR_LAYERNORM_MAX_C 8192
+
+/*
+ * attn_softmax_fw -- masked, optionally causal softmax over the last axis of attention scores.
+ * [HW4 "Problem structure and scoring": future tokens set to -inf, the attention mask added,
+ *  a row max, then exponentials summed and normalised; L10 "Technique 2": two reductions.]
+ *
+ *   For every row r = (b, h, i) of inp [B, H, Tq, Tk]:
+ *     z_j = inp[b,h,i,j] + mask[b,j]            (mask term omitted when mask == NULL)
+ *     z_j = -inf                 if causal and j > i
+ *     out[b,h,i,j] = exp(z_j - max_k z_k) / sum_k exp(z_k - max_k z_k)
+ *   A row whose every z_j is -inf is written as all zeros. Positions with z_j = -inf are
+ *   written as exact zeros.
+ *
+ *   out   [B, H, Tq, Tk] dtype, written. May equal inp (in place); no other overlap allowed.
+ *   inp   [B, H, Tq, Tk] dtype, read.
+ *   mask  [B, Tk] dtype, additive, broadcast over H and Tq (key padding: 0 keeps a key,
+ *         -inf removes it), or NULL.
+ *   causal nonzero applies the future-token mask and requires Tq == Tk (LNR_ERR_SHAPE).
+ *   Limits: 1 <= Tk <= LNR_SOFTMAX_MAX_TK (else LNR_ERR_UNSUPPORTED / LNR_ERR_SHAPE);
+ *           B, H, Tq >= 0.
+ */
+LNR_API int attn_softmax_fw(void *out, const void *inp, const void *mask, int64_t B, int64_t H,
+                    int64_t Tq, int64_t Tk, int causal, lnr_dtype dtype, void *stream);
+
+/*
+ * attn_softmax_bw -- gradient of attn_softmax_fw with respect to its input scores.
+ * [HW4 "Problem structure and scoring": the softmax backward kernel, templated on row length.]
+ *
+ *   For every row with forward output y = out_fw and upstream gradient dy = dout:
+ *     t = sum_j y_j * dy_j ;   dinp_j = y_j * (dy_j - t)
+ *   Masked and future positions need no mask argument: y_j = 0 there, so dinp_j = 0.
+ *
+ *   dinp   [B, H, Tq, Tk] dtype, written. May equal dout (in place); no other overlap.
+ *   dout   [B, H, Tq, Tk] dtype, read.
+ *   out_fw [B, H, Tq, Tk] dtype, read (the forward output y).
+ *   Limits as attn_softmax_fw.
+ */
+LNR_API int attn_softmax_bw(void *dinp, const void *dout, const void *out_fw, int64_t B, int64_t H,
+                    int64_t Tq, int64_t Tk, lnr_dtype dtype, void *stream);
+
+/*
+ * layernorm_fw -- LayerNorm over the last axis with mean and variance from one fused pass.
+ * [L10 "Technique 2": sigma(x) = sqrt(mu(x^2) - mu(x)^2), so mu(x) and mu(x^2) come from one
+ *  reduction; HW4 "Problem structure and scoring": eps inside the root, eps = 1e-8.]
+ *
+ *   For every row i of x [N, C]:
+ *     mu = (1/C) sum_j x_ij ;  v = max((1/C) sum_j x_ij^2 - mu^2, 0)
+ *     rstd = 1 / sqrt(v + eps) ;  y_ij = gamma_j * (x_ij - mu) * rstd + beta_j
+ *
+ *   y     [N, C] dtype, written. May equal x (in place); no other overlap.
+ *   mean  [N] float32, written (mu per row), or NULL.
+ *   rstd  [N] float32, written (1/sigma per row), or NULL. The backward needs both.
+ *   x     [N, C] dtype, read.   gamma, beta  [C] dtype, read.
+ *   eps   added to the variance inside the square root (the pages use 1e-8); must be >= 0.
+ *   Limits: 1 <= C <= LNR_LAYERNORM_MAX_C; N >= 0.
+ */
+LNR_API int layernorm_fw(void *y, float *mean, float *rstd, const void *x, const void *gamma,
+                 const void *beta, int64_t N, int64_t C, float eps, lnr_dtype dtype,
+                 void *stream);
+
+/*
+ * layernorm_bw_workspace_bytes -- device workspace that layernorm_bw needs for (N, C, dtype):
+ * per-block column partial sums of dgamma and dbeta. Returns 0 for an invalid shape/dtype.
+ */
+LNR_API size_t layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype);
+
+/*
+ * layernorm_bw -- LayerNorm backward: input gradient and gamma/beta gradients.
+ * [L10 "Technique 2": the input gradient rearranged into two sums computed in parallel;
+ *  HW4 "Problem structure and scoring": dgamma and dbeta summed across rows.]
+ *
+ *   With xhat_ij = (x_ij - mean_i) * rstd_i and g_ij = gamma_j * dy_ij:
+ *     dx_ij    = rstd_i * ( g_ij - (1/C) sum_k g_ik - xhat_ij * (1/C) sum_k g_ik xhat_ik )
+ *     dgamma_j = sum_i dy_ij * xhat_ij ,   dbeta_j = sum_i dy_ij
+ *   The row pass computes dx and accumulates per-block column partials of dgamma/dbeta in
+ *   the same read of x and dy; a second kernel sums the partials in a fixed order. Column
+ *   partials accumulate in float32 for fp16 storage and in float64 for fp32 storage.
+ *
+ *   dx      [N, C] dtype, written. Must not overlap x, dy, gamma, mean or rstd (LNR_ERR_ALIAS).
+ *   dgamma, dbeta [C] dtype, written.
+ *   dy, x   [N, C] dtype, read.  gamma [C] dtype, read.
+ *   mean, rstd [N] float32, read: the values layernorm_fw wrote for this x.
+ *   workspace  device buffer of at least layernorm_bw_workspace_bytes(N, C, dtype) bytes,
+ *              8-byte aligned, owned by the caller; its contents on entry do not matter.
+ *   Limits: 1 <= C <= LNR_LAYERNORM_MAX_C; N >= 0.
+ */
+LNR_API int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const void *x,
+                 const void *gamma, const float *mean, const float *rstd, int64_t N,
+                 int64_t C, lnr_dtype dtype, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/*
+ * lnr_copy -- measurement helper, not part of the method: copies `bytes` bytes from src to
+ * dst with the same 128-bit load/store pattern as the row kernels, giving the achievable
+ * streaming ceiling that the kernels' bandwidth is compared with. dst and src must not
+ * overlap; bytes must be a multiple of 16 and both pointers 16-byte aligned.
+ */
+LNR_API int lnr_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+/*
+ * lnr_softmax_plan -- introspection of the row-length dispatch (the compile-time template
+ * choice at launch that the L10 lecture's "Technique 2" describes and the HW4 page's
+ * softmax backward asks for): for rows of Tk elements of `dtype` in 16-byte-aligned
+ * buffers, writes the bucket (the longest row of the chosen instantiation; 0 = element-wise
+ * fallback), the lanes per row and the 16-byte vectors per lane. Touches no device.
+ */
+LNR_API int lnr_softmax_plan(int64_t Tk, lnr_dtype dtype, int *bucket, int *lanes_per_row,
+                     int *vectors_per_lane);
+
+/*
+ * lnr_layernorm_plan -- the same for LayerNorm rows of C elements: `which` = 0 for the
+ * forward kernel, 1 for the backward row kernel. Also writes the workgroup size and the
+ * number of workgroups (for the backward: the number of dgamma/dbeta partial rows) that a
+ * call with N rows launches. Touches no device.
+ */
+LNR_API int lnr_layernorm_plan(int64_t N, int64_t C, lnr_dtype dtype, int which, int *bucket,
+                       int *lanes_per_row, int *vectors_per_lane, int *workgroup,
+                       int64_t *blocks);
+
+/* lnr_strerror -- static text for an lnr_status value (never NULL). */
+LNR_API const char *lnr_strerror(int status);
+
+/* lnr_build_info -- static text naming the target architecture and library version. */
+LNR_API const char *lnr_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LNR_H */

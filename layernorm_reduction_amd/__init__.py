@@ -1,1 +1,353 @@
-"""MI355X-native fused softmax and LayerNorm row reductions (binding filled in below)."""
+"""layernorm_reduction_amd -- fused attention-softmax and LayerNorm row reductions for MI355X.
+
+A thin binding over the C ABI of ``liblnr.so`` (declared in ``include/lnr.h``). Every step of
+every operation runs in the library's HIP kernels; this module only checks tensors, picks
+the dtype code, passes raw device pointers and torch's current HIP stream, and turns a
+nonzero status into ``LnrError``. There is no CPU fallback: if the library is missing or a
+tensor is not on the GPU, the call raises.
+
+Functions mirror the C entry points:
+    attn_softmax_fw(inp, mask=None, causal=False, out=None) -> out
+    attn_softmax_bw(dout, out_fw, dinp=None) -> dinp
+    layernorm_fw(x, gamma, beta, eps=1e-8, y=None, mean=None, rstd=None) -> (y, mean, rstd)
+    layernorm_bw(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None,
+                 workspace=None) -> (dx, dgamma, dbeta)
+    layernorm_bw_workspace_bytes(N, C, dtype) -> int
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LnrError", "load", "library_path", "attn_softmax_fw", "attn_softmax_bw", "layernorm_fw",
+    "layernorm_bw", "layernorm_bw_workspace_bytes", "copy_bytes", "softmax_plan",
+    "layernorm_plan", "LNR_F32", "LNR_F16", "SOFTMAX_MAX_TK", "LAYERNORM_MAX_C",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "liblnr.so")
+
+LNR_F32, LNR_F16 = 0, 1
+SOFTMAX_MAX_TK = 2048
+LAYERNORM_MAX_C = 8192
+
+STATUS_NAMES = {
+    0: "LNR_OK", 1: "LNR_ERR_NULL", 2: "LNR_ERR_SHAPE", 3: "LNR_ERR_UNSUPPORTED",
+    4: "LNR_ERR_DTYPE", 5: "LNR_ERR_ALIGN", 6: "LNR_ERR_ALIAS", 7: "LNR_ERR_WORKSPACE",
+    8: "LNR_ERR_HIP",
+}
+
+
+class LnrError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({text})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load liblnr.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m layernorm_reduction_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.attn_softmax_fw.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
+    lib.attn_softmax_bw.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, vp]
+    lib.layernorm_fw.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ctypes.c_float, ci, vp]
+    lib.layernorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
+    lib.layernorm_bw_workspace_bytes.restype = sz
+    lib.layernorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
+    lib.lnr_copy.argtypes = [vp, vp, sz, vp]
+    lib.lnr_strerror.argtypes = [ci]
+    lib.lnr_strerror.restype = ctypes.c_char_p
+    lib.lnr_build_info.restype = ctypes.c_char_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.lnr_softmax_plan.argtypes = [i64, ci, ip, ip, ip]
+    lib.lnr_layernorm_plan.argtypes = [i64, i64, ci, ci, ip, ip, ip, ip, ctypes.POINTER(i64)]
+    for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw", "lnr_copy",
+              "lnr_softmax_plan", "lnr_layernorm_plan"):
+        getattr(lib, f).restype = ci
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LnrError(status, where, load().lnr_strerror(status).decode())
+
+
+# ------------------------------------------------------------------------------------------
+# Tensor marshalling (torch is used for device memory and streams only).
+# ------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return LNR_F16
+    if t.dtype == torch.float32:
+        return LNR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use float16 or float32 storage")
+
+
+def _dev(t, name: str, like=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if like is not None:
+        if t.device != like.device:
+            raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+        if t.dtype != like.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {like.dtype}")
+    return t
+
+
+def _f32(t, name: str, like):
+    torch = _torch()
+    _dev(t, name)
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+    return t
+
+
+def _stream(t) -> int:
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+# ------------------------------------------------------------------------------------------
+# Operations.
+# ------------------------------------------------------------------------------------------
+
+def attn_softmax_fw(inp, mask=None, causal: bool = False, out=None):
+    """Masked / causal softmax over the last axis of inp [B, H, Tq, Tk].
+
+    mask: additive [B, Tk] (0 keeps a key, -inf removes it) or None. out may be inp.
+    """
+    torch = _torch()
+    _dev(inp, "inp")
+    if inp.dim() != 4:
+        raise ValueError("inp must be [B, H, Tq, Tk]")
+    B, H, Tq, Tk = inp.shape
+    if mask is not None:
+        _dev(mask, "mask", like=inp)
+        if tuple(mask.shape) != (B, Tk):
+            raise ValueError(f"mask must be [B, Tk] = [{B}, {Tk}], got {tuple(mask.shape)}")
+    if out is None:
+        out = torch.empty_like(inp)
+    else:
+        _dev(out, "out", like=inp)
+        if out.shape != inp.shape:
+            raise ValueError("out must have the shape of inp")
+    st = load().attn_softmax_fw(_ptr(out), _ptr(inp), _ptr(mask), B, H, Tq, Tk, int(bool(causal)),
+                                _dtype_code(inp), _stream(inp))
+    _check(st, "attn_softmax_fw")
+    return out
+
+
+def attn_softmax_bw(dout, out_fw, dinp=None):
+    """Gradient of attn_softmax_fw: dinp = y * (dout - sum(y * dout)). dinp may be dout."""
+    torch = _torch()
+    _dev(dout, "dout")
+    _dev(out_fw, "out_fw", like=dout)
+    if dout.dim() != 4 or out_fw.shape != dout.shape:
+        raise ValueError("dout and out_fw must both be [B, H, Tq, Tk]")
+    B, H, Tq, Tk = dout.shape
+    if dinp is None:
+        dinp = torch.empty_like(dout)
+    else:
+        _dev(dinp, "dinp", like=dout)
+        if dinp.shape != dout.shape:
+            raise ValueError("dinp must have the shape of dout")
+    st = load().attn_softmax_bw(_ptr(dinp), _ptr(dout), _ptr(out_fw), B, H, Tq, Tk,
+                                _dtype_code(dout), _stream(dout))
+    _check(st, "attn_softmax_bw")
+    return dinp
+
+
+def layernorm_fw(x, gamma, beta, eps: float = 1e-8, y=None, mean=None, rstd=None):
+    """LayerNorm over the last axis of x [N, C]; returns (y, mean, rstd) (fp32 stats)."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [N, C]")
+    N, C = x.shape
+    _dev(gamma, "gamma", like=x)
+    _dev(beta, "beta", like=x)
+    if gamma.numel() != C or beta.numel() != C:
+        raise ValueError("gamma and beta must have C elements")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _dev(y, "y", like=x)
+        if y.shape != x.shape:
+            raise ValueError("y must have the shape of x")
+    if mean is None:
+        mean = torch.empty(N, dtype=torch.float32, device=x.device)
+    if rstd is None:
+        rstd = torch.empty(N, dtype=torch.float32, device=x.device)
+    _f32(mean, "mean", x)
+    _f32(rstd, "rstd", x)
+    if mean.numel() != N or rstd.numel() != N:
+        raise ValueError("mean and rstd must have N elements")
+    st = load().layernorm_fw(_ptr(y), _ptr(mean), _ptr(rstd), _ptr(x), _ptr(gamma), _ptr(beta),
+                             N, C, float(eps), _dtype_code(x), _stream(x))
+    _check(st, "layernorm_fw")
+    return y, mean, rstd
+
+
+def layernorm_bw_workspace_bytes(N: int, C: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (LNR_F16 if str(dtype).endswith("float16") else LNR_F32)
+    return int(load().layernorm_bw_workspace_bytes(int(N), int(C), code))
+
+
+def layernorm_bw(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None, workspace=None):
+    """LayerNorm backward; returns (dx, dgamma, dbeta).
+
+    workspace: a uint8 GPU tensor of at least layernorm_bw_workspace_bytes(N, C, dtype) bytes;
+    allocated here when not given.
+    """
+    torch = _torch()
+    _dev(x, "x")
+    _dev(dy, "dy", like=x)
+    if x.dim() != 2 or dy.shape != x.shape:
+        raise ValueError("x and dy must both be [N, C]")
+    N, C = x.shape
+    _dev(gamma, "gamma", like=x)
+    if gamma.numel() != C:
+        raise ValueError("gamma must have C elements")
+    _f32(mean, "mean", x)
+    _f32(rstd, "rstd", x)
+    if mean.numel() != N or rstd.numel() != N:
+        raise ValueError("mean and rstd must have N elements")
+    if dx is None:
+        dx = torch.empty_like(x)
+    else:
+        _dev(dx, "dx", like=x)
+    if dgamma is None:
+        dgamma = torch.empty(C, dtype=x.dtype, device=x.device)
+    else:
+        _dev(dgamma, "dgamma", like=x)
+    if dbeta is None:
+        dbeta = torch.empty(C, dtype=x.dtype, device=x.device)
+    else:
+        _dev(dbeta, "dbeta", like=x)
+    code = _dtype_code(x)
+    need = int(load().layernorm_bw_workspace_bytes(N, C, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    else:
+        _dev(workspace, "workspace")
+    st = load().layernorm_bw(_ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(dy), _ptr(x), _ptr(gamma),
+                             _ptr(mean), _ptr(rstd), N, C, code, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(x))
+    _check(st, "layernorm_bw")
+    return dx, dgamma, dbeta
+
+
+def copy_bytes(dst, src):
+    """Streaming 16-byte-vector copy of src into dst (measurement helper)."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(load().lnr_copy(_ptr(dst), _ptr(src), n, _stream(src)), "lnr_copy")
+    return dst
+
+
+def softmax_plan(Tk: int, dtype_code: int):
+    """(bucket, lanes per row, 16-byte vectors per lane) for aligned buffers; bucket 0 means
+    the element-wise fallback."""
+    b, g, it = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load().lnr_softmax_plan(int(Tk), int(dtype_code), ctypes.byref(b), ctypes.byref(g),
+                                   ctypes.byref(it)), "lnr_softmax_plan")
+    return b.value, g.value, it.value
+
+
+def layernorm_plan(N: int, C: int, dtype_code: int, backward: bool = False):
+    """(bucket, lanes per row, vectors per lane, workgroup size, blocks) of the LayerNorm
+    forward or backward kernel."""
+    b, g, it, wg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    blocks = ctypes.c_int64()
+    _check(load().lnr_layernorm_plan(int(N), int(C), int(dtype_code), int(bool(backward)),
+                                     ctypes.byref(b), ctypes.byref(g), ctypes.byref(it),
+                                     ctypes.byref(wg), ctypes.byref(blocks)), "lnr_layernorm_plan")
+    return b.value, g.value, it.value, wg.value, blocks.value
+
+
+# ------------------------------------------------------------------------------------------
+# Bound calls: validate tensors once, then re-issue the same C call with no Python checks.
+# For launch-bound loops (benchmarks, training steps with fixed buffers). The tensors must
+# stay alive and unchanged in shape while the bound call is used.
+# ------------------------------------------------------------------------------------------
+
+class BoundCall:
+    """A C-ABI call with fixed arguments; calling it enqueues the kernels again."""
+    __slots__ = ("name", "_fn", "_args", "_keep")
+
+    def __init__(self, name, fn, args, keep):
+        self.name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            _check(st, self.name)
+
+
+def bind_attn_softmax_fw(inp, mask, causal, out):
+    attn_softmax_fw(inp, mask, causal, out)          # full validation once
+    B, H, Tq, Tk = inp.shape
+    args = (out.data_ptr(), inp.data_ptr(), _ptr(mask), B, H, Tq, Tk, int(bool(causal)),
+            _dtype_code(inp), _stream(inp))
+    return BoundCall("attn_softmax_fw", load().attn_softmax_fw, args, (inp, mask, out))
+
+
+def bind_attn_softmax_bw(dout, out_fw, dinp):
+    attn_softmax_bw(dout, out_fw, dinp)
+    B, H, Tq, Tk = dout.shape
+    args = (dinp.data_ptr(), dout.data_ptr(), out_fw.data_ptr(), B, H, Tq, Tk, _dtype_code(dout),
+            _stream(dout))
+    return BoundCall("attn_softmax_bw", load().attn_softmax_bw, args, (dout, out_fw, dinp))
+
+
+def bind_layernorm_fw(x, gamma, beta, eps, y, mean, rstd):
+    layernorm_fw(x, gamma, beta, eps, y, mean, rstd)
+    N, C = x.shape
+    args = (y.data_ptr(), mean.data_ptr(), rstd.data_ptr(), x.data_ptr(), gamma.data_ptr(),
+            beta.data_ptr(), N, C, float(eps), _dtype_code(x), _stream(x))
+    return BoundCall("layernorm_fw", load().layernorm_fw, args, (x, gamma, beta, y, mean, rstd))
+
+
+def bind_layernorm_bw(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace):
+    layernorm_bw(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace)
+    N, C = x.shape
+    args = (dx.data_ptr(), dgamma.data_ptr(), dbeta.data_ptr(), dy.data_ptr(), x.data_ptr(),
+            gamma.data_ptr(), mean.data_ptr(), rstd.data_ptr(), N, C, _dtype_code(x),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(x))
+    return BoundCall("layernorm_bw", load().layernorm_bw, args,
+                     (dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace))

@@ -1,0 +1,639 @@
+// lnr_layernorm.hip -- LayerNorm forward and backward for gfx950.
+//
+// Method: "CMU 11-868 L10 ...", section "Technique 2: rewrite the formula, drop a
+// synchronization": sigma = sqrt(mu(x^2) - mu(x)^2), so mu(x) and mu(x^2) come from ONE
+// reduction; the backward input gradient is two row sums (of gamma*dy and gamma*dy*xhat)
+// computed together; FP32 compute with FP16 storage. "CMU 11-868 HW4 ...", section "Problem
+// structure and scoring": eps = 1e-8 inside the root; gamma/beta gradients summed across
+// rows (the page stages them in shared memory and reduces along the row axis).
+//
+// Design on CDNA4:
+//   * Row kernels hold a row in registers across G lanes (G <= 64: one wave, several rows
+//     per wave for short rows; G = 128..1024: several waves per row, the two partial sums
+//     crossing waves through LDS with one barrier pair). 128-bit loads and stores.
+//   * Forward: one read of x, one write of y, per-row mean and rstd in fp32. The variance
+//     from the one-pass sums is clamped at 0 before eps is added.
+//   * Backward, fused: each workgroup walks a contiguous chunk of rows. Because a lane owns
+//     the same columns in every row, it accumulates dgamma/dbeta column partials in
+//     registers while it computes dx, so x and dy are read from HBM exactly once. At the
+//     end the workgroup's row groups are combined through an LDS column tile, in group
+//     order, and one partial row per workgroup goes to the workspace. A second small kernel
+//     sums the partials in a fixed order. No atomics: results are bitwise reproducible.
+//     Partials are fp32 for fp16 storage and fp64 for fp32 storage, so the long column sums
+//     over tens of thousands of rows add no rounding beyond the per-element products.
+#include <math.h>
+
+#include "lnr_common.h"
+#include "lnr_prims.h"
+
+namespace lnr {
+
+template <typename T> struct Accum;
+template <> struct Accum<f16> { using type = float; };
+template <> struct Accum<float> { using type = double; };
+
+__device__ __forceinline__ float ln_rstd(float s1, float s2, int C, float eps, float &mu) {
+    mu = s1 / static_cast<float>(C);
+    const float var = fmaxf(s2 / static_cast<float>(C) - mu * mu, 0.f);
+    return 1.0f / sqrtf(var + eps);
+}
+
+// ------------------------------------------------------------------------------------------
+// Forward, vector path.
+// ------------------------------------------------------------------------------------------
+template <typename T, int G, int IT, int WG>
+__global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__ mean,
+                                                       float *__restrict__ rstd, const T *x,
+                                                       const T *__restrict__ gamma,
+                                                       const T *__restrict__ beta, int64_t N,
+                                                       int32_t C, float eps) {
+    constexpr int V = Vec16<T>::N;
+    constexpr int RPB = WG / G;
+    __shared__ float red[2 * (WG / 64)];
+    const int lane = threadIdx.x % G;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / G;
+    const bool live = row < N;
+    const int nvec = C / V;
+    const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
+
+    float v[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (live && c < nvec) {
+            load_vec<T>(x + base + static_cast<int64_t>(c) * V, v[k]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) v[k][e] = 0.f;
+        }
+    }
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            s1 += v[k][e];
+            s2 += v[k][e] * v[k][e];
+        }
+    row_allreduce_sum2<G>(s1, s2, red);
+    float mu;
+    const float rs = ln_rstd(s1, s2, C, eps, mu);
+
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (live && c < nvec) {
+            float g[V], b[V], o[V];
+            load_vec<T>(gamma + c * V, g);
+            load_vec<T>(beta + c * V, b);
+#pragma unroll
+            for (int e = 0; e < V; ++e) o[e] = (v[k][e] - mu) * rs * g[e] + b[e];
+            store_vec<T>(y + base + static_cast<int64_t>(c) * V, o);
+        }
+    }
+    if (live && lane == 0 && mean != nullptr) {
+        mean[row] = mu;
+        rstd[row] = rs;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward, vector path: dx plus per-workgroup dgamma/dbeta column partials.
+// part layout: [P][2][C] of Accum<T>; slot 0 = dgamma, slot 1 = dbeta.
+// ------------------------------------------------------------------------------------------
+template <typename T, int G, int IT, int WG>
+__global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>::type *part,
+                                                       const T *dy, const T *x,
+                                                       const T *__restrict__ gamma,
+                                                       const float *__restrict__ mean,
+                                                       const float *__restrict__ rstd,
+                                                       int64_t N, int32_t C,
+                                                       int64_t rows_per_block) {
+    using A = typename Accum<T>::type;
+    constexpr int V = Vec16<T>::N;
+    constexpr int NG = WG / G;  // row groups per workgroup
+    __shared__ float red[2 * (WG / 64)];
+    __shared__ A tile[2][NG > 1 ? NG : 1][NG > 1 ? G * V : 1];
+
+    const int lane = threadIdx.x % G;
+    const int grp = threadIdx.x / G;
+    const int nvec = C / V;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+    const int64_t r1 = (r0 + rows_per_block < N) ? r0 + rows_per_block : N;
+    const float invC = 1.0f / static_cast<float>(C);
+
+    float gm[IT][V];
+    A adg[IT][V], adb[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (c < nvec) {
+            load_vec<T>(gamma + c * V, gm[k]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) gm[k][e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) adg[k][e] = adb[k][e] = A(0);
+    }
+
+    // Same trip count for every group so that multi-wave rows can use barriers.
+    const int64_t iters = (rows_per_block + NG - 1) / NG;
+    for (int64_t it = 0; it < iters; ++it) {
+        const int64_t row = r0 + it * NG + grp;
+        const bool live = row < r1;
+        const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
+        float xv[IT][V], dv[IT][V];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int c = k * G + lane;
+            if (live && c < nvec) {
+                load_vec<T>(x + base + static_cast<int64_t>(c) * V, xv[k]);
+                load_vec<T>(dy + base + static_cast<int64_t>(c) * V, dv[k]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) xv[k][e] = dv[k][e] = 0.f;
+            }
+        }
+        const float mu = live ? mean[row] : 0.f;
+        const float rs = live ? rstd[row] : 0.f;
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float xh = (xv[k][e] - mu) * rs;
+                const float g = gm[k][e] * dv[k][e];
+                xv[k][e] = xh;
+                sg += g;
+                sgx += g * xh;
+            }
+        row_allreduce_sum2<G>(sg, sgx, red);
+        const float a = sg * invC, b = sgx * invC;
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int c = k * G + lane;
+            if (live && c < nvec) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    o[e] = rs * (gm[k][e] * dv[k][e] - a - xv[k][e] * b);
+                store_vec<T>(dx + base + static_cast<int64_t>(c) * V, o);
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                adg[k][e] += static_cast<A>(dv[k][e] * xv[k][e]);
+                adb[k][e] += static_cast<A>(dv[k][e]);
+            }
+        }
+    }
+
+    A *pg = part + static_cast<int64_t>(blockIdx.x) * 2 * C;
+    A *pb = pg + C;
+    if constexpr (NG == 1) {
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int c = k * G + lane;
+            if (c < nvec) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    pg[c * V + e] = adg[k][e];
+                    pb[c * V + e] = adb[k][e];
+                }
+            }
+        }
+    } else {
+        // LDS column tile: for vector slot k, every group stages its G*V columns, then the
+        // workgroup sums the NG groups of each column in group order.
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                tile[0][grp][lane * V + e] = adg[k][e];
+                tile[1][grp][lane * V + e] = adb[k][e];
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < 2 * G * V; idx += WG) {
+                const int which = idx / (G * V);
+                const int cc = idx % (G * V);
+                A s = tile[which][0][cc];
+#pragma unroll
+                for (int g = 1; g < NG; ++g) s += tile[which][g][cc];
+                const int col = k * G * V + cc;
+                if (col < C) (which == 0 ? pg : pb)[col] = s;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Column finalize: dgamma/dbeta = fixed-order sums of the P partial rows.
+// Block = 16 columns x 16 slices; slice s sums partials p = s, s+16, s+32, ... in order,
+// then slice 0 adds the 16 slice sums in slice order.
+// ------------------------------------------------------------------------------------------
+constexpr int kColTile = 16;
+constexpr int kColSlices = 16;
+
+template <typename T>
+__global__ __launch_bounds__(kColTile *kColSlices) void layernorm_bw_colsum(
+    T *__restrict__ dgamma, T *__restrict__ dbeta, const typename Accum<T>::type *__restrict__ part,
+    int32_t P, int32_t C) {
+    using A = typename Accum<T>::type;
+    __shared__ A slab[kColSlices][kColTile];
+    const int cl = threadIdx.x % kColTile;
+    const int sl = threadIdx.x / kColTile;
+    const int which = blockIdx.y;
+    const int col = blockIdx.x * kColTile + cl;
+    A s = A(0);
+    if (col < C) {
+#pragma unroll 8
+        for (int p = sl; p < P; p += kColSlices) s += part[(static_cast<int64_t>(p) * 2 + which) * C + col];
+    }
+    slab[sl][cl] = s;
+    __syncthreads();
+    if (sl == 0 && col < C) {
+        A t = slab[0][cl];
+#pragma unroll
+        for (int k = 1; k < kColSlices; ++k) t += slab[k][cl];
+        (which == 0 ? dgamma : dbeta)[col] = from_f32<T>(static_cast<float>(t));
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Element-wise fallback kernels (any C, any element alignment): one workgroup per row.
+// ------------------------------------------------------------------------------------------
+constexpr int kLnGenericWG = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kLnGenericWG) void layernorm_fw_generic(
+    T *y, float *__restrict__ mean, float *__restrict__ rstd, const T *x,
+    const T *__restrict__ gamma, const T *__restrict__ beta, int64_t N, int32_t C, float eps) {
+    __shared__ float red[2 * (kLnGenericWG / 64)];
+    const int64_t row = blockIdx.x;
+    const T *xr = x + row * static_cast<int64_t>(C);
+    float s1 = 0.f, s2 = 0.f;
+    for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
+        const float v = to_f32(xr[j]);
+        s1 += v;
+        s2 += v * v;
+    }
+    row_allreduce_sum2<kLnGenericWG>(s1, s2, red);
+    float mu;
+    const float rs = ln_rstd(s1, s2, C, eps, mu);
+    T *yr = y + row * static_cast<int64_t>(C);
+    for (int j = threadIdx.x; j < C; j += kLnGenericWG)
+        yr[j] = from_f32<T>((to_f32(xr[j]) - mu) * rs * to_f32(gamma[j]) + to_f32(beta[j]));
+    if (threadIdx.x == 0 && mean != nullptr) {
+        mean[row] = mu;
+        rstd[row] = rs;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_dx_generic(
+    T *dx, const T *dy, const T *x, const T *__restrict__ gamma, const float *__restrict__ mean,
+    const float *__restrict__ rstd, int64_t N, int32_t C) {
+    __shared__ float red[2 * (kLnGenericWG / 64)];
+    const int64_t row = blockIdx.x;
+    const int64_t base = row * static_cast<int64_t>(C);
+    const float mu = mean[row], rs = rstd[row];
+    float sg = 0.f, sgx = 0.f;
+    for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
+        const float xh = (to_f32(x[base + j]) - mu) * rs;
+        const float g = to_f32(gamma[j]) * to_f32(dy[base + j]);
+        sg += g;
+        sgx += g * xh;
+    }
+    row_allreduce_sum2<kLnGenericWG>(sg, sgx, red);
+    const float invC = 1.0f / static_cast<float>(C);
+    const float a = sg * invC, b = sgx * invC;
+    for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
+        const float xh = (to_f32(x[base + j]) - mu) * rs;
+        const float g = to_f32(gamma[j]) * to_f32(dy[base + j]);
+        dx[base + j] = from_f32<T>(rs * (g - a - xh * b));
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_colpart_generic(
+    typename Accum<T>::type *part, const T *dy, const T *x, const float *__restrict__ mean,
+    const float *__restrict__ rstd, int64_t N, int32_t C, int64_t rows_per_block) {
+    using A = typename Accum<T>::type;
+    const int col = blockIdx.x * kLnGenericWG + threadIdx.x;
+    if (col >= C) return;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per_block;
+    const int64_t r1 = (r0 + rows_per_block < N) ? r0 + rows_per_block : N;
+    A sg = A(0), sb = A(0);
+    for (int64_t r = r0; r < r1; ++r) {
+        const float d = to_f32(dy[r * C + col]);
+        const float xh = (to_f32(x[r * C + col]) - mean[r]) * rstd[r];
+        sg += static_cast<A>(d * xh);
+        sb += static_cast<A>(d);
+    }
+    part[(static_cast<int64_t>(blockIdx.y) * 2 + 0) * C + col] = sg;
+    part[(static_cast<int64_t>(blockIdx.y) * 2 + 1) * C + col] = sb;
+}
+
+// ------------------------------------------------------------------------------------------
+// Hidden-size buckets.
+// ------------------------------------------------------------------------------------------
+struct LnPlan {
+    int bucket;  // widest row this instantiation takes
+    int G;       // lanes per row (multiples of 64 above one wave)
+    int IT;      // 16-byte vectors per lane
+};
+
+template <typename T> struct LnFwTable;
+template <> struct LnFwTable<f16> {  // V = 8
+    static constexpr LnPlan plans[] = {{64, 8, 1},    {128, 16, 1},  {256, 16, 2},
+                                       {512, 16, 4},  {768, 32, 3},  {1024, 32, 4},
+                                       {2048, 64, 4}, {4096, 128, 4}, {8192, 256, 4}};
+};
+template <> struct LnFwTable<float> {  // V = 4
+    static constexpr LnPlan plans[] = {{64, 16, 1},    {128, 16, 2},   {256, 16, 4},
+                                       {512, 32, 4},   {768, 64, 3},   {1024, 64, 4},
+                                       {2048, 128, 4}, {4096, 256, 4}, {8192, 512, 4}};
+};
+template <typename T> struct LnBwTable;
+template <> struct LnBwTable<f16> {
+    static constexpr LnPlan plans[] = {{64, 8, 1},     {128, 16, 1},   {256, 32, 1},
+                                       {512, 64, 1},   {768, 32, 3},   {1024, 64, 2},
+                                       {2048, 128, 2}, {4096, 256, 2}, {8192, 512, 2}};
+};
+template <> struct LnBwTable<float> {
+    static constexpr LnPlan plans[] = {{64, 16, 1},    {128, 32, 1},   {256, 64, 1},
+                                       {512, 64, 2},   {768, 64, 3},   {1024, 128, 2},
+                                       {2048, 256, 2}, {4096, 512, 2}, {8192, 1024, 2}};
+};
+
+constexpr int kLnFwMinWG = 256;
+constexpr int kLnBwMinWG = 512;
+constexpr int64_t kLnBwTargetBlocks = 512;  // two 512-thread workgroups per CU on 256 CUs
+
+constexpr int ln_fw_wg(int G) { return G > kLnFwMinWG ? G : kLnFwMinWG; }
+constexpr int ln_bw_wg(int G) { return G > kLnBwMinWG ? G : kLnBwMinWG; }
+
+template <typename Table>
+static bool find_plan(int64_t C, LnPlan &out) {
+    for (const LnPlan &p : Table::plans)
+        if (C <= p.bucket) {
+            out = p;
+            return true;
+        }
+    return false;
+}
+
+// Rows per backward workgroup: about N / kLnBwTargetBlocks, rounded up to whole row groups.
+static int64_t bw_rows_per_block(int64_t N, int64_t groups) {
+    int64_t r = (N + kLnBwTargetBlocks - 1) / kLnBwTargetBlocks;
+    if (r < 1) r = 1;
+    return ((r + groups - 1) / groups) * groups;
+}
+
+static int64_t bw_blocks(int64_t N, int64_t rpb) { return N == 0 ? 0 : (N + rpb - 1) / rpb; }
+
+// Workgroups (= partial rows) of each backward path for this shape.
+static void bw_partials(int64_t N, int64_t C, lnr_dtype dtype, int64_t &p_vec, int64_t &p_gen,
+                        int64_t &rpb_vec, int64_t &rpb_gen) {
+    LnPlan p{};
+    const bool ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, p) : find_plan<LnBwTable<float>>(C, p);
+    const int64_t groups = ok ? ln_bw_wg(p.G) / p.G : 1;
+    rpb_vec = bw_rows_per_block(N, groups);
+    p_vec = bw_blocks(N, rpb_vec);
+    rpb_gen = bw_rows_per_block(N, 1);
+    p_gen = bw_blocks(N, rpb_gen);
+}
+
+struct LnFwArgs {
+    void *y;
+    float *mean;
+    float *rstd;
+    const void *x, *gamma, *beta;
+    int64_t N;
+    int32_t C;
+    float eps;
+};
+struct LnBwArgs {
+    void *dx;
+    void *part;
+    const void *dy, *x, *gamma;
+    const float *mean, *rstd;
+    int64_t N;
+    int32_t C;
+    int64_t rows_per_block;
+    int64_t blocks;
+};
+
+template <typename T, int I>
+static hipError_t dispatch_ln_fw(const LnFwArgs &a, hipStream_t st) {
+    constexpr LnPlan p = LnFwTable<T>::plans[I];
+    if (a.C <= p.bucket) {
+        constexpr int WG = ln_fw_wg(p.G);
+        constexpr int RPB = WG / p.G;
+        const int64_t blocks = (a.N + RPB - 1) / RPB;
+        return launch(layernorm_fw_vec<T, p.G, p.IT, WG>, dim3(static_cast<uint32_t>(blocks)), dim3(WG),
+                      st, static_cast<T *>(a.y), a.mean, a.rstd, static_cast<const T *>(a.x),
+                      static_cast<const T *>(a.gamma), static_cast<const T *>(a.beta), a.N, a.C,
+                      a.eps);
+    }
+    if constexpr (I + 1 < static_cast<int>(sizeof(LnFwTable<T>::plans) / sizeof(LnPlan)))
+        return dispatch_ln_fw<T, I + 1>(a, st);
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int I>
+static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
+    constexpr LnPlan p = LnBwTable<T>::plans[I];
+    if (a.C <= p.bucket) {
+        constexpr int WG = ln_bw_wg(p.G);
+        return launch(layernorm_bw_vec<T, p.G, p.IT, WG>, dim3(static_cast<uint32_t>(a.blocks)),
+                      dim3(WG), st, static_cast<T *>(a.dx),
+                      static_cast<typename Accum<T>::type *>(a.part), static_cast<const T *>(a.dy),
+                      static_cast<const T *>(a.x), static_cast<const T *>(a.gamma), a.mean, a.rstd,
+                      a.N, a.C, a.rows_per_block);
+    }
+    if constexpr (I + 1 < static_cast<int>(sizeof(LnBwTable<T>::plans) / sizeof(LnPlan)))
+        return dispatch_ln_bw<T, I + 1>(a, st);
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_colsum(void *dgamma, void *dbeta, const void *part, int64_t P, int32_t C,
+                                hipStream_t st) {
+    const dim3 grid(static_cast<uint32_t>((C + kColTile - 1) / kColTile), 2);
+    return launch(layernorm_bw_colsum<T>, grid, dim3(kColTile * kColSlices), st,
+                  static_cast<T *>(dgamma), static_cast<T *>(dbeta),
+                  static_cast<const typename Accum<T>::type *>(part), static_cast<int32_t>(P), C);
+}
+
+static size_t accum_size(lnr_dtype d) { return d == LNR_F16 ? sizeof(float) : sizeof(double); }
+
+}  // namespace lnr
+
+using namespace lnr;
+
+extern "C" int layernorm_fw(void *y, float *mean, float *rstd, const void *x, const void *gamma,
+                            const void *beta, int64_t N, int64_t C, float eps, lnr_dtype dtype,
+                            void *stream) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (N < 0 || C < 1) return LNR_ERR_SHAPE;
+    if (C > LNR_LAYERNORM_MAX_C) return LNR_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || !isfinite(eps)) return LNR_ERR_SHAPE;
+    if ((mean == nullptr) != (rstd == nullptr)) return LNR_ERR_NULL;
+    if (N == 0) return LNR_OK;
+    if (N > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    if (y == nullptr || x == nullptr || gamma == nullptr || beta == nullptr) return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned_to(y, es) || !aligned_to(x, es) || !aligned_to(gamma, es) || !aligned_to(beta, es) ||
+        !aligned_to(mean, 4) || !aligned_to(rstd, 4))
+        return LNR_ERR_ALIGN;
+    const size_t nbytes = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
+    if (bad_alias(y, x, nbytes) || overlap(y, nbytes, gamma, C * es) || overlap(y, nbytes, beta, C * es) ||
+        overlap(y, nbytes, mean, N * 4) || overlap(y, nbytes, rstd, N * 4) ||
+        overlap(mean, N * 4, rstd, N * 4))
+        return LNR_ERR_ALIAS;
+
+    LnFwArgs a{y, mean, rstd, x, gamma, beta, N, static_cast<int32_t>(C), eps};
+    const bool vec = (static_cast<size_t>(C) * es) % 16 == 0 && aligned_to(y, 16) &&
+                     aligned_to(x, 16) && aligned_to(gamma, 16) && aligned_to(beta, 16);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (vec) {
+        e = dtype == LNR_F16 ? dispatch_ln_fw<f16, 0>(a, s) : dispatch_ln_fw<float, 0>(a, s);
+    } else if (dtype == LNR_F16) {
+        e = launch(layernorm_fw_generic<f16>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), s,
+                   static_cast<f16 *>(y), mean, rstd, static_cast<const f16 *>(x),
+                   static_cast<const f16 *>(gamma), static_cast<const f16 *>(beta), N, a.C, eps);
+    } else {
+        e = launch(layernorm_fw_generic<float>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), s,
+                   static_cast<float *>(y), mean, rstd, static_cast<const float *>(x),
+                   static_cast<const float *>(gamma), static_cast<const float *>(beta), N, a.C, eps);
+    }
+    return status_of(e);
+}
+
+extern "C" size_t layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype) {
+    if (!valid_dtype(dtype) || N < 0 || C < 1 || C > LNR_LAYERNORM_MAX_C) return 0;
+    int64_t pv, pg, rv, rg;
+    bw_partials(N, C, dtype, pv, pg, rv, rg);
+    const int64_t P = pv > pg ? pv : pg;
+    return static_cast<size_t>(P) * 2 * static_cast<size_t>(C) * accum_size(dtype);
+}
+
+extern "C" int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const void *x,
+                            const void *gamma, const float *mean, const float *rstd, int64_t N,
+                            int64_t C, lnr_dtype dtype, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (N < 0 || C < 1) return LNR_ERR_SHAPE;
+    if (C > LNR_LAYERNORM_MAX_C) return LNR_ERR_UNSUPPORTED;
+    if (N > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    if (dgamma == nullptr || dbeta == nullptr) return LNR_ERR_NULL;
+    if (N > 0 && (dx == nullptr || dy == nullptr || x == nullptr || gamma == nullptr ||
+                  mean == nullptr || rstd == nullptr))
+        return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned_to(dx, es) || !aligned_to(dgamma, es) || !aligned_to(dbeta, es) ||
+        !aligned_to(dy, es) || !aligned_to(x, es) || !aligned_to(gamma, es) ||
+        !aligned_to(mean, 4) || !aligned_to(rstd, 4))
+        return LNR_ERR_ALIGN;
+    const size_t need = layernorm_bw_workspace_bytes(N, C, dtype);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LNR_ERR_WORKSPACE;
+    if (need > 0 && !aligned_to(workspace, 8)) return LNR_ERR_ALIGN;
+    const size_t nbytes = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
+    const size_t cbytes = static_cast<size_t>(C) * es;
+    if (overlap(dx, nbytes, x, nbytes) || overlap(dx, nbytes, dy, nbytes) ||
+        overlap(dx, nbytes, gamma, cbytes) || overlap(dx, nbytes, mean, N * 4) ||
+        overlap(dx, nbytes, rstd, N * 4) || overlap(dgamma, cbytes, dbeta, cbytes) ||
+        overlap(workspace, need, dx, nbytes) || overlap(workspace, need, x, nbytes) ||
+        overlap(workspace, need, dy, nbytes) || overlap(workspace, need, dgamma, cbytes) ||
+        overlap(workspace, need, dbeta, cbytes))
+        return LNR_ERR_ALIAS;
+    for (const void *out : {dgamma, dbeta})
+        if (overlap(out, cbytes, x, nbytes) || overlap(out, cbytes, dy, nbytes) ||
+            overlap(out, cbytes, dx, nbytes) || overlap(out, cbytes, gamma, cbytes))
+            return LNR_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t pv, pg, rv, rg;
+    bw_partials(N, C, dtype, pv, pg, rv, rg);
+    const int32_t C32 = static_cast<int32_t>(C);
+    hipError_t e = hipSuccess;
+    int64_t P = 0;
+    if (N > 0) {
+        const bool vec = (static_cast<size_t>(C) * es) % 16 == 0 && aligned_to(dx, 16) &&
+                         aligned_to(dy, 16) && aligned_to(x, 16) && aligned_to(gamma, 16);
+        if (vec) {
+            P = pv;
+            LnBwArgs a{dx, workspace, dy, x, gamma, mean, rstd, N, C32, rv, pv};
+            e = dtype == LNR_F16 ? dispatch_ln_bw<f16, 0>(a, s) : dispatch_ln_bw<float, 0>(a, s);
+        } else {
+            P = pg;
+            if (dtype == LNR_F16) {
+                e = launch(layernorm_bw_dx_generic<f16>, dim3(static_cast<uint32_t>(N)),
+                           dim3(kLnGenericWG), s, static_cast<f16 *>(dx),
+                           static_cast<const f16 *>(dy), static_cast<const f16 *>(x),
+                           static_cast<const f16 *>(gamma), mean, rstd, N, C32);
+                if (e == hipSuccess)
+                    e = launch(layernorm_bw_colpart_generic<f16>,
+                               dim3(static_cast<uint32_t>((C + kLnGenericWG - 1) / kLnGenericWG),
+                                    static_cast<uint32_t>(pg)),
+                               dim3(kLnGenericWG), s, static_cast<float *>(workspace),
+                               static_cast<const f16 *>(dy), static_cast<const f16 *>(x), mean,
+                               rstd, N, C32, rg);
+            } else {
+                e = launch(layernorm_bw_dx_generic<float>, dim3(static_cast<uint32_t>(N)),
+                           dim3(kLnGenericWG), s, static_cast<float *>(dx),
+                           static_cast<const float *>(dy), static_cast<const float *>(x),
+                           static_cast<const float *>(gamma), mean, rstd, N, C32);
+                if (e == hipSuccess)
+                    e = launch(layernorm_bw_colpart_generic<float>,
+                               dim3(static_cast<uint32_t>((C + kLnGenericWG - 1) / kLnGenericWG),
+                                    static_cast<uint32_t>(pg)),
+                               dim3(kLnGenericWG), s, static_cast<double *>(workspace),
+                               static_cast<const float *>(dy), static_cast<const float *>(x), mean,
+                               rstd, N, C32, rg);
+            }
+        }
+    }
+    if (e == hipSuccess)
+        e = dtype == LNR_F16 ? launch_colsum<f16>(dgamma, dbeta, workspace, P, C32, s)
+                             : launch_colsum<float>(dgamma, dbeta, workspace, P, C32, s);
+    return status_of(e);
+}
+
+// Introspection: the bucket, lanes per row, vectors per lane and workgroup size of the
+// forward (which = 0) or backward (which = 1) vector kernel for (C, dtype); bucket 0 means
+// the element-wise fallback. For the backward, *blocks gets the number of partial rows.
+extern "C" int lnr_layernorm_plan(int64_t N, int64_t C, lnr_dtype dtype, int which, int *bucket,
+                                  int *lanes_per_row, int *vectors_per_lane, int *workgroup,
+                                  int64_t *blocks) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (N < 0 || C < 1) return LNR_ERR_SHAPE;
+    if (C > LNR_LAYERNORM_MAX_C) return LNR_ERR_UNSUPPORTED;
+    if (!bucket || !lanes_per_row || !vectors_per_lane || !workgroup || !blocks) return LNR_ERR_NULL;
+    const bool vec = (static_cast<size_t>(C) * dtype_size(dtype)) % 16 == 0;
+    LnPlan p{0, kLnGenericWG, 0};
+    bool ok = false;
+    if (vec) {
+        if (which == 0)
+            ok = dtype == LNR_F16 ? find_plan<LnFwTable<f16>>(C, p) : find_plan<LnFwTable<float>>(C, p);
+        else
+            ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, p) : find_plan<LnBwTable<float>>(C, p);
+    }
+    if (!ok) p = LnPlan{0, kLnGenericWG, 0};
+    *bucket = p.bucket;
+    *lanes_per_row = p.G;
+    *vectors_per_lane = p.IT;
+    int64_t pv, pg, rv, rg;
+    bw_partials(N, C, dtype, pv, pg, rv, rg);
+    if (which == 0) {
+        *workgroup = ok ? ln_fw_wg(p.G) : kLnGenericWG;
+        *blocks = ok ? (N + (*workgroup / p.G) - 1) / (*workgroup / p.G) : N;
+    } else {
+        *workgroup = ok ? ln_bw_wg(p.G) : kLnGenericWG;
+        *blocks = ok ? pv : pg;
+    }
+    return LNR_OK;
+}

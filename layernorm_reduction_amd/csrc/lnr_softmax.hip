@@ -1,0 +1,406 @@
+// lnr_softmax.hip -- masked / causal attention softmax, forward and backward, for gfx950.
+//
+// Method: "CMU 11-868 HW4: Softmax and LayerNorm as fused CUDA kernels", section "Problem
+// structure and scoring" (scores plus the attention mask, future tokens at -inf, a row max,
+// then a sum of exponentials; the backward templated on row length from {32, ..., 2048})
+// and "CMU 11-868 L10 ...", section "Technique 2" (two reductions per row; rows <= 32 on
+// one warp; elements per thread and blocks fixed at compile time, picked at launch).
+//
+// Design on CDNA4:
+//   * A row of Tk elements is held in registers by a group of G lanes of one wave64; each
+//     lane owns IT vectors of 16 bytes. Vector k of lane l covers elements
+//     [(k*G + l)*V, +V), so every load instruction of a group reads G*16 contiguous bytes.
+//     Short rows use small G and put several rows in one wave (16 rows of 32 fp16 each at
+//     G = 4); rows up to 2048 use the whole wave. (G, IT) per row-length bucket is a
+//     compile-time choice, picked by the host from Tk.
+//   * The two softmax reductions (max, then sum) are lane-crossing DPP/ds_swizzle
+//     butterflies inside the group (lnr_prims.h): no LDS, no barrier.
+//   * One pass over HBM: each row is read once and written once. Rows whose byte length is
+//     not a multiple of 16, or unaligned buffers, go to an element-wise fallback kernel
+//     (one wave per row, three passes over the row through the caches).
+#include <math.h>
+
+#include "lnr_common.h"
+#include "lnr_prims.h"
+
+namespace lnr {
+
+// ------------------------------------------------------------------------------------------
+// Vector kernels.
+// ------------------------------------------------------------------------------------------
+template <typename T, int G, int IT, int WG>
+__global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
+                                                     const T *__restrict__ mask, int64_t rows,
+                                                     int32_t Tq, int32_t Tk,
+                                                     int64_t rows_per_batch, int32_t causal) {
+    constexpr int V = Vec16<T>::N;
+    constexpr int RPB = WG / G;
+    const int lane = threadIdx.x % G;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / G;
+    const bool live = row < rows;
+    const int nvec = Tk / V;
+    const int64_t base = (live ? row : 0) * static_cast<int64_t>(Tk);
+
+    float z[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (live && c < nvec) {
+            load_vec<T>(inp + base + static_cast<int64_t>(c) * V, z[k]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) z[k][e] = -INFINITY;
+        }
+    }
+    if (mask != nullptr) {
+        const T *mrow = mask + (live ? row / rows_per_batch : 0) * static_cast<int64_t>(Tk);
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int c = k * G + lane;
+            if (live && c < nvec) {
+                float m[V];
+                load_vec<T>(mrow + static_cast<int64_t>(c) * V, m);
+#pragma unroll
+                for (int e = 0; e < V; ++e) z[k][e] += m[e];
+            }
+        }
+    }
+    if (causal) {
+        const int qi = static_cast<int>(row % Tq);
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if ((k * G + lane) * V + e > qi) z[k][e] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) mx = fmaxf(mx, z[k][e]);
+    mx = group_allreduce<G>(mx, OpMax());
+    if (mx == -INFINITY) mx = 0.f;  // fully masked (or idle) row: every exponential is 0
+
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            z[k][e] = exp_nonpos(z[k][e] - mx);
+            s += z[k][e];
+        }
+    s = group_allreduce<G>(s, OpSum());
+    const float inv = s > 0.f ? 1.0f / s : 0.f;
+
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (live && c < nvec) {
+            float y[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) y[e] = z[k][e] * inv;
+            store_vec<T>(out + base + static_cast<int64_t>(c) * V, y);
+        }
+    }
+}
+
+template <typename T, int G, int IT, int WG>
+__global__ __launch_bounds__(WG) void softmax_bw_vec(T *dinp, const T *dout,
+                                                     const T *__restrict__ y, int64_t rows,
+                                                     int32_t Tk) {
+    constexpr int V = Vec16<T>::N;
+    constexpr int RPB = WG / G;
+    const int lane = threadIdx.x % G;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / G;
+    const bool live = row < rows;
+    const int nvec = Tk / V;
+    const int64_t base = (live ? row : 0) * static_cast<int64_t>(Tk);
+
+    float yv[IT][V], gv[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (live && c < nvec) {
+            load_vec<T>(y + base + static_cast<int64_t>(c) * V, yv[k]);
+            load_vec<T>(dout + base + static_cast<int64_t>(c) * V, gv[k]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) yv[k][e] = gv[k][e] = 0.f;
+        }
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) t += yv[k][e] * gv[k][e];
+    t = group_allreduce<G>(t, OpSum());
+
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (live && c < nvec) {
+            float d[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = yv[k][e] * (gv[k][e] - t);
+            store_vec<T>(dinp + base + static_cast<int64_t>(c) * V, d);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Element-wise fallback kernels: one wave per row, any Tk, any element alignment.
+// ------------------------------------------------------------------------------------------
+constexpr int kGenericWG = 256;
+constexpr int kGenericRowsPerBlock = kGenericWG / 64;
+
+template <typename T>
+__device__ __forceinline__ float masked_score(const T *x, const T *m, int j, int qi, int causal) {
+    if (causal && j > qi) return -INFINITY;
+    float z = to_f32(x[j]);
+    if (m != nullptr) z += to_f32(m[j]);
+    return z;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGenericWG) void softmax_fw_generic(T *out, const T *inp,
+                                                                 const T *__restrict__ mask,
+                                                                 int64_t rows, int32_t Tq,
+                                                                 int32_t Tk,
+                                                                 int64_t rows_per_batch,
+                                                                 int32_t causal) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kGenericRowsPerBlock + (threadIdx.x >> 6);
+    const bool live = row < rows;  // uniform across the wave
+    const int64_t base = (live ? row : 0) * static_cast<int64_t>(Tk);
+    const T *x = inp + base;
+    const T *m = mask != nullptr ? mask + (live ? row / rows_per_batch : 0) * static_cast<int64_t>(Tk)
+                                 : nullptr;
+    const int qi = static_cast<int>(row % Tq);
+
+    float mx = -INFINITY;
+    if (live)
+        for (int j = lane; j < Tk; j += 64) mx = fmaxf(mx, masked_score(x, m, j, qi, causal));
+    mx = group_allreduce<64>(mx, OpMax());
+    if (mx == -INFINITY) mx = 0.f;
+    float s = 0.f;
+    if (live)
+        for (int j = lane; j < Tk; j += 64) s += exp_nonpos(masked_score(x, m, j, qi, causal) - mx);
+    s = group_allreduce<64>(s, OpSum());
+    const float inv = s > 0.f ? 1.0f / s : 0.f;
+    if (live)
+        for (int j = lane; j < Tk; j += 64)
+            out[base + j] = from_f32<T>(exp_nonpos(masked_score(x, m, j, qi, causal) - mx) * inv);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const T *dout,
+                                                                 const T *__restrict__ y,
+                                                                 int64_t rows, int32_t Tk) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kGenericRowsPerBlock + (threadIdx.x >> 6);
+    const bool live = row < rows;
+    const int64_t base = (live ? row : 0) * static_cast<int64_t>(Tk);
+    float t = 0.f;
+    if (live)
+        for (int j = lane; j < Tk; j += 64) t += to_f32(y[base + j]) * to_f32(dout[base + j]);
+    t = group_allreduce<64>(t, OpSum());
+    if (live)
+        for (int j = lane; j < Tk; j += 64) {
+            const float yj = to_f32(y[base + j]);
+            dinp[base + j] = from_f32<T>(yj * (to_f32(dout[base + j]) - t));
+        }
+}
+
+// ------------------------------------------------------------------------------------------
+// Row-length buckets: (G lanes per row, IT vectors per lane) for each storage type.
+// Capacity G * IT * V equals the bucket length; rows shorter than their bucket leave the
+// trailing vectors idle. The bucket lengths are the HW4 page's template list.
+// ------------------------------------------------------------------------------------------
+struct Plan {
+    int bucket;  // longest row this instantiation takes; 0 = element-wise fallback
+    int G;
+    int IT;
+};
+
+constexpr int kSoftmaxWG = 256;
+
+template <typename T> struct SoftmaxTable;
+template <> struct SoftmaxTable<f16> {   // V = 8
+    static constexpr Plan plans[] = {{32, 4, 1},   {64, 8, 1},   {128, 8, 2},
+                                     {256, 16, 2}, {384, 16, 3}, {512, 16, 4},
+                                     {768, 32, 3}, {1024, 32, 4}, {2048, 64, 4}};
+};
+template <> struct SoftmaxTable<float> { // V = 4
+    static constexpr Plan plans[] = {{32, 8, 1},   {64, 8, 2},   {128, 16, 2},
+                                     {256, 16, 4}, {384, 32, 3}, {512, 32, 4},
+                                     {768, 64, 3}, {1024, 64, 4}, {2048, 64, 8}};
+};
+
+struct SoftmaxFwArgs {
+    void *out;
+    const void *inp;
+    const void *mask;
+    int64_t rows;
+    int32_t Tq, Tk;
+    int64_t rows_per_batch;
+    int32_t causal;
+};
+struct SoftmaxBwArgs {
+    void *dinp;
+    const void *dout;
+    const void *y;
+    int64_t rows;
+    int32_t Tk;
+};
+
+template <typename T, int G, int IT>
+static hipError_t launch_fw_vec(const SoftmaxFwArgs &a, hipStream_t st) {
+    constexpr int RPB = kSoftmaxWG / G;
+    const int64_t blocks = (a.rows + RPB - 1) / RPB;
+    return launch(softmax_fw_vec<T, G, IT, kSoftmaxWG>, dim3(static_cast<uint32_t>(blocks)),
+                  dim3(kSoftmaxWG), st, static_cast<T *>(a.out), static_cast<const T *>(a.inp),
+                  static_cast<const T *>(a.mask), a.rows, a.Tq, a.Tk, a.rows_per_batch, a.causal);
+}
+
+template <typename T, int G, int IT>
+static hipError_t launch_bw_vec(const SoftmaxBwArgs &a, hipStream_t st) {
+    constexpr int RPB = kSoftmaxWG / G;
+    const int64_t blocks = (a.rows + RPB - 1) / RPB;
+    return launch(softmax_bw_vec<T, G, IT, kSoftmaxWG>, dim3(static_cast<uint32_t>(blocks)),
+                  dim3(kSoftmaxWG), st, static_cast<T *>(a.dinp), static_cast<const T *>(a.dout),
+                  static_cast<const T *>(a.y), a.rows, a.Tk);
+}
+
+// Compile-time walk over the bucket table: instantiate every (G, IT) and pick the first
+// bucket that holds Tk.
+template <typename T, int I>
+static hipError_t dispatch_fw(const SoftmaxFwArgs &a, hipStream_t st) {
+    constexpr Plan p = SoftmaxTable<T>::plans[I];
+    if (a.Tk <= p.bucket) return launch_fw_vec<T, p.G, p.IT>(a, st);
+    if constexpr (I + 1 < static_cast<int>(sizeof(SoftmaxTable<T>::plans) / sizeof(Plan)))
+        return dispatch_fw<T, I + 1>(a, st);
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int I>
+static hipError_t dispatch_bw(const SoftmaxBwArgs &a, hipStream_t st) {
+    constexpr Plan p = SoftmaxTable<T>::plans[I];
+    if (a.Tk <= p.bucket) return launch_bw_vec<T, p.G, p.IT>(a, st);
+    if constexpr (I + 1 < static_cast<int>(sizeof(SoftmaxTable<T>::plans) / sizeof(Plan)))
+        return dispatch_bw<T, I + 1>(a, st);
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+static Plan softmax_plan(int64_t Tk, bool vector_ok) {
+    if (vector_ok)
+        for (const Plan &p : SoftmaxTable<T>::plans)
+            if (Tk <= p.bucket) return p;
+    return Plan{0, 64, 0};
+}
+
+static int check_common(const void *a, const void *b, const void *c, int64_t B, int64_t H,
+                        int64_t Tq, int64_t Tk, lnr_dtype dtype) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (B < 0 || H < 0 || Tq < 0 || Tk < 1) return LNR_ERR_SHAPE;
+    if (Tk > LNR_SOFTMAX_MAX_TK) return LNR_ERR_UNSUPPORTED;
+    if (Tq > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    const int64_t rows = B * H * Tq;
+    if (rows == 0) return LNR_OK;
+    if (a == nullptr || b == nullptr || c == nullptr) return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned_to(a, es) || !aligned_to(b, es) || !aligned_to(c, es)) return LNR_ERR_ALIGN;
+    // Grid size limit of the fallback (4 rows per block) bounds every path.
+    if ((rows + kGenericRowsPerBlock - 1) / kGenericRowsPerBlock > INT32_MAX)
+        return LNR_ERR_UNSUPPORTED;
+    return LNR_OK;
+}
+
+}  // namespace lnr
+
+using namespace lnr;
+
+extern "C" int attn_softmax_fw(void *out, const void *inp, const void *mask, int64_t B,
+                               int64_t H, int64_t Tq, int64_t Tk, int causal, lnr_dtype dtype,
+                               void *stream) {
+    const void *mask_or_inp = mask != nullptr ? mask : inp;
+    int st = check_common(out, inp, mask_or_inp, B, H, Tq, Tk, dtype);
+    if (st != LNR_OK) return st;
+    if (causal && Tq != Tk) return LNR_ERR_SHAPE;
+    const int64_t rows = B * H * Tq;
+    if (rows == 0) return LNR_OK;
+    const size_t es = dtype_size(dtype);
+    const size_t nbytes = static_cast<size_t>(rows) * static_cast<size_t>(Tk) * es;
+    if (bad_alias(out, inp, nbytes)) return LNR_ERR_ALIAS;
+    if (mask != nullptr && overlap(out, nbytes, mask, static_cast<size_t>(B * Tk) * es))
+        return LNR_ERR_ALIAS;
+
+    SoftmaxFwArgs a{out, inp, mask, rows, static_cast<int32_t>(Tq), static_cast<int32_t>(Tk),
+                    H * Tq, causal ? 1 : 0};
+    const bool vec = (static_cast<size_t>(Tk) * es) % 16 == 0 && aligned_to(out, 16) &&
+                     aligned_to(inp, 16) && (mask == nullptr || aligned_to(mask, 16));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (vec) {
+        e = dtype == LNR_F16 ? dispatch_fw<f16, 0>(a, s) : dispatch_fw<float, 0>(a, s);
+    } else {
+        const dim3 grid(static_cast<uint32_t>((rows + kGenericRowsPerBlock - 1) / kGenericRowsPerBlock));
+        if (dtype == LNR_F16)
+            e = launch(softmax_fw_generic<f16>, grid, dim3(kGenericWG), s, static_cast<f16 *>(out),
+                       static_cast<const f16 *>(inp), static_cast<const f16 *>(mask), rows, a.Tq,
+                       a.Tk, a.rows_per_batch, a.causal);
+        else
+            e = launch(softmax_fw_generic<float>, grid, dim3(kGenericWG), s, static_cast<float *>(out),
+                       static_cast<const float *>(inp), static_cast<const float *>(mask), rows, a.Tq,
+                       a.Tk, a.rows_per_batch, a.causal);
+    }
+    return status_of(e);
+}
+
+extern "C" int attn_softmax_bw(void *dinp, const void *dout, const void *out_fw, int64_t B,
+                               int64_t H, int64_t Tq, int64_t Tk, lnr_dtype dtype, void *stream) {
+    int st = check_common(dinp, dout, out_fw, B, H, Tq, Tk, dtype);
+    if (st != LNR_OK) return st;
+    const int64_t rows = B * H * Tq;
+    if (rows == 0) return LNR_OK;
+    const size_t es = dtype_size(dtype);
+    const size_t nbytes = static_cast<size_t>(rows) * static_cast<size_t>(Tk) * es;
+    if (bad_alias(dinp, dout, nbytes) || overlap(dinp, nbytes, out_fw, nbytes)) return LNR_ERR_ALIAS;
+
+    SoftmaxBwArgs a{dinp, dout, out_fw, rows, static_cast<int32_t>(Tk)};
+    const bool vec = (static_cast<size_t>(Tk) * es) % 16 == 0 && aligned_to(dinp, 16) &&
+                     aligned_to(dout, 16) && aligned_to(out_fw, 16);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (vec) {
+        e = dtype == LNR_F16 ? dispatch_bw<f16, 0>(a, s) : dispatch_bw<float, 0>(a, s);
+    } else {
+        const dim3 grid(static_cast<uint32_t>((rows + kGenericRowsPerBlock - 1) / kGenericRowsPerBlock));
+        if (dtype == LNR_F16)
+            e = launch(softmax_bw_generic<f16>, grid, dim3(kGenericWG), s, static_cast<f16 *>(dinp),
+                       static_cast<const f16 *>(dout), static_cast<const f16 *>(out_fw), rows, a.Tk);
+        else
+            e = launch(softmax_bw_generic<float>, grid, dim3(kGenericWG), s, static_cast<float *>(dinp),
+                       static_cast<const float *>(dout), static_cast<const float *>(out_fw), rows, a.Tk);
+    }
+    return status_of(e);
+}
+
+// Introspection for tests and benchmarks: the bucket, lanes per row and vectors per lane
+// that attn_softmax_fw/bw use for (Tk, dtype) with aligned buffers; bucket 0 means the
+// element-wise fallback. Returns LNR_OK or the shape/dtype error of the call it mirrors.
+extern "C" int lnr_softmax_plan(int64_t Tk, lnr_dtype dtype, int *bucket, int *lanes_per_row,
+                                int *vectors_per_lane) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (Tk < 1) return LNR_ERR_SHAPE;
+    if (Tk > LNR_SOFTMAX_MAX_TK) return LNR_ERR_UNSUPPORTED;
+    if (bucket == nullptr || lanes_per_row == nullptr || vectors_per_lane == nullptr) return LNR_ERR_NULL;
+    const bool vec = (static_cast<size_t>(Tk) * dtype_size(dtype)) % 16 == 0;
+    const Plan p = dtype == LNR_F16 ? softmax_plan<f16>(Tk, vec) : softmax_plan<float>(Tk, vec);
+    *bucket = p.bucket;
+    *lanes_per_row = p.G;
+    *vectors_per_lane = p.IT;
+    return LNR_OK;
+}

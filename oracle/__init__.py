@@ -70,6 +70,8 @@ def _load():
     lib.lnr_oracle_layernorm_bw_dgamma_dbeta.argtypes = [d, d, i64, i64, ctypes.c_double, d, d, d, d]
     lib.lnr_oracle_rmsnorm_fw.argtypes = [d, d, i64, i64, ctypes.c_double, d, d]
     lib.lnr_oracle_rmsnorm_bw.argtypes = [d, d, d, i64, i64, ctypes.c_double, d, d]
+    lib.lnr_oracle_threads.argtypes = []
+    lib.lnr_oracle_threads.restype = ctypes.c_int
     for f in (lib.lnr_oracle_softmax_fw, lib.lnr_oracle_softmax_fw_rows, lib.lnr_oracle_softmax_bw,
               lib.lnr_oracle_layernorm_fw, lib.lnr_oracle_layernorm_bw_dx,
               lib.lnr_oracle_layernorm_bw_dgamma_dbeta, lib.lnr_oracle_rmsnorm_fw,
@@ -77,6 +79,11 @@ def _load():
         f.restype = None
     _lib = lib
     return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_load().lnr_oracle_threads())
 
 
 def _f64(a) -> np.ndarray:

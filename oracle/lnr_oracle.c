@@ -289,3 +289,16 @@ ORACLE_API void lnr_oracle_rmsnorm_bw(const double *x, const double *dy, const d
             dgamma[j] += dy[i * C + j] * (xr[j] / rms);
     }
 }
+
+/* Threads the OpenMP loops above will use (reported next to CPU timings). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+ORACLE_API int lnr_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,204 @@
+"""The C ABI on a host without a GPU: liblnr.so loads, exports every function that
+include/lnr.h declares, and rejects bad arguments with the documented status before it
+enqueues anything. No call here passes validation, so nothing reaches the device.
+
+The dispatcher introspection pins the row-length buckets to the template list printed on the
+HW4 page ("Problem structure and scoring").
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import layernorm_reduction_amd as lnr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lnr.h")
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_constants.json")))
+
+OK, NULL, SHAPE, UNSUP, DTYPE, ALIGN, ALIAS, WS = 0, 1, 2, 3, 4, 5, 6, 7
+F32, F16 = lnr.LNR_F32, lnr.LNR_F16
+A = 0x7F0000000000  # a fake, 256-byte aligned device address; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lnr.library_path()):
+        from layernorm_reduction_amd import build
+        build.build()
+    return lnr.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"#define[^\n]*", "", text)
+    return re.findall(r"LNR_API\s+[\w\s\*]*?\b(\w+)\s*\(", text)
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_and_build_info(lib):
+    for s in range(9):
+        assert lib.lnr_strerror(s)
+    assert b"unknown" in lib.lnr_strerror(99)
+    assert b"gfx950" in lib.lnr_build_info()
+
+
+# ------------------------------------------------------------------------- softmax checks
+
+def sfw(lib, out=A, inp=A + 2 ** 30, mask=None, B=2, H=2, Tq=16, Tk=16, causal=0, dtype=F16):
+    return lib.attn_softmax_fw(out, inp, mask, B, H, Tq, Tk, causal, dtype, None)
+
+
+def sbw(lib, dinp=A, dout=A + 2 ** 30, y=A + 2 ** 31, B=2, H=2, Tq=16, Tk=16, dtype=F16):
+    return lib.attn_softmax_bw(dinp, dout, y, B, H, Tq, Tk, dtype, None)
+
+
+def test_softmax_fw_validation(lib):
+    assert sfw(lib, dtype=7) == DTYPE
+    assert sfw(lib, Tk=0) == SHAPE
+    assert sfw(lib, B=-1) == SHAPE
+    assert sfw(lib, Tk=2049) == UNSUP
+    assert sfw(lib, out=None) == NULL
+    assert sfw(lib, inp=None) == NULL
+    assert sfw(lib, inp=A + 1) == ALIGN                      # odd address for fp16
+    assert sfw(lib, inp=A + 2, dtype=F32) == ALIGN
+    assert sfw(lib, Tq=8, causal=1) == SHAPE                 # causal needs Tq == Tk
+    assert sfw(lib, inp=A + 64) == ALIAS                     # partial overlap of out and inp
+    assert sfw(lib, mask=A + 128) == ALIAS                   # mask inside out
+    assert sfw(lib, B=0) == OK                               # empty: nothing to do
+    assert sfw(lib, out=None, inp=None, H=0) == OK
+
+
+def test_softmax_bw_validation(lib):
+    assert sbw(lib, dtype=2) == DTYPE
+    assert sbw(lib, Tk=-3) == SHAPE
+    assert sbw(lib, Tk=4096) == UNSUP
+    assert sbw(lib, y=None) == NULL
+    assert sbw(lib, dout=A + 2 ** 30 + 1) == ALIGN
+    assert sbw(lib, dout=A + 32) == ALIAS
+    assert sbw(lib, y=A + 16) == ALIAS                       # dinp may alias dout only
+    assert sbw(lib, Tq=0) == OK
+
+
+# ------------------------------------------------------------------------- LayerNorm checks
+
+def lfw(lib, y=A, mean=A + 2 ** 32, rstd=A + 2 ** 32 + 2 ** 20, x=A + 2 ** 30, g=A + 2 ** 31,
+        b=A + 2 ** 31 + 2 ** 20, N=64, C=64, eps=1e-8, dtype=F16):
+    return lib.layernorm_fw(y, mean, rstd, x, g, b, N, C, eps, dtype, None)
+
+
+def test_layernorm_fw_validation(lib):
+    assert lfw(lib, dtype=5) == DTYPE
+    assert lfw(lib, C=0) == SHAPE
+    assert lfw(lib, N=-2) == SHAPE
+    assert lfw(lib, C=8193) == UNSUP
+    assert lfw(lib, eps=-1.0) == SHAPE
+    assert lfw(lib, eps=float("nan")) == SHAPE
+    assert lfw(lib, mean=None) == NULL                       # mean and rstd: both or neither
+    assert lfw(lib, g=None) == NULL
+    assert lfw(lib, x=A + 2 ** 30 + 1) == ALIGN
+    assert lfw(lib, rstd=A + 2 ** 32 + 2 ** 20 + 2) == ALIGN
+    assert lfw(lib, x=A + 256) == ALIAS
+    assert lfw(lib, g=A + 512) == ALIAS
+    assert lfw(lib, N=0) == OK
+
+
+def lbw(lib, dx=A, dg=A + 2 ** 33, db=A + 2 ** 33 + 2 ** 20, dy=A + 2 ** 30, x=A + 2 ** 31,
+        g=A + 2 ** 32, mean=A + 2 ** 32 + 2 ** 20, rstd=A + 2 ** 32 + 2 ** 21, N=64, C=64,
+        dtype=F16, ws=A + 2 ** 34, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.layernorm_bw_workspace_bytes(N, C, dtype)
+    return lib.layernorm_bw(dx, dg, db, dy, x, g, mean, rstd, N, C, dtype, ws, ws_bytes, None)
+
+
+def test_layernorm_bw_validation(lib):
+    assert lbw(lib, dtype=9) == DTYPE
+    assert lbw(lib, C=0) == SHAPE
+    assert lbw(lib, C=10000) == UNSUP
+    assert lbw(lib, dg=None) == NULL
+    assert lbw(lib, mean=None) == NULL
+    assert lbw(lib, x=A + 2 ** 31 + 1) == ALIGN
+    assert lbw(lib, ws=A + 2 ** 34 + 4) == ALIGN
+    need = lib.layernorm_bw_workspace_bytes(64, 64, F16)
+    assert need > 0
+    assert lbw(lib, ws_bytes=need - 1) == WS
+    assert lbw(lib, ws=None) == WS
+    assert lbw(lib, dx=A + 2 ** 31) == ALIAS                 # dx over x
+    assert lbw(lib, dx=A + 2 ** 30 + 64) == ALIAS            # dx over dy
+    assert lbw(lib, db=A + 2 ** 33 + 2) == ALIAS             # dbeta over dgamma
+    assert lbw(lib, ws=A + 2 ** 30) == ALIAS                 # workspace over dy
+
+
+def test_workspace_bytes(lib):
+    assert lib.layernorm_bw_workspace_bytes(16384, 1024, F16) > 0
+    # fp32 storage accumulates the column partials in fp64: twice the bytes per partial.
+    n16 = lib.layernorm_bw_workspace_bytes(1000, 1000, F16)
+    n32 = lib.layernorm_bw_workspace_bytes(1000, 1000, F32)
+    assert n32 >= 2 * n16 * 0.99
+    assert lib.layernorm_bw_workspace_bytes(10, 0, F16) == 0
+    assert lib.layernorm_bw_workspace_bytes(10, 9000, F16) == 0
+    assert lib.layernorm_bw_workspace_bytes(10, 10, 3) == 0
+    assert lib.layernorm_bw_workspace_bytes(0, 10, F16) == 0
+
+
+def test_copy_validation(lib):
+    assert lib.lnr_copy(A, A + 2 ** 30, 15, None) == SHAPE
+    assert lib.lnr_copy(A + 8, A + 2 ** 30, 16, None) == ALIGN
+    assert lib.lnr_copy(A, A + 16, 64, None) == ALIAS
+    assert lib.lnr_copy(None, A, 16, None) == NULL
+    assert lib.lnr_copy(A, A + 2 ** 30, 0, None) == OK
+
+
+# ------------------------------------------------------------------------- dispatcher
+
+def test_softmax_buckets_are_the_pages_template_list(lib):
+    templates = GOLDEN["softmax_bw_row_length_templates"]["value"]
+    for dtype, V in ((F16, 8), (F32, 4)):
+        buckets = set()
+        for Tk in templates:
+            b, G, IT = lnr.softmax_plan(Tk, dtype)
+            assert b == Tk and G * IT * V == b, (dtype, Tk, b, G, IT)
+            assert G in (1, 2, 4, 8, 16, 32, 64)
+            buckets.add(b)
+        assert sorted(buckets) == templates
+        # lengths between templates take the next larger bucket; rows too short for a
+        # vector multiple take the element-wise fallback (bucket 0)
+        assert lnr.softmax_plan(264, dtype)[0] == 384
+        assert lnr.softmax_plan(2047, dtype)[0] == 0
+        assert lnr.softmax_plan(33, dtype)[0] == 0
+    assert lnr.softmax_plan(16, F16)[0] == 32
+    assert lnr.layernorm_plan(16, 100, F16)[0] == 0              # 200 B rows: fallback
+    assert lnr.layernorm_plan(16, 100, F32)[0] == 128            # 400 B rows: masked tail
+    # short rows (<= 32) pack several rows into one wavefront
+    assert lnr.softmax_plan(32, F16)[1] <= GOLDEN["short_row_threshold"]["value"] // 8
+
+
+def test_layernorm_buckets(lib):
+    for dtype, V in ((F16, 8), (F32, 4)):
+        for C in (64, 256, 768, 1024, 4096, 8192):
+            for bw in (False, True):
+                b, G, IT, WG, blocks = lnr.layernorm_plan(16384, C, dtype, backward=bw)
+                assert b == C and G * IT * V == C, (dtype, C, bw)
+                assert WG % G == 0 and WG % 64 == 0
+        assert lnr.layernorm_plan(16, 101, dtype)[0] == 0        # odd rows: fallback
+        assert lnr.layernorm_plan(16, 1000, F16)[0] == 1024      # 2000 B rows: masked tail
+    # the backward writes one partial row per workgroup: a few hundred for large N
+    assert 256 <= lnr.layernorm_plan(16384, 1024, F16, backward=True)[4] <= 1024
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 4)
+    with pytest.raises(ValueError):
+        lnr.attn_softmax_fw(x)
+    with pytest.raises(ValueError):
+        lnr.layernorm_fw(torch.zeros(4, 4), torch.ones(4), torch.zeros(4))
