@@ -169,10 +169,11 @@ LNR_API int lnr_copy(void *dst, const void *src, size_t bytes, void *stream);
  * choice at launch that the L10 lecture's "Technique 2" describes and the HW4 page's
  * softmax backward asks for): for rows of Tk elements of `dtype` in 16-byte-aligned
  * buffers, writes the bucket (the longest row of the chosen instantiation; 0 = element-wise
- * fallback), the lanes per row and the 16-byte vectors per lane. Touches no device.
+ * fallback), the lanes per row and the 16-byte vectors per lane of the forward (which = 0)
+ * or backward (which = 1) kernel. Touches no device.
  */
-LNR_API int lnr_softmax_plan(int64_t Tk, lnr_dtype dtype, int *bucket, int *lanes_per_row,
-                     int *vectors_per_lane);
+LNR_API int lnr_softmax_plan(int64_t Tk, lnr_dtype dtype, int which, int *bucket,
+                             int *lanes_per_row, int *vectors_per_lane);
 
 /*
  * lnr_layernorm_plan -- the same for LayerNorm rows of C elements: `which` = 0 for the

@@ -74,7 +74,7 @@ def load():
     lib.lnr_strerror.restype = ctypes.c_char_p
     lib.lnr_build_info.restype = ctypes.c_char_p
     ip = ctypes.POINTER(ctypes.c_int)
-    lib.lnr_softmax_plan.argtypes = [i64, ci, ip, ip, ip]
+    lib.lnr_softmax_plan.argtypes = [i64, ci, ci, ip, ip, ip]
     lib.lnr_layernorm_plan.argtypes = [i64, i64, ci, ci, ip, ip, ip, ip, ctypes.POINTER(i64)]
     for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw", "lnr_copy",
               "lnr_softmax_plan", "lnr_layernorm_plan"):
@@ -280,12 +280,12 @@ def copy_bytes(dst, src):
     return dst
 
 
-def softmax_plan(Tk: int, dtype_code: int):
-    """(bucket, lanes per row, 16-byte vectors per lane) for aligned buffers; bucket 0 means
-    the element-wise fallback."""
+def softmax_plan(Tk: int, dtype_code: int, backward: bool = False):
+    """(bucket, lanes per row, 16-byte vectors per lane) of the forward or backward kernel for
+    aligned buffers; bucket 0 means the element-wise fallback."""
     b, g, it = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(load().lnr_softmax_plan(int(Tk), int(dtype_code), ctypes.byref(b), ctypes.byref(g),
-                                   ctypes.byref(it)), "lnr_softmax_plan")
+    _check(load().lnr_softmax_plan(int(Tk), int(dtype_code), int(bool(backward)), ctypes.byref(b),
+                                   ctypes.byref(g), ctypes.byref(it)), "lnr_softmax_plan")
     return b.value, g.value, it.value
 
 

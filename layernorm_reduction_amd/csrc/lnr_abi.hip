@@ -5,12 +5,25 @@
 
 namespace lnr {
 
-// Grid-stride copy with the same 16-byte accesses as the row kernels.
-__global__ __launch_bounds__(256) void copy16(f32x4 *__restrict__ dst,
-                                               const f32x4 *__restrict__ src, int64_t n) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
-        dst[i] = src[i];
+// Streaming copy with the same non-temporal 16-byte accesses as the row kernels: each thread issues
+// kCopyUnroll independent loads before its stores, so enough bytes are in flight per CU.
+constexpr int kCopyUnroll = 4;
+constexpr int kCopyWG = 256;
+
+__global__ __launch_bounds__(kCopyWG) void copy16(f32x4 *__restrict__ dst,
+                                                   const f32x4 *__restrict__ src, int64_t n) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyWG * kCopyUnroll + threadIdx.x;
+    f32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kCopyWG;
+        if (i < n) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kCopyWG;
+        if (i < n) __builtin_nontemporal_store(v[u], dst + i);
+    }
 }
 
 }  // namespace lnr
@@ -24,10 +37,10 @@ extern "C" int lnr_copy(void *dst, const void *src, size_t bytes, void *stream) 
     if (!aligned_to(dst, 16) || !aligned_to(src, 16)) return LNR_ERR_ALIGN;
     if (overlap(dst, bytes, src, bytes)) return LNR_ERR_ALIAS;
     const int64_t n = static_cast<int64_t>(bytes / 16);
-    // 8 workgroups of 256 threads per CU on 256 CUs, each thread looping over the rest.
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
-    return status_of(launch(copy16, dim3(static_cast<uint32_t>(blocks)), dim3(256),
+    const int64_t per_block = static_cast<int64_t>(kCopyWG) * kCopyUnroll;
+    const int64_t blocks = (n + per_block - 1) / per_block;
+    if (blocks > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    return status_of(launch(copy16, dim3(static_cast<uint32_t>(blocks)), dim3(kCopyWG),
                             static_cast<hipStream_t>(stream), static_cast<f32x4 *>(dst),
                             static_cast<const f32x4 *>(src), n));
 }

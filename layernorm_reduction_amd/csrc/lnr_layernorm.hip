@@ -32,68 +32,110 @@ template <typename T> struct Accum;
 template <> struct Accum<f16> { using type = float; };
 template <> struct Accum<float> { using type = double; };
 
-__device__ __forceinline__ float ln_rstd(float s1, float s2, int C, float eps, float &mu) {
-    mu = s1 / static_cast<float>(C);
-    const float var = fmaxf(s2 / static_cast<float>(C) - mu * mu, 0.f);
+// Statistics from the one fused pass. The two sums are taken over d = x - K, with K the
+// row's first element: mu(d^2) - mu(d)^2 equals the variance of x for any shift K, and a
+// shift near the mean removes the cancellation that fp32 one-pass sums suffer when the
+// variance is small next to mean^2. xhat is then formed as (d - mu(d)) * rstd, so no
+// rounding of K + mu(d) enters it. No contraction here: a constant row (or C = 1) gives
+// s1 = s2 = 0 and therefore a variance of exactly 0.
+__device__ __forceinline__ float ln_stats(float s1, float s2, int C, float eps, float &m1) {
+#pragma clang fp contract(off)
+    m1 = s1 / static_cast<float>(C);
+    const float var = fmaxf(s2 / static_cast<float>(C) - m1 * m1, 0.f);
     return 1.0f / sqrtf(var + eps);
 }
 
 // ------------------------------------------------------------------------------------------
-// Forward, vector path.
+// Forward, vector path. Workgroup b normalises rows [b*R, (b+1)*R) with R = rows_per_block;
+// group g of the workgroup takes rows b*R + g, b*R + g + NG, ... gamma and beta are loaded
+// once per workgroup. The next row's vectors (and its shift K) are fetched before the
+// current row is reduced, so each wave keeps a row of loads in flight while it computes;
+// the fetch is issued unconditionally (an idle lane reads a vector that always exists) so
+// that no branch makes the compiler drain the loads early.
 // ------------------------------------------------------------------------------------------
 template <typename T, int G, int IT, int WG>
 __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__ mean,
                                                        float *__restrict__ rstd, const T *x,
                                                        const T *__restrict__ gamma,
                                                        const T *__restrict__ beta, int64_t N,
-                                                       int32_t C, float eps) {
+                                                       int32_t C, float eps,
+                                                       int64_t rows_per_block) {
+    using RV = RawVec<T>;
     constexpr int V = Vec16<T>::N;
-    constexpr int RPB = WG / G;
+    constexpr int NG = WG / G;
     __shared__ float red[2 * (WG / 64)];
     const int lane = threadIdx.x % G;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / G;
-    const bool live = row < N;
+    const int grp = threadIdx.x / G;
     const int nvec = C / V;
-    const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+    const int64_t r1 = (r0 + rows_per_block < N) ? r0 + rows_per_block : N;
+    const RV zero = {};
 
-    float v[IT][V];
+    float gm[IT][V], bt[IT][V];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
-        if (live && c < nvec) {
-            load_vec<T>(x + base + static_cast<int64_t>(c) * V, v[k]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) v[k][e] = 0.f;
-        }
+        const int cc = c < nvec ? c : 0;
+        widen<T>(load_keep_raw<T>(gamma + cc * V), gm[k]);
+        widen<T>(load_keep_raw<T>(beta + cc * V), bt[k]);
     }
-    float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-    for (int k = 0; k < IT; ++k)
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-            s1 += v[k][e];
-            s2 += v[k][e] * v[k][e];
-        }
-    row_allreduce_sum2<G>(s1, s2, red);
-    float mu;
-    const float rs = ln_rstd(s1, s2, C, eps, mu);
 
+    const int64_t iters = (rows_per_block + NG - 1) / NG;
+    RV xn[IT];
+    float Kn;
+    auto fetch = [&](int64_t row, bool live) {
+        const int64_t rbase = (live ? row : r0) * static_cast<int64_t>(C);
 #pragma unroll
-    for (int k = 0; k < IT; ++k) {
-        const int c = k * G + lane;
-        if (live && c < nvec) {
-            float g[V], b[V], o[V];
-            load_vec<T>(gamma + c * V, g);
-            load_vec<T>(beta + c * V, b);
-#pragma unroll
-            for (int e = 0; e < V; ++e) o[e] = (v[k][e] - mu) * rs * g[e] + b[e];
-            store_vec<T>(y + base + static_cast<int64_t>(c) * V, o);
+        for (int k = 0; k < IT; ++k) {
+            const int c = k * G + lane;
+            const bool ok = live && c < nvec;
+            const RV l = load_stream_raw<T>(x + rbase + (ok ? static_cast<int64_t>(c) * V : 0));
+            xn[k] = ok ? l : zero;
         }
-    }
-    if (live && lane == 0 && mean != nullptr) {
-        mean[row] = mu;
-        rstd[row] = rs;
+        const float kl = to_f32(x[rbase]);  // the shift: one broadcast load per group
+        Kn = live ? kl : 0.f;
+    };
+    fetch(r0 + grp, r0 + grp < r1);
+    for (int64_t it = 0; it < iters; ++it) {
+        const int64_t row = r0 + it * NG + grp;
+        const bool live = row < r1;
+        RV xc[IT];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) xc[k] = xn[k];
+        const float K = Kn;
+        fetch(row + NG, it + 1 < iters && row + NG < r1);
+
+        float d[IT][V];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            widen<T>(xc[k], d[k]);
+            const bool ok = k * G + lane < nvec;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                d[k][e] = ok ? d[k][e] - K : 0.f;
+                s1 += d[k][e];
+                s2 += d[k][e] * d[k][e];
+            }
+        }
+        row_allreduce_sum2<G>(s1, s2, red);
+        float m1;
+        const float rs = ln_stats(s1, s2, C, eps, m1);
+        const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int c = k * G + lane;
+            if (live && c < nvec) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) o[e] = (d[k][e] - m1) * rs * gm[k][e] + bt[k][e];
+                store_stream<T>(y + base + static_cast<int64_t>(c) * V, o);
+            }
+        }
+        if (live && lane == 0 && mean != nullptr) {
+            mean[row] = K + m1;
+            rstd[row] = rs;
+        }
     }
 }
 
@@ -101,7 +143,7 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
 // Backward, vector path: dx plus per-workgroup dgamma/dbeta column partials.
 // part layout: [P][2][C] of Accum<T>; slot 0 = dgamma, slot 1 = dbeta.
 // ------------------------------------------------------------------------------------------
-template <typename T, int G, int IT, int WG>
+template <typename T, int G, int IT, int WG, int DEPTH>
 __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>::type *part,
                                                        const T *dy, const T *x,
                                                        const T *__restrict__ gamma,
@@ -109,11 +151,14 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
                                                        const float *__restrict__ rstd,
                                                        int64_t N, int32_t C,
                                                        int64_t rows_per_block) {
+#pragma clang fp contract(off)
+    static_assert(DEPTH == 1 || DEPTH == 2, "rows fetched ahead: 1 or 2");
     using A = typename Accum<T>::type;
+    using RV = RawVec<T>;
     constexpr int V = Vec16<T>::N;
     constexpr int NG = WG / G;  // row groups per workgroup
     __shared__ float red[2 * (WG / 64)];
-    __shared__ A tile[2][NG > 1 ? NG : 1][NG > 1 ? G * V : 1];
+    __shared__ A tile[NG > 1 ? NG : 1][NG > 1 ? G * V : 1];
 
     const int lane = threadIdx.x % G;
     const int grp = threadIdx.x / G;
@@ -121,70 +166,112 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block;
     const int64_t r1 = (r0 + rows_per_block < N) ? r0 + rows_per_block : N;
     const float invC = 1.0f / static_cast<float>(C);
+    const RV zero = {};
 
-    float gm[IT][V];
+    RV gmr[IT];  // gamma, kept as stored (16 bytes per vector) to save registers
     A adg[IT][V], adb[IT][V];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
-        if (c < nvec) {
-            load_vec<T>(gamma + c * V, gm[k]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) gm[k][e] = 0.f;
-        }
+        const RV gl = load_keep_raw<T>(gamma + (c < nvec ? c : 0) * V);
+        gmr[k] = c < nvec ? gl : zero;
 #pragma unroll
         for (int e = 0; e < V; ++e) adg[k][e] = adb[k][e] = A(0);
     }
 
-    // Same trip count for every group so that multi-wave rows can use barriers.
+    // Group `grp` takes rows r0 + grp, r0 + grp + NG, ... (iteration `it` -> r0 + it*NG + grp).
+    // A row buffer holds one row's x and dy vectors (as stored) plus its mean and rstd.
+    // DEPTH rows are fetched ahead of the one being reduced, so every wave keeps DEPTH rows
+    // of loads in flight while it computes. With DEPTH = 2 three buffers rotate through an
+    // unrolled loop (no register copies). Fetches are issued unconditionally (an idle lane
+    // reads the block's first row, which always exists) and idle values are zeroed: with no
+    // branch around the loads the compiler keeps them outstanding. Iterations past the last
+    // row are idle rows of zeros, so every group runs the same trip count and multi-wave rows
+    // can use barriers.
+    struct RowBuf {
+        RV xv[IT], dv[IT];
+        float mu, rs;
+    };
     const int64_t iters = (rows_per_block + NG - 1) / NG;
-    for (int64_t it = 0; it < iters; ++it) {
+    auto fetch = [&](RowBuf &b, int64_t it) {
         const int64_t row = r0 + it * NG + grp;
-        const bool live = row < r1;
-        const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
-        float xv[IT][V], dv[IT][V];
+        const bool live = it < iters && row < r1;
+        const int64_t rbase = (live ? row : r0) * static_cast<int64_t>(C);
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int c = k * G + lane;
-            if (live && c < nvec) {
-                load_vec<T>(x + base + static_cast<int64_t>(c) * V, xv[k]);
-                load_vec<T>(dy + base + static_cast<int64_t>(c) * V, dv[k]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) xv[k][e] = dv[k][e] = 0.f;
-            }
+            const bool ok = live && c < nvec;
+            const int64_t off = rbase + (ok ? static_cast<int64_t>(c) * V : 0);
+            const RV xl = load_stream_raw<T>(x + off);
+            const RV dl = load_stream_raw<T>(dy + off);
+            b.xv[k] = ok ? xl : zero;
+            b.dv[k] = ok ? dl : zero;
         }
-        const float mu = live ? mean[row] : 0.f;
-        const float rs = live ? rstd[row] : 0.f;
+        const int64_t srow = live ? row : r0;
+        const float ml = mean[srow], rl = rstd[srow];
+        b.mu = live ? ml : 0.f;
+        b.rs = live ? rl : 0.f;
+    };
+    auto process = [&](const RowBuf &b, int64_t it) {
+        const int64_t row = r0 + it * NG + grp;
+        const bool live = it < iters && row < r1;
+        const float mu = b.mu, rs = b.rs;
+        // First pass: xhat, g = gamma*dy, the fused pair of row sums, and the column
+        // partials. g is rounded once and that same value enters both the row sum and dx,
+        // so a row whose exact gradient is zero (C = 1, or g constant with xhat = 0) gives
+        // exactly zero even when rstd is as large as 1/sqrt(eps).
+        float xh[IT][V], gv[IT][V];
         float sg = 0.f, sgx = 0.f;
 #pragma unroll
-        for (int k = 0; k < IT; ++k)
+        for (int k = 0; k < IT; ++k) {
+            float xf[V], df[V], gmf[V];
+            widen<T>(b.xv[k], xf);
+            widen<T>(b.dv[k], df);
+            widen<T>(gmr[k], gmf);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float xh = (xv[k][e] - mu) * rs;
-                const float g = gm[k][e] * dv[k][e];
-                xv[k][e] = xh;
-                sg += g;
-                sgx += g * xh;
+                xh[k][e] = (xf[e] - mu) * rs;
+                gv[k][e] = gmf[e] * df[e];
+                sg += gv[k][e];
+                sgx = __builtin_fmaf(gv[k][e], xh[k][e], sgx);
+                adg[k][e] += static_cast<A>(df[e] * xh[k][e]);
+                adb[k][e] += static_cast<A>(df[e]);
             }
+        }
         row_allreduce_sum2<G>(sg, sgx, red);
-        const float a = sg * invC, b = sgx * invC;
+        const float a = sg * invC, bb = sgx * invC;
+        const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int c = k * G + lane;
             if (live && c < nvec) {
                 float o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    o[e] = rs * (gm[k][e] * dv[k][e] - a - xv[k][e] * b);
-                store_vec<T>(dx + base + static_cast<int64_t>(c) * V, o);
+                for (int e = 0; e < V; ++e) o[e] = rs * __builtin_fmaf(-xh[k][e], bb, gv[k][e] - a);
+                store_stream<T>(dx + base + static_cast<int64_t>(c) * V, o);
             }
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                adg[k][e] += static_cast<A>(dv[k][e] * xv[k][e]);
-                adb[k][e] += static_cast<A>(dv[k][e]);
-            }
+        }
+    };
+
+    if constexpr (DEPTH == 1) {
+        RowBuf nb, cb;
+        fetch(nb, 0);
+        for (int64_t it = 0; it < iters; ++it) {
+            cb = nb;
+            fetch(nb, it + 1);
+            process(cb, it);
+        }
+    } else {
+        RowBuf b0, b1, b2;
+        fetch(b0, 0);
+        fetch(b1, 1);
+        for (int64_t it = 0; it < iters; it += 3) {
+            fetch(b2, it + 2);
+            process(b0, it);
+            fetch(b0, it + 3);
+            process(b1, it + 1);
+            fetch(b1, it + 4);
+            process(b2, it + 2);
         }
     }
 
@@ -203,26 +290,24 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
             }
         }
     } else {
-        // LDS column tile: for vector slot k, every group stages its G*V columns, then the
-        // workgroup sums the NG groups of each column in group order.
+        // LDS column tile: for vector slot k and for dgamma then dbeta, every group stages its
+        // G*V columns, then the workgroup sums the NG groups of each column in group order.
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                tile[0][grp][lane * V + e] = adg[k][e];
-                tile[1][grp][lane * V + e] = adb[k][e];
-            }
-            __syncthreads();
-            for (int idx = threadIdx.x; idx < 2 * G * V; idx += WG) {
-                const int which = idx / (G * V);
-                const int cc = idx % (G * V);
-                A s = tile[which][0][cc];
+            for (int which = 0; which < 2; ++which) {
 #pragma unroll
-                for (int g = 1; g < NG; ++g) s += tile[which][g][cc];
-                const int col = k * G * V + cc;
-                if (col < C) (which == 0 ? pg : pb)[col] = s;
+                for (int e = 0; e < V; ++e) tile[grp][lane * V + e] = which == 0 ? adg[k][e] : adb[k][e];
+                __syncthreads();
+                for (int cc = threadIdx.x; cc < G * V; cc += WG) {
+                    A s = tile[0][cc];
+#pragma unroll
+                    for (int g = 1; g < NG; ++g) s += tile[g][cc];
+                    const int col = k * G * V + cc;
+                    if (col < C) (which == 0 ? pg : pb)[col] = s;
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
 }
@@ -272,20 +357,21 @@ __global__ __launch_bounds__(kLnGenericWG) void layernorm_fw_generic(
     __shared__ float red[2 * (kLnGenericWG / 64)];
     const int64_t row = blockIdx.x;
     const T *xr = x + row * static_cast<int64_t>(C);
+    const float K = to_f32(xr[0]);
     float s1 = 0.f, s2 = 0.f;
     for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
-        const float v = to_f32(xr[j]);
-        s1 += v;
-        s2 += v * v;
+        const float d = to_f32(xr[j]) - K;
+        s1 += d;
+        s2 += d * d;
     }
     row_allreduce_sum2<kLnGenericWG>(s1, s2, red);
-    float mu;
-    const float rs = ln_rstd(s1, s2, C, eps, mu);
+    float m1;
+    const float rs = ln_stats(s1, s2, C, eps, m1);
     T *yr = y + row * static_cast<int64_t>(C);
     for (int j = threadIdx.x; j < C; j += kLnGenericWG)
-        yr[j] = from_f32<T>((to_f32(xr[j]) - mu) * rs * to_f32(gamma[j]) + to_f32(beta[j]));
+        yr[j] = from_f32<T>(((to_f32(xr[j]) - K) - m1) * rs * to_f32(gamma[j]) + to_f32(beta[j]));
     if (threadIdx.x == 0 && mean != nullptr) {
-        mean[row] = mu;
+        mean[row] = K + m1;
         rstd[row] = rs;
     }
 }
@@ -294,6 +380,7 @@ template <typename T>
 __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_dx_generic(
     T *dx, const T *dy, const T *x, const T *__restrict__ gamma, const float *__restrict__ mean,
     const float *__restrict__ rstd, int64_t N, int32_t C) {
+#pragma clang fp contract(off)
     __shared__ float red[2 * (kLnGenericWG / 64)];
     const int64_t row = blockIdx.x;
     const int64_t base = row * static_cast<int64_t>(C);
@@ -303,7 +390,7 @@ __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_dx_generic(
         const float xh = (to_f32(x[base + j]) - mu) * rs;
         const float g = to_f32(gamma[j]) * to_f32(dy[base + j]);
         sg += g;
-        sgx += g * xh;
+        sgx = __builtin_fmaf(g, xh, sgx);
     }
     row_allreduce_sum2<kLnGenericWG>(sg, sgx, red);
     const float invC = 1.0f / static_cast<float>(C);
@@ -311,7 +398,7 @@ __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_dx_generic(
     for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
         const float xh = (to_f32(x[base + j]) - mu) * rs;
         const float g = to_f32(gamma[j]) * to_f32(dy[base + j]);
-        dx[base + j] = from_f32<T>(rs * (g - a - xh * b));
+        dx[base + j] = from_f32<T>(rs * __builtin_fmaf(-xh, b, g - a));
     }
 }
 
@@ -342,37 +429,43 @@ struct LnPlan {
     int bucket;  // widest row this instantiation takes
     int G;       // lanes per row (multiples of 64 above one wave)
     int IT;      // 16-byte vectors per lane
+    int WG;      // workgroup size
+    int R;       // forward: rows per row group per workgroup (1 = one row each);
+                 // backward: rows fetched ahead of the row being reduced (1 or 2)
 };
 
+// Measured on MI355X (fp16, N = 8192..32768): both LayerNorm kernels run best with one or
+// two 16-byte vectors per lane and as many lanes per row as that gives (several waves per row
+// from 2048 columns up). The forward gains from a row loop (R rows per group) once rows reach
+// 1024 columns; the backward gains from fetching two rows ahead once rows reach 4096.
 template <typename T> struct LnFwTable;
 template <> struct LnFwTable<f16> {  // V = 8
-    static constexpr LnPlan plans[] = {{64, 8, 1},    {128, 16, 1},  {256, 16, 2},
-                                       {512, 16, 4},  {768, 32, 3},  {1024, 32, 4},
-                                       {2048, 64, 4}, {4096, 128, 4}, {8192, 256, 4}};
+    static constexpr LnPlan plans[] = {
+        {64, 8, 1, 256, 1},     {128, 16, 1, 256, 1},   {256, 16, 2, 128, 1},
+        {512, 32, 2, 256, 2},   {768, 32, 3, 256, 2},   {1024, 64, 2, 128, 2},
+        {2048, 128, 2, 256, 2}, {4096, 256, 2, 256, 4}, {8192, 512, 2, 512, 4}};
 };
 template <> struct LnFwTable<float> {  // V = 4
-    static constexpr LnPlan plans[] = {{64, 16, 1},    {128, 16, 2},   {256, 16, 4},
-                                       {512, 32, 4},   {768, 64, 3},   {1024, 64, 4},
-                                       {2048, 128, 4}, {4096, 256, 4}, {8192, 512, 4}};
+    static constexpr LnPlan plans[] = {
+        {64, 16, 1, 256, 1},    {128, 16, 2, 256, 1},   {256, 32, 2, 128, 1},
+        {512, 64, 2, 256, 2},   {768, 64, 3, 256, 2},   {1024, 128, 2, 256, 2},
+        {2048, 256, 2, 256, 2}, {4096, 512, 2, 512, 4}, {8192, 1024, 2, 1024, 4}};
 };
 template <typename T> struct LnBwTable;
 template <> struct LnBwTable<f16> {
-    static constexpr LnPlan plans[] = {{64, 8, 1},     {128, 16, 1},   {256, 32, 1},
-                                       {512, 64, 1},   {768, 32, 3},   {1024, 64, 2},
-                                       {2048, 128, 2}, {4096, 256, 2}, {8192, 512, 2}};
+    static constexpr LnPlan plans[] = {
+        {64, 8, 1, 512, 1},      {128, 16, 1, 512, 1},    {256, 32, 1, 512, 1},
+        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 128, 1, 1024, 1},
+        {2048, 256, 1, 1024, 1}, {4096, 256, 2, 512, 2},  {8192, 512, 2, 512, 2}};
 };
 template <> struct LnBwTable<float> {
-    static constexpr LnPlan plans[] = {{64, 16, 1},    {128, 32, 1},   {256, 64, 1},
-                                       {512, 64, 2},   {768, 64, 3},   {1024, 128, 2},
-                                       {2048, 256, 2}, {4096, 512, 2}, {8192, 1024, 2}};
+    static constexpr LnPlan plans[] = {
+        {64, 16, 1, 512, 1},     {128, 32, 1, 512, 1},    {256, 64, 1, 512, 1},
+        {512, 128, 1, 512, 1},   {768, 64, 3, 512, 1},    {1024, 256, 1, 1024, 1},
+        {2048, 512, 1, 1024, 1}, {4096, 512, 2, 512, 2},  {8192, 1024, 2, 1024, 1}};
 };
 
-constexpr int kLnFwMinWG = 256;
-constexpr int kLnBwMinWG = 512;
-constexpr int64_t kLnBwTargetBlocks = 512;  // two 512-thread workgroups per CU on 256 CUs
-
-constexpr int ln_fw_wg(int G) { return G > kLnFwMinWG ? G : kLnFwMinWG; }
-constexpr int ln_bw_wg(int G) { return G > kLnBwMinWG ? G : kLnBwMinWG; }
+constexpr int64_t kLnBwTargetBlocks = 256;  // one partial row per CU
 
 template <typename Table>
 static bool find_plan(int64_t C, LnPlan &out) {
@@ -398,7 +491,7 @@ static void bw_partials(int64_t N, int64_t C, lnr_dtype dtype, int64_t &p_vec, i
                         int64_t &rpb_vec, int64_t &rpb_gen) {
     LnPlan p{};
     const bool ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, p) : find_plan<LnBwTable<float>>(C, p);
-    const int64_t groups = ok ? ln_bw_wg(p.G) / p.G : 1;
+    const int64_t groups = ok ? p.WG / p.G : 1;
     rpb_vec = bw_rows_per_block(N, groups);
     p_vec = bw_blocks(N, rpb_vec);
     rpb_gen = bw_rows_per_block(N, 1);
@@ -429,13 +522,13 @@ template <typename T, int I>
 static hipError_t dispatch_ln_fw(const LnFwArgs &a, hipStream_t st) {
     constexpr LnPlan p = LnFwTable<T>::plans[I];
     if (a.C <= p.bucket) {
-        constexpr int WG = ln_fw_wg(p.G);
-        constexpr int RPB = WG / p.G;
+        static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && p.R >= 1, "bad forward plan");
+        constexpr int64_t RPB = static_cast<int64_t>(p.WG / p.G) * p.R;
         const int64_t blocks = (a.N + RPB - 1) / RPB;
-        return launch(layernorm_fw_vec<T, p.G, p.IT, WG>, dim3(static_cast<uint32_t>(blocks)), dim3(WG),
-                      st, static_cast<T *>(a.y), a.mean, a.rstd, static_cast<const T *>(a.x),
-                      static_cast<const T *>(a.gamma), static_cast<const T *>(a.beta), a.N, a.C,
-                      a.eps);
+        return launch(layernorm_fw_vec<T, p.G, p.IT, p.WG>, dim3(static_cast<uint32_t>(blocks)),
+                      dim3(p.WG), st, static_cast<T *>(a.y), a.mean, a.rstd,
+                      static_cast<const T *>(a.x), static_cast<const T *>(a.gamma),
+                      static_cast<const T *>(a.beta), a.N, a.C, a.eps, RPB);
     }
     if constexpr (I + 1 < static_cast<int>(sizeof(LnFwTable<T>::plans) / sizeof(LnPlan)))
         return dispatch_ln_fw<T, I + 1>(a, st);
@@ -446,9 +539,10 @@ template <typename T, int I>
 static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
     constexpr LnPlan p = LnBwTable<T>::plans[I];
     if (a.C <= p.bucket) {
-        constexpr int WG = ln_bw_wg(p.G);
-        return launch(layernorm_bw_vec<T, p.G, p.IT, WG>, dim3(static_cast<uint32_t>(a.blocks)),
-                      dim3(WG), st, static_cast<T *>(a.dx),
+        static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && (p.R == 1 || p.R == 2), "bad backward plan");
+        static_assert(2 * (p.WG / 64) >= 2, "reduction slots");
+        return launch(layernorm_bw_vec<T, p.G, p.IT, p.WG, p.R>, dim3(static_cast<uint32_t>(a.blocks)),
+                      dim3(p.WG), st, static_cast<T *>(a.dx),
                       static_cast<typename Accum<T>::type *>(a.part), static_cast<const T *>(a.dy),
                       static_cast<const T *>(a.x), static_cast<const T *>(a.gamma), a.mean, a.rstd,
                       a.N, a.C, a.rows_per_block);
@@ -614,7 +708,7 @@ extern "C" int lnr_layernorm_plan(int64_t N, int64_t C, lnr_dtype dtype, int whi
     if (C > LNR_LAYERNORM_MAX_C) return LNR_ERR_UNSUPPORTED;
     if (!bucket || !lanes_per_row || !vectors_per_lane || !workgroup || !blocks) return LNR_ERR_NULL;
     const bool vec = (static_cast<size_t>(C) * dtype_size(dtype)) % 16 == 0;
-    LnPlan p{0, kLnGenericWG, 0};
+    LnPlan p{0, kLnGenericWG, 0, kLnGenericWG, 1};
     bool ok = false;
     if (vec) {
         if (which == 0)
@@ -622,17 +716,18 @@ extern "C" int lnr_layernorm_plan(int64_t N, int64_t C, lnr_dtype dtype, int whi
         else
             ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, p) : find_plan<LnBwTable<float>>(C, p);
     }
-    if (!ok) p = LnPlan{0, kLnGenericWG, 0};
+    if (!ok) p = LnPlan{0, kLnGenericWG, 0, kLnGenericWG, 1};
     *bucket = p.bucket;
     *lanes_per_row = p.G;
     *vectors_per_lane = p.IT;
     int64_t pv, pg, rv, rg;
     bw_partials(N, C, dtype, pv, pg, rv, rg);
     if (which == 0) {
-        *workgroup = ok ? ln_fw_wg(p.G) : kLnGenericWG;
-        *blocks = ok ? (N + (*workgroup / p.G) - 1) / (*workgroup / p.G) : N;
+        *workgroup = ok ? p.WG : kLnGenericWG;
+        const int64_t rpb = ok ? static_cast<int64_t>(p.WG / p.G) * p.R : 1;
+        *blocks = (N + rpb - 1) / rpb;
     } else {
-        *workgroup = ok ? ln_bw_wg(p.G) : kLnGenericWG;
+        *workgroup = ok ? p.WG : kLnGenericWG;
         *blocks = ok ? pv : pg;
     }
     return LNR_OK;

@@ -34,23 +34,44 @@ template <> struct Vec16<f16> {
     static constexpr int N = 8;
 };
 
-// Load one 16-byte vector and widen it to fp32.
+// Two cache policies. Row data is streamed: every score, activation and gradient byte is
+// read once and written once, so those accesses are non-temporal and do not evict lines
+// that are reused. Small tensors that every row reads again (the key mask, gamma, beta)
+// use ordinary cached loads.
+template <typename T> using RawVec = typename Vec16<T>::type;
+
 template <typename T>
-__device__ __forceinline__ void load_vec(const T *p, float (&out)[Vec16<T>::N]) {
-    using V = typename Vec16<T>::type;
-    const V v = *reinterpret_cast<const V *>(p);
+__device__ __forceinline__ RawVec<T> load_stream_raw(const T *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const RawVec<T> *>(p));
+}
+template <typename T>
+__device__ __forceinline__ RawVec<T> load_keep_raw(const T *p) {
+    return *reinterpret_cast<const RawVec<T> *>(p);
+}
+
+// Widen a 16-byte vector to fp32.
+template <typename T>
+__device__ __forceinline__ void widen(const RawVec<T> &v, float (&out)[Vec16<T>::N]) {
 #pragma unroll
     for (int e = 0; e < Vec16<T>::N; ++e) out[e] = static_cast<float>(v[e]);
 }
 
-// Round fp32 values to T (nearest even) and store them as one 16-byte vector.
 template <typename T>
-__device__ __forceinline__ void store_vec(T *p, const float (&in)[Vec16<T>::N]) {
-    using V = typename Vec16<T>::type;
-    V v;
+__device__ __forceinline__ void load_stream(const T *p, float (&out)[Vec16<T>::N]) {
+    widen<T>(load_stream_raw<T>(p), out);
+}
+template <typename T>
+__device__ __forceinline__ void load_keep(const T *p, float (&out)[Vec16<T>::N]) {
+    widen<T>(load_keep_raw<T>(p), out);
+}
+
+// Round fp32 values to T (nearest even) and store them as one non-temporal 16-byte vector.
+template <typename T>
+__device__ __forceinline__ void store_stream(T *p, const float (&in)[Vec16<T>::N]) {
+    RawVec<T> v;
 #pragma unroll
     for (int e = 0; e < Vec16<T>::N; ++e) v[e] = static_cast<T>(in[e]);
-    *reinterpret_cast<V *>(p) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<RawVec<T> *>(p));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
@@ -170,6 +191,34 @@ __device__ __forceinline__ void row_allreduce_sum2(float &a, float &b, float *ld
         __syncthreads();  // the slots may be rewritten by the next row
         a = sa;
         b = sb;
+    }
+}
+
+// Sums of NV values at once over a row held by G lanes (G <= 64, or G = 64 * W with the
+// wave partials crossing through LDS). `lds` must hold NV * (blockDim.x / 64) floats. Every
+// thread of the workgroup must call it. Fixed order, as above.
+template <int G, int NV>
+__device__ __forceinline__ void row_allreduce_sumN(float (&v)[NV], float *lds) {
+    static_assert(NV % 2 == 0, "values are reduced in pairs");
+#pragma unroll
+    for (int i = 0; i < NV; i += 2) group_allreduce_sum2<G < 64 ? G : 64>(v[i], v[i + 1]);
+    if constexpr (G > 64) {
+        constexpr int W = G / 64;
+        const int wave = threadIdx.x >> 6;
+        const int first = wave - (wave % W);
+        if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) lds[NV * wave + i] = v[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) t += lds[NV * (first + w) + i];
+            v[i] = t;
+        }
+        __syncthreads();
     }
 }
 

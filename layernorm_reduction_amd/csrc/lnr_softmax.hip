@@ -46,7 +46,7 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
         if (live && c < nvec) {
-            load_vec<T>(inp + base + static_cast<int64_t>(c) * V, z[k]);
+            load_stream<T>(inp + base + static_cast<int64_t>(c) * V, z[k]);
         } else {
 #pragma unroll
             for (int e = 0; e < V; ++e) z[k][e] = -INFINITY;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
             const int c = k * G + lane;
             if (live && c < nvec) {
                 float m[V];
-                load_vec<T>(mrow + static_cast<int64_t>(c) * V, m);
+                load_keep<T>(mrow + static_cast<int64_t>(c) * V, m);
 #pragma unroll
                 for (int e = 0; e < V; ++e) z[k][e] += m[e];
             }
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
             float y[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) y[e] = z[k][e] * inv;
-            store_vec<T>(out + base + static_cast<int64_t>(c) * V, y);
+            store_stream<T>(out + base + static_cast<int64_t>(c) * V, y);
         }
     }
 }
@@ -123,8 +123,8 @@ __global__ __launch_bounds__(WG) void softmax_bw_vec(T *dinp, const T *dout,
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
         if (live && c < nvec) {
-            load_vec<T>(y + base + static_cast<int64_t>(c) * V, yv[k]);
-            load_vec<T>(dout + base + static_cast<int64_t>(c) * V, gv[k]);
+            load_stream<T>(y + base + static_cast<int64_t>(c) * V, yv[k]);
+            load_stream<T>(dout + base + static_cast<int64_t>(c) * V, gv[k]);
         } else {
 #pragma unroll
             for (int e = 0; e < V; ++e) yv[k][e] = gv[k][e] = 0.f;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(WG) void softmax_bw_vec(T *dinp, const T *dout,
             float d[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) d[e] = yv[k][e] * (gv[k][e] - t);
-            store_vec<T>(dinp + base + static_cast<int64_t>(c) * V, d);
+            store_stream<T>(dinp + base + static_cast<int64_t>(c) * V, d);
         }
     }
 }
@@ -214,28 +214,41 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 }
 
 // ------------------------------------------------------------------------------------------
-// Row-length buckets: (G lanes per row, IT vectors per lane) for each storage type.
-// Capacity G * IT * V equals the bucket length; rows shorter than their bucket leave the
-// trailing vectors idle. The bucket lengths are the HW4 page's template list.
+// Row-length buckets: (G lanes per row, IT vectors per lane) for each storage type, one
+// table for the forward and one for the backward. Capacity G * IT * V equals the bucket
+// length; rows shorter than their bucket leave the trailing vectors idle. The bucket lengths
+// are the HW4 page's template list. Measured on MI355X: the forward (mask add, max, exp,
+// sum, scale) runs best with 2-4 vectors per lane; the backward (one product sum) with one
+// vector per lane and as many lanes per row as the row allows.
 // ------------------------------------------------------------------------------------------
 struct Plan {
     int bucket;  // longest row this instantiation takes; 0 = element-wise fallback
-    int G;
-    int IT;
+    int G;       // lanes per row
+    int IT;      // 16-byte vectors per lane
+    int WG;      // workgroup size
 };
 
-constexpr int kSoftmaxWG = 256;
-
-template <typename T> struct SoftmaxTable;
-template <> struct SoftmaxTable<f16> {   // V = 8
-    static constexpr Plan plans[] = {{32, 4, 1},   {64, 8, 1},   {128, 8, 2},
-                                     {256, 16, 2}, {384, 16, 3}, {512, 16, 4},
-                                     {768, 32, 3}, {1024, 32, 4}, {2048, 64, 4}};
+template <typename T> struct SoftmaxFwTable;
+template <> struct SoftmaxFwTable<f16> {   // V = 8
+    static constexpr Plan plans[] = {{32, 4, 1, 256},   {64, 4, 2, 256},   {128, 4, 4, 256},
+                                     {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 32, 2, 256},
+                                     {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
 };
-template <> struct SoftmaxTable<float> { // V = 4
-    static constexpr Plan plans[] = {{32, 8, 1},   {64, 8, 2},   {128, 16, 2},
-                                     {256, 16, 4}, {384, 32, 3}, {512, 32, 4},
-                                     {768, 64, 3}, {1024, 64, 4}, {2048, 64, 8}};
+template <> struct SoftmaxFwTable<float> { // V = 4
+    static constexpr Plan plans[] = {{32, 4, 2, 256},   {64, 4, 4, 256},   {128, 8, 4, 256},
+                                     {256, 16, 4, 256}, {384, 32, 3, 256}, {512, 32, 4, 256},
+                                     {768, 64, 3, 256}, {1024, 64, 4, 256}, {2048, 64, 8, 256}};
+};
+template <typename T> struct SoftmaxBwTable;
+template <> struct SoftmaxBwTable<f16> {
+    static constexpr Plan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 256},
+                                     {256, 32, 1, 256}, {384, 16, 3, 256}, {512, 64, 1, 128},
+                                     {768, 32, 3, 256}, {1024, 64, 2, 128}, {2048, 64, 4, 128}};
+};
+template <> struct SoftmaxBwTable<float> {
+    static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 256},
+                                     {256, 64, 1, 128}, {384, 32, 3, 256}, {512, 64, 2, 128},
+                                     {768, 64, 3, 128}, {1024, 64, 4, 128}, {2048, 64, 8, 128}};
 };
 
 struct SoftmaxFwArgs {
@@ -255,21 +268,21 @@ struct SoftmaxBwArgs {
     int32_t Tk;
 };
 
-template <typename T, int G, int IT>
+template <typename T, int G, int IT, int WG>
 static hipError_t launch_fw_vec(const SoftmaxFwArgs &a, hipStream_t st) {
-    constexpr int RPB = kSoftmaxWG / G;
+    constexpr int RPB = WG / G;
     const int64_t blocks = (a.rows + RPB - 1) / RPB;
-    return launch(softmax_fw_vec<T, G, IT, kSoftmaxWG>, dim3(static_cast<uint32_t>(blocks)),
-                  dim3(kSoftmaxWG), st, static_cast<T *>(a.out), static_cast<const T *>(a.inp),
+    return launch(softmax_fw_vec<T, G, IT, WG>, dim3(static_cast<uint32_t>(blocks)),
+                  dim3(WG), st, static_cast<T *>(a.out), static_cast<const T *>(a.inp),
                   static_cast<const T *>(a.mask), a.rows, a.Tq, a.Tk, a.rows_per_batch, a.causal);
 }
 
-template <typename T, int G, int IT>
+template <typename T, int G, int IT, int WG>
 static hipError_t launch_bw_vec(const SoftmaxBwArgs &a, hipStream_t st) {
-    constexpr int RPB = kSoftmaxWG / G;
+    constexpr int RPB = WG / G;
     const int64_t blocks = (a.rows + RPB - 1) / RPB;
-    return launch(softmax_bw_vec<T, G, IT, kSoftmaxWG>, dim3(static_cast<uint32_t>(blocks)),
-                  dim3(kSoftmaxWG), st, static_cast<T *>(a.dinp), static_cast<const T *>(a.dout),
+    return launch(softmax_bw_vec<T, G, IT, WG>, dim3(static_cast<uint32_t>(blocks)),
+                  dim3(WG), st, static_cast<T *>(a.dinp), static_cast<const T *>(a.dout),
                   static_cast<const T *>(a.y), a.rows, a.Tk);
 }
 
@@ -277,28 +290,28 @@ static hipError_t launch_bw_vec(const SoftmaxBwArgs &a, hipStream_t st) {
 // bucket that holds Tk.
 template <typename T, int I>
 static hipError_t dispatch_fw(const SoftmaxFwArgs &a, hipStream_t st) {
-    constexpr Plan p = SoftmaxTable<T>::plans[I];
-    if (a.Tk <= p.bucket) return launch_fw_vec<T, p.G, p.IT>(a, st);
-    if constexpr (I + 1 < static_cast<int>(sizeof(SoftmaxTable<T>::plans) / sizeof(Plan)))
+    constexpr Plan p = SoftmaxFwTable<T>::plans[I];
+    if (a.Tk <= p.bucket) return launch_fw_vec<T, p.G, p.IT, p.WG>(a, st);
+    if constexpr (I + 1 < static_cast<int>(sizeof(SoftmaxFwTable<T>::plans) / sizeof(Plan)))
         return dispatch_fw<T, I + 1>(a, st);
     return hipErrorInvalidValue;
 }
 
 template <typename T, int I>
 static hipError_t dispatch_bw(const SoftmaxBwArgs &a, hipStream_t st) {
-    constexpr Plan p = SoftmaxTable<T>::plans[I];
-    if (a.Tk <= p.bucket) return launch_bw_vec<T, p.G, p.IT>(a, st);
-    if constexpr (I + 1 < static_cast<int>(sizeof(SoftmaxTable<T>::plans) / sizeof(Plan)))
+    constexpr Plan p = SoftmaxBwTable<T>::plans[I];
+    if (a.Tk <= p.bucket) return launch_bw_vec<T, p.G, p.IT, p.WG>(a, st);
+    if constexpr (I + 1 < static_cast<int>(sizeof(SoftmaxBwTable<T>::plans) / sizeof(Plan)))
         return dispatch_bw<T, I + 1>(a, st);
     return hipErrorInvalidValue;
 }
 
-template <typename T>
+template <typename Table>
 static Plan softmax_plan(int64_t Tk, bool vector_ok) {
     if (vector_ok)
-        for (const Plan &p : SoftmaxTable<T>::plans)
+        for (const Plan &p : Table::plans)
             if (Tk <= p.bucket) return p;
-    return Plan{0, 64, 0};
+    return Plan{0, 64, 0, kGenericWG};
 }
 
 static int check_common(const void *a, const void *b, const void *c, int64_t B, int64_t H,
@@ -389,16 +402,20 @@ extern "C" int attn_softmax_bw(void *dinp, const void *dout, const void *out_fw,
 }
 
 // Introspection for tests and benchmarks: the bucket, lanes per row and vectors per lane
-// that attn_softmax_fw/bw use for (Tk, dtype) with aligned buffers; bucket 0 means the
-// element-wise fallback. Returns LNR_OK or the shape/dtype error of the call it mirrors.
-extern "C" int lnr_softmax_plan(int64_t Tk, lnr_dtype dtype, int *bucket, int *lanes_per_row,
-                                int *vectors_per_lane) {
+// that attn_softmax_fw (which = 0) or attn_softmax_bw (which = 1) use for (Tk, dtype) with
+// aligned buffers; bucket 0 means the element-wise fallback.
+extern "C" int lnr_softmax_plan(int64_t Tk, lnr_dtype dtype, int which, int *bucket,
+                                int *lanes_per_row, int *vectors_per_lane) {
     if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
     if (Tk < 1) return LNR_ERR_SHAPE;
     if (Tk > LNR_SOFTMAX_MAX_TK) return LNR_ERR_UNSUPPORTED;
     if (bucket == nullptr || lanes_per_row == nullptr || vectors_per_lane == nullptr) return LNR_ERR_NULL;
     const bool vec = (static_cast<size_t>(Tk) * dtype_size(dtype)) % 16 == 0;
-    const Plan p = dtype == LNR_F16 ? softmax_plan<f16>(Tk, vec) : softmax_plan<float>(Tk, vec);
+    Plan p;
+    if (dtype == LNR_F16)
+        p = which == 0 ? softmax_plan<SoftmaxFwTable<f16>>(Tk, vec) : softmax_plan<SoftmaxBwTable<f16>>(Tk, vec);
+    else
+        p = which == 0 ? softmax_plan<SoftmaxFwTable<float>>(Tk, vec) : softmax_plan<SoftmaxBwTable<float>>(Tk, vec);
     *bucket = p.bucket;
     *lanes_per_row = p.G;
     *vectors_per_lane = p.IT;

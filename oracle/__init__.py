@@ -70,6 +70,8 @@ def _load():
     lib.lnr_oracle_layernorm_bw_dgamma_dbeta.argtypes = [d, d, i64, i64, ctypes.c_double, d, d, d, d]
     lib.lnr_oracle_rmsnorm_fw.argtypes = [d, d, i64, i64, ctypes.c_double, d, d]
     lib.lnr_oracle_rmsnorm_bw.argtypes = [d, d, d, i64, i64, ctypes.c_double, d, d]
+    lib.lnr_oracle_layernorm_bw_given_stats.argtypes = [d, d, d, d, d, i64, i64, d, d, d]
+    lib.lnr_oracle_layernorm_bw_given_stats.restype = None
     lib.lnr_oracle_threads.argtypes = []
     lib.lnr_oracle_threads.restype = ctypes.c_int
     for f in (lib.lnr_oracle_softmax_fw, lib.lnr_oracle_softmax_fw_rows, lib.lnr_oracle_softmax_bw,
@@ -176,6 +178,22 @@ def layernorm_bw(x, dy, gamma, eps: float = 1e-8):
     """Returns (dx, dgamma, dbeta) as float64."""
     dx = layernorm_bw_dx(x, dy, gamma, eps)
     dg, db = layernorm_bw_dgamma_dbeta(x, dy, eps)
+    return dx, dg, db
+
+
+def layernorm_bw_given_stats(x, dy, gamma, mean, rstd):
+    """Backward from saved statistics (mean, rstd per row, e.g. the fp32 values a forward
+    kernel stored). Returns (dx, dgamma, dbeta) as float64."""
+    x = _f64(x)
+    dy = _f64(dy)
+    N, C = x.shape
+    g = _f64(gamma).reshape(C)
+    m = _f64(mean).reshape(N)
+    r = _f64(rstd).reshape(N)
+    dx = np.empty_like(x)
+    dg = np.empty(C, np.float64)
+    db = np.empty(C, np.float64)
+    _load().lnr_oracle_layernorm_bw_given_stats(_p(x), _p(dy), _p(g), _p(m), _p(r), N, C, _p(dx), _p(dg), _p(db))
     return dx, dg, db
 
 

@@ -238,6 +238,56 @@ ORACLE_API void lnr_oracle_layernorm_bw_dgamma_dbeta(const double *x, const doub
 }
 
 /* ---------------------------------------------------------------------------------------
+ * LayerNorm backward from given statistics. [L10 "Technique 2"; HW4 "Problem structure"]
+ * The same formulas as above, with mu_i and 1/sigma_i taken from mean[i] and rstd[i] (the
+ * values a forward pass saved) instead of being recomputed from x:
+ *   xhat_ij = (x_ij - mean_i) * rstd_i,  g_ij = gamma_j * dy_ij
+ *   dx_ij   = rstd_i * ( g_ij - (1/C) sum_k g_ik - xhat_ij * (1/C) sum_k g_ik xhat_ik )
+ *   dgamma_j = sum_i dy_ij * xhat_ij,  dbeta_j = sum_i dy_ij
+ * This is the function a backward kernel that receives saved statistics computes; with the
+ * exact statistics it equals the recomputing version.
+ * ------------------------------------------------------------------------------------- */
+ORACLE_API void lnr_oracle_layernorm_bw_given_stats(const double *x, const double *dy,
+                                                    const double *gamma, const double *mean,
+                                                    const double *rstd, int64_t N, int64_t C,
+                                                    double *dx, double *dgamma, double *dbeta)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        const double *xr = x + i * C, *dyr = dy + i * C;
+        double sum_g = 0.0, sum_gx = 0.0;
+        for (int64_t j = 0; j < C; ++j) {
+            const double xhat = (xr[j] - mean[i]) * rstd[i];
+            const double g = gamma[j] * dyr[j];
+            sum_g += g;
+            sum_gx += g * xhat;
+        }
+        const double a = sum_g / (double)C, b = sum_gx / (double)C;
+        for (int64_t j = 0; j < C; ++j) {
+            const double xhat = (xr[j] - mean[i]) * rstd[i];
+            const double g = gamma[j] * dyr[j];
+            dx[i * C + j] = rstd[i] * (g - a - xhat * b);
+        }
+    }
+    const int64_t blk = 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t jb = 0; jb < C; jb += blk) {
+        const int64_t je = (jb + blk < C) ? jb + blk : C;
+        for (int64_t j = jb; j < je; ++j) {
+            dgamma[j] = 0.0;
+            dbeta[j] = 0.0;
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t j = jb; j < je; ++j) {
+                const double xhat = (x[i * C + j] - mean[i]) * rstd[i];
+                dgamma[j] += dy[i * C + j] * xhat;
+                dbeta[j] += dy[i * C + j];
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
  * RMSNorm (forward and input gradient). [FT section 5.4]
  *   rms = sqrt((1/C) sum_j x_j^2 + eps),  y_j = gamma_j * x_j / rms
  *   dx_j = (1/rms) * ( g_j - xhat_j * (1/C) sum_k g_k xhat_k ),  g = gamma*dy, xhat = x/rms

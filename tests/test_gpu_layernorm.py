@@ -2,16 +2,25 @@
 
   * forward: y, mean and rstd on the seeded inputs of each workload, every element;
   * backward on identical stored inputs: the GPU receives the oracle's mean/rstd rounded to
-    fp32 (the ABI's stats format) while the oracle recomputes them from x in fp64; dx, dgamma
-    and dbeta are compared element by element;
-  * chained: GPU forward statistics feeding the GPU backward, against the oracle.
+    fp32 (the ABI's statistics format) and is compared, element by element, with the oracle's
+    backward evaluated on those same fp32 statistics (dx, dgamma, dbeta);
+  * chained: GPU forward statistics feeding the GPU backward, against the true gradient (the
+    oracle recomputes the statistics from x in fp64), with twice the tolerance because the
+    chain also carries the fp32 rounding of the statistics.
 Workloads 1, 2, 4 and 5 run at their full sizes, in the launch configuration the benchmark uses.
 
-dgamma with fp32 storage over N = 32768 rows: the column sums of dy * xhat over 32768 rows
-carry the fp32 rounding of the per-row statistics (about 6e-8 relative per row, random over
-rows), which is about 1e-5 absolute, so near-zero columns can miss an element-wise 1e-5
-bound whatever the summation precision. That case is checked with the norm-wise bound
-max |err| <= atol + rtol * max |ref|, and its element-wise pass rate is printed.
+dx tolerance: the fp32 formula dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) carries a
+rounding error of a few units of fp32 roundoff times rstd * max |g| of its row, because the
+terms it subtracts are that large. For rows of ordinary spread this is far below atol; for
+rows whose exact dx is a tiny remainder (C = 2 rows with nearly equal entries, where the
+projection removes all but eps/(var + eps) of g - mean(g)) it is the whole error. The dx
+bound is therefore atol + rtol * |ref| + 16 * 2^-24 * rstd_i * max_j |g_ij|.
+
+Chained dgamma with fp32 storage over N = 32768 rows: the column sums of dy * xhat over 32768
+rows carry the fp32 rounding of every row's statistics (about 6e-8 relative per row, random
+over rows), about 1e-5 absolute, so near-zero columns can miss an element-wise 1e-5 bound
+however exactly the sum is taken. That one comparison uses the norm-wise bound
+max |err| <= atol + rtol * max |ref| and prints its element-wise pass rate.
 """
 import numpy as np
 import pytest
@@ -26,7 +35,25 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def run_ln(case, chain=True, dgamma_normwise=False):
+U32 = 2.0 ** -24
+
+
+def assert_dx_close(dx, ref, dtype, what, dy64, g64, rstd, scale=1.0):
+    """Element-wise bound plus the fp32 formula's own rounding term (see the module note)."""
+    atol, rtol = TOL[dtype]
+    got = to_host64(dx)
+    cond = 16.0 * U32 * np.asarray(rstd, np.float64).reshape(-1, 1) * \
+        np.max(np.abs(dy64 * g64.reshape(1, -1)), axis=1, keepdims=True)
+    err = np.abs(got - ref)
+    lim = scale * (atol + rtol * np.abs(ref)) + cond
+    bad = ~(err <= lim)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err - lim, -np.inf)), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} elements outside the bound; "
+                             f"worst at {i}: gpu={got[i]!r} oracle={ref[i]!r} bound={lim[i]:.3e}")
+
+
+def run_ln(case, chain=True, chain_dgamma_normwise=False):
     atol, rtol = TOL[case.dtype]
     say(case.name, "oracle forward")
     x64 = case.x.double().numpy()
@@ -42,35 +69,37 @@ def run_ln(case, chain=True, dgamma_normwise=False):
     assert_close(rstd, rstd_ref, case.dtype, f"{case.name} rstd")
     del y_ref, y
 
-    say(case.name, "oracle backward")
+    say(case.name, "oracle backward (given fp32 statistics)")
     dy64 = case.dy.double().numpy()
-    dx_ref, dg_ref, db_ref = oracle.layernorm_bw(x64, dy64, g64, case.eps)
+    m32 = torch.from_numpy(mean_ref).float()
+    r32 = torch.from_numpy(rstd_ref).float()
+    dx_ref, dg_ref, db_ref = oracle.layernorm_bw_given_stats(x64, dy64, g64, m32, r32)
     say(case.name, "GPU backward")
     dyd = case.dy.to(DEV)
-    m_in = torch.from_numpy(mean_ref).float().to(DEV)
-    r_in = torch.from_numpy(rstd_ref).float().to(DEV)
-    dx, dg, db = lnr.layernorm_bw(dyd, xd, gd, m_in, r_in)
+    dx, dg, db = lnr.layernorm_bw(dyd, xd, gd, m32.to(DEV), r32.to(DEV))
     torch.cuda.synchronize()
-    assert_close(dx, dx_ref, case.dtype, f"{case.name} dx")
+    assert_dx_close(dx, dx_ref, case.dtype, f"{case.name} dx", dy64, g64, r32.double().numpy())
+    assert_close(dg, dg_ref, case.dtype, f"{case.name} dgamma")
     assert_close(db, db_ref, case.dtype, f"{case.name} dbeta")
-    if dgamma_normwise:
-        bad, _ = violations(to_host64(dg), dg_ref, atol, rtol)
-        print(f"[info] {case.name} dgamma element-wise: {case.C - bad}/{case.C} within "
-              f"atol=rtol={atol}", flush=True)
-        err = np.max(np.abs(to_host64(dg) - dg_ref))
-        assert err <= atol + rtol * np.max(np.abs(dg_ref)), err
-    else:
-        assert_close(dg, dg_ref, case.dtype, f"{case.name} dgamma")
+    del dx_ref, dg_ref, db_ref, dx, dg, db
 
     if chain:
-        say(case.name, "chained fw -> bw")
+        say(case.name, "oracle backward (exact) and GPU chained fw -> bw")
+        tdx, tdg, tdb = oracle.layernorm_bw(x64, dy64, g64, case.eps)
         dx2, dg2, db2 = lnr.layernorm_bw(dyd, xd, gd, mean, rstd)
         torch.cuda.synchronize()
         s = 2.0
-        assert_close(dx2, dx_ref, case.dtype, f"{case.name} chain dx", atol=atol * s, rtol=rtol * s)
-        assert_close(db2, db_ref, case.dtype, f"{case.name} chain dbeta", atol=atol * s, rtol=rtol * s)
-        if not dgamma_normwise:
-            assert_close(dg2, dg_ref, case.dtype, f"{case.name} chain dgamma", atol=atol * s,
+        assert_dx_close(dx2, tdx, case.dtype, f"{case.name} chain dx", dy64, g64, rstd_ref, scale=s)
+        assert_close(db2, tdb, case.dtype, f"{case.name} chain dbeta", atol=atol * s, rtol=rtol * s)
+        if chain_dgamma_normwise:
+            got = to_host64(dg2)
+            bad, _ = violations(got, tdg, atol * s, rtol * s)
+            print(f"[info] {case.name} chained dgamma element-wise: {case.C - bad}/{case.C} within "
+                  f"atol=rtol={atol * s}", flush=True)
+            err = np.max(np.abs(got - tdg))
+            assert err <= atol * s + rtol * s * np.max(np.abs(tdg)), err
+        else:
+            assert_close(dg2, tdg, case.dtype, f"{case.name} chain dgamma", atol=atol * s,
                          rtol=rtol * s)
     del xd, gd, bd, dyd
     torch.cuda.empty_cache()
@@ -94,8 +123,7 @@ def test_workload4_hidden_size_sweep(C):
 @pytest.mark.parametrize("C", [1024, 4096])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
 def test_workload5_encoder_layer(C, dtype):
-    run_ln(W.workload5_layernorm(C, dtype), chain=False,
-           dgamma_normwise=(dtype == torch.float32))
+    run_ln(W.workload5_layernorm(C, dtype), chain_dgamma_normwise=(dtype == torch.float32))
 
 
 # ------------------------------------------------------------------------- edge cases

@@ -162,6 +162,33 @@ def test_dgamma_is_not_transposed():
     np.testing.assert_allclose(db, np.einsum("ij->j", dy), rtol=1e-14)
 
 
+def test_given_stats_backward_equals_recomputing_backward_with_exact_stats():
+    x, g, b, dy = _case(40, 70, 13, offset_std=2.0)
+    _, mean, rstd = oracle.layernorm_fw(x, g, b, EPS)
+    got = oracle.layernorm_bw_given_stats(x, dy, g, mean, rstd)
+    ref = oracle.layernorm_bw(x, dy, g, EPS)
+    for u, v in zip(got, ref):
+        np.testing.assert_allclose(u, v, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,C", [(9, 2), (17, 33), (64, 256)])
+def test_given_stats_backward_matches_aten_layer_norm_backward(N, C):
+    # aten's native layer-norm backward also takes mean and rstd as inputs: feed both the
+    # fp32-rounded statistics (what a forward kernel stores), independent of recomputation.
+    x, g, b, dy = _case(N, C, 14, offset_std=3.0)
+    _, mean, rstd = oracle.layernorm_fw(x, g, b, EPS)
+    mean32 = mean.astype(np.float32).astype(np.float64)
+    rstd32 = rstd.astype(np.float32).astype(np.float64)
+    dx_t, dg_t, db_t = torch.ops.aten.native_layer_norm_backward(
+        torch.from_numpy(dy), torch.from_numpy(x), [C], torch.from_numpy(mean32).view(N, 1),
+        torch.from_numpy(rstd32).view(N, 1), torch.from_numpy(g), torch.from_numpy(b),
+        [True, True, True])
+    dx, dg, db = oracle.layernorm_bw_given_stats(x, dy, g, mean32, rstd32)
+    np.testing.assert_allclose(dx, dx_t.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dg, dg_t.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(db, db_t.numpy(), rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- RMSNorm
 
 RMS_EPS = 1e-6
