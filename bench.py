@@ -46,7 +46,134 @@ def parse():
     p.add_argument("--workload", choices=("w2", "w5"), default="w2")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-ops", action="store_true", help="skip the per-op diagnostic timings")
+    p.add_argument("--table", action="store_true",
+                   help="time every op at every workload shape (row-length sweep, hidden-size sweep, "
+                        "encoder layer fp16/fp32); one JSON line per case")
+    p.add_argument("--summarize-profiles", metavar="DIR",
+                   help="CPU only: read the rocprofv3 outputs under DIR (prof_<w>/, pmc_fetch_<w>/, "
+                        "pmc_write_<w>/) and write the summaries under profiles/")
     return p.parse_args()
+
+
+TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
+             "-d $REPO/gpurun_out/prof_{w} -o {w} -- python3 $REPO/bench.py{args}")
+PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {ctr} -f csv "
+           "-d $REPO/gpurun_out/pmc_{kind}_{w} -o {w} -- python3 $REPO/bench.py{args} "
+           "--steps 20 --warmup 5 --no-cpu-baseline")
+DOMINANT = "softmax_bw_vec"
+COPY = "copy16"
+
+
+def summarize_profiles(root_dir: str, workload: str):
+    """Write profiles/<workload>_kernel_trace.md from the kernel-trace statistics and, when the
+    two counter runs are present, profiles/<workload>_traffic.md plus the machine-readable
+    profiles/traffic_softmax_bw_<workload>.json that the benchmark reports as roofline.traffic
+    (only while the HIP sources still hash to the value recorded there)."""
+    import csv
+    import collections
+
+    args = "" if workload == "w2" else " --workload w5 --steps 50 --warmup 5 --no-cpu-baseline"
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    stats = os.path.join(root_dir, f"prof_{workload}", f"{workload}_kernel_stats.csv")
+    lines = [f"# Kernel trace: {workload} benchmark\n",
+             "Command ($REPO = the repository root on the GPU host):\n",
+             "```", TRACE_CMD.format(w=workload, args=args), "```\n"]
+    def roofline_of(path):
+        if os.path.exists(path):
+            for line in open(path):
+                if line.startswith("{") and '"roofline"' in line:
+                    return json.loads(line)["roofline"]
+        return None
+
+    live = roofline_of(os.path.join(root_dir, f"bench_{workload}.json"))
+    under = roofline_of(os.path.join(root_dir, f"prof_{workload}.log"))
+    if live:
+        lines.append(f"The same command run without the profiler (same sources): `{DOMINANT}` averages "
+                     f"{live['avg_us']} us over {live.get('launches', '?')} timed launches (HIP events "
+                     f"recorded by the kernel itself), {live['achieved']} GB/s, {live['frac']:.1%} of "
+                     f"8 TB/s.\n")
+    if under:
+        lines.append(f"Under the profiler the bench's own events read {under['avg_us']} us: the tracer adds "
+                     f"work to every dispatch between the recorded start and the kernel, so the table "
+                     f"below, not that figure, is the profiled duration.\n")
+    lines += ["| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats)):
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    with open(os.path.join(out_dir, f"{workload}_kernel_trace.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    def per_kernel(kind):
+        path = os.path.join(root_dir, f"pmc_{kind}_{workload}", f"{workload}_counter_collection.csv")
+        if not os.path.exists(path):
+            return None
+        by = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            by[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
+        return {k: statistics.mean(v) for k, v in by.items()}
+
+    fetch, write = per_kernel("fetch"), per_kernel("write")
+    if not fetch or not write:
+        return
+    pick = lambda d, key: next(v for k, v in d.items() if key in k)
+    copy_bytes = float(1 << 30)
+    f_scale = copy_bytes / pick(fetch, COPY)
+    w_scale = copy_bytes / pick(write, COPY)
+    rows = ["# HBM traffic per dispatch: {w} benchmark\n".format(w=workload),
+            "Commands (each counter in a run of its own):\n", "```",
+            PMC_CMD.format(ctr="FETCH_SIZE", kind="fetch", w=workload, args=args),
+            PMC_CMD.format(ctr="WRITE_SIZE", kind="write", w=workload, args=args), "```\n",
+            f"Scale: the 16-byte streaming copy of 1 GiB (`copy16`) reads {pick(fetch, COPY) / 2**20:.1f} MiB "
+            f"by FETCH_SIZE and writes {pick(write, COPY) / 2**20:.1f} MiB by WRITE_SIZE, so fetch counts are "
+            f"multiplied by {f_scale:.4f} and write counts by {w_scale:.4f}.\n",
+            "| kernel | fetch MB (scaled) | write MB (scaled) | total MB |", "|---|---|---|---|"]
+    for k in fetch:
+        if k in write:
+            fb, wb = fetch[k] * f_scale, write[k] * w_scale
+            rows.append(f"| `{k[:90]}` | {fb / 1e6:.3f} | {wb / 1e6:.3f} | {(fb + wb) / 1e6:.3f} |")
+    dom_f, dom_w = pick(fetch, DOMINANT) * f_scale, pick(write, DOMINANT) * w_scale
+    with open(os.path.join(out_dir, f"{workload}_traffic.md"), "w") as fh:
+        fh.write("\n".join(rows) + "\n")
+    with open(os.path.join(out_dir, f"traffic_softmax_bw_{workload}.json"), "w") as fh:
+        json.dump({"kernel": DOMINANT, "workload": workload, "source_sha256": source_digest(),
+                   "fetch_bytes": round(dom_f), "write_bytes": round(dom_w),
+                   "bytes_per_launch": round(dom_f + dom_w), "fetch_scale": f_scale,
+                   "write_scale": w_scale}, fh, indent=1)
+        fh.write("\n")
+
+
+class HipEvents:
+    """Timing events created through the HIP runtime (hipEvent_t handles as plain ints), so
+    the library's lnr_time_next_launch hook can record them at a kernel's own start/end."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = self.ct.c_void_p()
+            if self.hip.hipEventCreate(self.ct.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventSynchronize(b) != 0 or self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
 
 
 def source_digest() -> str:
@@ -60,8 +187,134 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+def table_cases():
+    """(name, kind, shape, dtype, extra) for every op shape of the five workloads."""
+    import torch
+    from layernorm_reduction_amd import workloads as W
+    cases = []
+    for Tk in W.SOFTMAX_TK_SWEEP:
+        for causal in (True, False):
+            B = W.workload3_batch(Tk)
+            cases.append((f"w3 softmax [{B},8,{Tk},{Tk}] {'causal' if causal else 'full'} padded fp16",
+                          "softmax", (B, 8, Tk, Tk), torch.float16, {"causal": causal, "mask": True}))
+    cases.append(("w2 softmax [32,8,256,256] causal fp16", "softmax", (32, 8, 256, 256), torch.float16,
+                  {"causal": True, "mask": False}))
+    for dt in (torch.float16, torch.float32):
+        tag = "fp16" if dt == torch.float16 else "fp32"
+        cases.append((f"w5 softmax [64,16,512,512] padded {tag}", "softmax", (64, 16, 512, 512), dt,
+                      {"causal": False, "mask": True}))
+    cases.append(("w2 layernorm [8192,256] fp16", "layernorm", (8192, 256), torch.float16, {}))
+    for C in W.LAYERNORM_C_SWEEP:
+        cases.append((f"w4 layernorm [16384,{C}] fp16", "layernorm", (16384, C), torch.float16, {}))
+    for dt in (torch.float16, torch.float32):
+        tag = "fp16" if dt == torch.float16 else "fp32"
+        for C in (1024, 4096):
+            cases.append((f"w5 layernorm [32768,{C}] {tag}", "layernorm", (32768, C), dt, {}))
+    return cases
+
+
+def run_table():
+    """Back-to-back launches of each op over rotating buffers (>= 1 GiB footprint): average
+    per launch from one event pair around the batch, plus the kernel's own median duration
+    from events the kernel records (first kernel only for layernorm_bw)."""
+    import torch
+    import layernorm_reduction_amd as lnr
+    from layernorm_reduction_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    hev = HipEvents()
+    hook = lnr.load().lnr_time_next_launch
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    reps = 30
+
+    def timed(calls):
+        for c in calls[:3]:
+            c()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            calls[i % len(calls)]()
+        b.record()
+        torch.cuda.synchronize()
+        b2b = a.elapsed_time(b) * 1e3 / reps
+        ka, kb = hev.create(reps), hev.create(reps)
+        for i in range(reps):
+            hook(ka[i], kb[i])
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        k = sorted(hev.elapsed_ms(x, y) * 1e3 for x, y in zip(ka, kb))
+        hev.destroy(ka + kb)
+        return b2b, k[len(k) // 2]
+
+    for name, kind, shape, dt, extra in table_cases():
+        s = W.dtype_size(dt)
+        if kind == "softmax":
+            B, H, T, _ = shape
+            per = B * H * T * T * s
+            n = max(2, math.ceil(MIN_FOOTPRINT / (4 * per)))
+            fw, bw = [], []
+            keep = []
+            for _ in range(n):
+                x = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                dy = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                y, dx = torch.empty_like(x), torch.empty_like(x)
+                m = None
+                if extra["mask"]:
+                    m = torch.zeros(B, T, device=dev, dtype=dt)
+                    m[:, T * 3 // 4:] = float("-inf")
+                fw.append(lnr.bind_attn_softmax_fw(x, m, extra["causal"], y))
+                bw.append(lnr.bind_attn_softmax_bw(dy, y, dx))
+                keep += [x, dy, y, dx, m]
+            bf = W.softmax_fw_bytes(B, H, T, T, s, has_mask=extra["mask"])
+            bb = W.softmax_bw_bytes(B, H, T, T, s)
+        else:
+            N, C = shape
+            per = N * C * s
+            n = max(2, math.ceil(MIN_FOOTPRINT / (4 * per)))
+            fw, bw = [], []
+            keep = []
+            wsb = lnr.layernorm_bw_workspace_bytes(N, C, lnr.LNR_F16 if dt == torch.float16 else lnr.LNR_F32)
+            for _ in range(n):
+                x = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                dy = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                gm = torch.rand(C, device=dev, dtype=dt, generator=g) + 0.5
+                bt = torch.randn(C, device=dev, dtype=dt, generator=g)
+                y, dx = torch.empty_like(x), torch.empty_like(x)
+                mean = torch.empty(N, device=dev, dtype=torch.float32)
+                rstd = torch.empty(N, device=dev, dtype=torch.float32)
+                dg, db = torch.empty(C, device=dev, dtype=dt), torch.empty(C, device=dev, dtype=dt)
+                ws = torch.empty(max(wsb, 1), device=dev, dtype=torch.uint8)
+                fw.append(lnr.bind_layernorm_fw(x, gm, bt, W.LN_EPS, y, mean, rstd))
+                bw.append(lnr.bind_layernorm_bw(dy, x, gm, mean, rstd, dx, dg, db, ws))
+                keep += [x, dy, gm, bt, y, dx, mean, rstd, dg, db, ws]
+            bf = W.layernorm_fw_bytes(N, C, s)
+            bb = W.layernorm_bw_bytes(N, C, s)
+        torch.cuda.synchronize()
+        f_b2b, f_k = timed(fw)
+        b_b2b, b_k = timed(bw)
+        rec = {"case": name, "fw_us": round(f_b2b, 2), "bw_us": round(b_b2b, 2),
+               "fw_kernel_us": round(f_k, 2), "bw_first_kernel_us": round(b_k, 2),
+               "fw_GBps": round(bf / f_b2b * 1e-3, 1), "bw_GBps": round(bb / b_b2b * 1e-3, 1),
+               "fwbw_GBps": round((bf + bb) / (f_b2b + b_b2b) * 1e-3, 1),
+               "fwbw_frac_of_peak": round((bf + bb) / (f_b2b + b_b2b) * 1e-3 / PEAK_HBM_GBPS, 4),
+               "bytes_fw": bf, "bytes_bw": bb, "input_sets": n}
+        print(json.dumps(rec), flush=True)
+        log(f"{name:48s} fw {f_b2b:8.1f} us {rec['fw_GBps']:7.0f} GB/s | bw {b_b2b:8.1f} us "
+            f"{rec['bw_GBps']:7.0f} GB/s | fw+bw {rec['fwbw_GBps']:7.0f} GB/s")
+        del keep, fw, bw
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.table:
+        run_table()
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only; multi-GPU runs (--gpus N > 1) are not "
               "supported. Rows shard across GPUs with no communication except one 2*C-float "
@@ -135,18 +388,20 @@ def main():
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed region
-    # The dominant kernel (softmax backward: 3 tensor passes of the quadratic score tensor)
-    # is bracketed by HIP events on the stream it runs on, inside the timed steps.
+    # The dominant kernel (softmax backward: three passes over the quadratic score tensor) is
+    # timed inside the timed steps with HIP events that the kernel itself records at its start
+    # and end (lnr_time_next_launch), on the stream it runs on.
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    hev = HipEvents()
+    ev_a, ev_b = hev.create(K), hev.create(K)
+    hook = lnr.load().lnr_time_next_launch
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         sfw, sbw, lfw, lbw = sets[i % n_sets]["calls"]
         sfw()
-        evs[i][0].record()
+        hook(ev_a[i], ev_b[i])
         sbw()
-        evs[i][1].record()
         lfw()
         lbw()
     torch.cuda.synchronize()
@@ -154,31 +409,41 @@ def main():
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / K
     value = step_bytes * K / elapsed / 1e9
-    sbw_ms = [a.elapsed_time(b) for a, b in evs]
+    sbw_ms = [hev.elapsed_ms(a, b) for a, b in zip(ev_a, ev_b)]
+    hev.destroy(ev_a + ev_b)
     sbw_avg_us = statistics.mean(sbw_ms) * 1e3
     sbw_gbps = b_sbw / (sbw_avg_us * 1e-6) / 1e9
     log(f"step {ms_per_step * 1e3:.1f} us -> {value:.0f} GB/s ({value / PEAK_HBM_GBPS:.1%} of 8 TB/s); "
-        f"softmax_bw {sbw_avg_us:.1f} us -> {sbw_gbps:.0f} GB/s")
+        f"softmax_bw kernel {sbw_avg_us:.1f} us -> {sbw_gbps:.0f} GB/s")
 
     # ---------------------------------------------------------------- diagnostics (untimed)
     ops = {}
     if not args.no_ops:
+        # Per operation: the whole call bracketed by events (includes the launch latency of
+        # each of its kernels), and the first kernel's own duration through the hook.
         names = ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw")
         nbytes = (b_sfw, b_sbw, b_lfw, b_lbw)
         reps = max(20, min(K, 200))
         for k, (name, nb) in enumerate(zip(names, nbytes)):
             pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            ka, kb = hev.create(reps), hev.create(reps)
             for i in range(reps):
                 c = sets[i % n_sets]["calls"][k]
                 pairs[i][0].record()
+                hook(ka[i], kb[i])
                 c()
                 pairs[i][1].record()
             torch.cuda.synchronize()
             us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
-            med = us[len(us) // 2]
-            ops[name] = {"bytes": nb, "median_us": round(med, 2), "min_us": round(us[0], 2),
+            kus = sorted(hev.elapsed_ms(a, b) * 1e3 for a, b in zip(ka, kb))
+            hev.destroy(ka + kb)
+            med, kmed = us[len(us) // 2], kus[len(kus) // 2]
+            ops[name] = {"bytes": nb, "call_median_us": round(med, 2),
+                         "kernel_median_us": round(kmed, 2),
                          "GBps": round(nb / (med * 1e-6) / 1e9, 1),
                          "frac_of_peak": round(nb / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+            if name != "layernorm_bw":   # one kernel: its own duration is the op's
+                ops[name]["kernel_GBps"] = round(nb / (kmed * 1e-6) / 1e9, 1)
         # streaming copy ceiling: 16-byte loads/stores over 1 GiB
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -192,11 +457,12 @@ def main():
             b.record()
         torch.cuda.synchronize()
         cus = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)[5]
-        ops["copy_1GiB"] = {"bytes": 2 * n, "median_us": round(cus, 1),
+        ops["copy_1GiB"] = {"bytes": 2 * n, "call_median_us": round(cus, 1),
                             "GBps": round(2 * n / (cus * 1e-6) / 1e9, 1)}
         del src, dst
         for k, v in ops.items():
-            log(f"  {k:16s} {v['median_us']:9.1f} us  {v['GBps']:8.1f} GB/s")
+            log(f"  {k:16s} call {v['call_median_us']:9.1f} us  {v['GBps']:8.1f} GB/s"
+                + (f"  | kernel {v['kernel_median_us']:8.1f} us" if "kernel_median_us" in v else ""))
 
     # ---------------------------------------------------------------- roofline
     traffic = None
@@ -208,7 +474,8 @@ def main():
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "kernel": "softmax_bw_vec (attn_softmax_bw)", "achieved": round(sbw_gbps, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(sbw_gbps / PEAK_HBM_GBPS, 4),
-                "traffic": traffic, "avg_us": round(sbw_avg_us, 2), "bytes_per_launch": b_sbw}
+                "traffic": traffic, "avg_us": round(sbw_avg_us, 3), "launches": K,
+                "bytes_per_launch": b_sbw}
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None

@@ -165,6 +165,18 @@ LNR_API int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, co
 LNR_API int lnr_copy(void *dst, const void *src, size_t bytes, void *stream);
 
 /*
+ * lnr_time_next_launch -- measurement helper, not part of the method: the next kernel that
+ * the calling thread launches through this library records `start_event` when that kernel
+ * begins and `stop_event` when it ends (both hipEvent_t, created by the caller with timing
+ * enabled), so hipEventElapsedTime gives that kernel's own duration without the dispatch
+ * latency an event recorded before the call would include. Only the next launch is timed,
+ * then the request is cleared; for an operation of two kernels (layernorm_bw) that is the
+ * first kernel. Both NULL cancels a pending request; exactly one NULL is LNR_ERR_NULL.
+ * Per-thread state; touches no device until the timed launch.
+ */
+LNR_API int lnr_time_next_launch(void *start_event, void *stop_event);
+
+/*
  * lnr_softmax_plan -- introspection of the row-length dispatch (the compile-time template
  * choice at launch that the L10 lecture's "Technique 2" describes and the HW4 page's
  * softmax backward asks for): for rows of Tk elements of `dtype` in 16-byte-aligned

@@ -70,6 +70,8 @@ def load():
     lib.layernorm_bw_workspace_bytes.restype = sz
     lib.layernorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
     lib.lnr_copy.argtypes = [vp, vp, sz, vp]
+    lib.lnr_time_next_launch.argtypes = [vp, vp]
+    lib.lnr_time_next_launch.restype = ci
     lib.lnr_strerror.argtypes = [ci]
     lib.lnr_strerror.restype = ctypes.c_char_p
     lib.lnr_build_info.restype = ctypes.c_char_p

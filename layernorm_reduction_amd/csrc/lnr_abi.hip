@@ -45,6 +45,13 @@ extern "C" int lnr_copy(void *dst, const void *src, size_t bytes, void *stream) 
                             static_cast<const f32x4 *>(src), n));
 }
 
+extern "C" int lnr_time_next_launch(void *start_event, void *stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) return LNR_ERR_NULL;
+    next_launch_events() = NextLaunchEvents{static_cast<hipEvent_t>(start_event),
+                                            static_cast<hipEvent_t>(stop_event)};
+    return LNR_OK;
+}
+
 extern "C" const char *lnr_strerror(int status) {
     switch (status) {
         case LNR_OK: return "success";

@@ -3,6 +3,7 @@
 // which could report an unrelated earlier error of the caller).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -33,6 +34,17 @@ inline bool bad_alias(const void *out, const void *in, size_t n) {
     return out != in && overlap(out, n, in, n);
 }
 
+// Measurement hook (lnr_time_next_launch): events that the next launch made by this thread
+// records at its kernel's own start and end. Cleared by that launch.
+struct NextLaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+inline NextLaunchEvents &next_launch_events() {
+    static thread_local NextLaunchEvents ev;
+    return ev;
+}
+
 // Launch `kernel` with argument values converted to its exact parameter types and return
 // the status of this launch.
 template <typename... KArgs, typename... Args>
@@ -45,6 +57,13 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStr
         int i = 0;
         ((argv[i++] = static_cast<void *>(&v)), ...);
     }, values);
+    NextLaunchEvents &ev = next_launch_events();
+    if (ev.start != nullptr) {
+        const hipEvent_t a = ev.start, b = ev.stop;
+        ev = NextLaunchEvents{};
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0,
+                                  stream, a, b, 0);
+    }
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, stream);
 }
 

@@ -40,9 +40,15 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_time_next_launch_validation(lib):
+    assert lib.lnr_time_next_launch(None, A) == NULL
+    assert lib.lnr_time_next_launch(A, None) == NULL
+    assert lib.lnr_time_next_launch(None, None) == OK       # cancels; no device touched
 
 
 def test_strerror_and_build_info(lib):
