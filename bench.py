@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--table", action="store_true",
                    help="time every op at every workload shape (row-length sweep, hidden-size sweep, "
                         "encoder layer fp16/fp32); one JSON line per case")
+    p.add_argument("--cpu-table", action="store_true",
+                   help="CPU only: time the oracle's fw+bw on the tiny, GPT-2 and hidden-size-sweep "
+                        "shapes with all host threads and with one thread; one JSON line per case")
     p.add_argument("--summarize-profiles", metavar="DIR",
                    help="CPU only: read the rocprofv3 outputs under DIR (prof_<w>/, pmc_fetch_<w>/, "
                         "pmc_write_<w>/) and write the summaries under profiles/")
@@ -215,8 +218,15 @@ def table_cases():
 
 def run_table():
     """Back-to-back launches of each op over rotating buffers (>= 1 GiB footprint): average
-    per launch from one event pair around the batch, plus the kernel's own median duration
-    from events the kernel records (first kernel only for layernorm_bw)."""
+    per launch from one event pair around the batch, plus the kernel's own min / median / p90
+    duration from events the kernel records (first kernel only for layernorm_bw).
+
+    Beside each op, the same-size streaming ceiling: the library's 16-byte non-temporal copy
+    (read one tensor, write one: the forward pattern) and read-two-write-one (lnr_xor2: the
+    backward pattern) over tensors of the op's own size, timed the same way. Small tensors
+    cannot reach the large-transfer bandwidth (launch ramp and drain), so
+    fwbw_frac_of_ceiling = (t_copy + t_xor2) / (t_fw + t_bw) says how close an op comes to
+    what any streaming kernel achieves at its size."""
     import torch
     import layernorm_reduction_amd as lnr
     from layernorm_reduction_amd import workloads as W
@@ -246,7 +256,31 @@ def run_table():
         torch.cuda.synchronize()
         k = sorted(hev.elapsed_ms(x, y) * 1e3 for x, y in zip(ka, kb))
         hev.destroy(ka + kb)
-        return b2b, k[len(k) // 2]
+        return b2b, {"min": round(k[0], 2), "median": round(k[len(k) // 2], 2),
+                     "p90": round(k[int(0.9 * (len(k) - 1))], 2)}
+
+    def ceiling(nbytes):
+        """(copy us, read-two-write-one us) over rotating nbytes tensors, back to back."""
+        nb = (nbytes + 15) // 16 * 16
+        n = max(2, math.ceil(MIN_FOOTPRINT / (3 * nb)))
+        bufs = [[torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(3)] for _ in range(n)]
+        cp = [(lambda b=b: lnr.copy_bytes(b[2], b[0])) for b in bufs]
+        xr = [(lambda b=b: lnr.xor_bytes(b[2], b[0], b[1])) for b in bufs]
+        out = []
+        for calls in (cp, xr):
+            for c in calls[:3]:
+                c()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                calls[i % len(calls)]()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) * 1e3 / reps)
+        del bufs
+        torch.cuda.empty_cache()
+        return out
 
     for name, kind, shape, dt, extra in table_cases():
         s = W.dtype_size(dt)
@@ -269,6 +303,7 @@ def run_table():
                 keep += [x, dy, y, dx, m]
             bf = W.softmax_fw_bytes(B, H, T, T, s, has_mask=extra["mask"])
             bb = W.softmax_bw_bytes(B, H, T, T, s)
+            rows, tensor = B * H * T, per
         else:
             N, C = shape
             per = N * C * s
@@ -291,26 +326,96 @@ def run_table():
                 keep += [x, dy, gm, bt, y, dx, mean, rstd, dg, db, ws]
             bf = W.layernorm_fw_bytes(N, C, s)
             bb = W.layernorm_bw_bytes(N, C, s)
+            rows, tensor = N, per
         torch.cuda.synchronize()
         f_b2b, f_k = timed(fw)
         b_b2b, b_k = timed(bw)
+        del keep, fw, bw
+        torch.cuda.empty_cache()
+        c_fw, c_bw = ceiling(tensor)
         rec = {"case": name, "fw_us": round(f_b2b, 2), "bw_us": round(b_b2b, 2),
-               "fw_kernel_us": round(f_k, 2), "bw_first_kernel_us": round(b_k, 2),
+               "fw_kernel_us": f_k, "bw_first_kernel_us": b_k,
                "fw_GBps": round(bf / f_b2b * 1e-3, 1), "bw_GBps": round(bb / b_b2b * 1e-3, 1),
                "fwbw_GBps": round((bf + bb) / (f_b2b + b_b2b) * 1e-3, 1),
                "fwbw_frac_of_peak": round((bf + bb) / (f_b2b + b_b2b) * 1e-3 / PEAK_HBM_GBPS, 4),
+               "fw_rows_per_s": round(rows / (f_b2b * 1e-6)), "bw_rows_per_s": round(rows / (b_b2b * 1e-6)),
+               "ceiling_copy_us": round(c_fw, 2), "ceiling_read2write1_us": round(c_bw, 2),
+               "fwbw_frac_of_ceiling": round((c_fw + c_bw) / (f_b2b + b_b2b), 4),
                "bytes_fw": bf, "bytes_bw": bb, "input_sets": n}
         print(json.dumps(rec), flush=True)
         log(f"{name:48s} fw {f_b2b:8.1f} us {rec['fw_GBps']:7.0f} GB/s | bw {b_b2b:8.1f} us "
-            f"{rec['bw_GBps']:7.0f} GB/s | fw+bw {rec['fwbw_GBps']:7.0f} GB/s")
-        del keep, fw, bw
-        torch.cuda.empty_cache()
+            f"{rec['bw_GBps']:7.0f} GB/s | fw+bw {rec['fwbw_GBps']:7.0f} GB/s "
+            f"({rec['fwbw_frac_of_peak']:.0%} of 8 TB/s, {rec['fwbw_frac_of_ceiling']:.0%} of the same-size ceiling)")
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_cpu_table():
+    """The oracle (fp64 correctness reference, not a tuned CPU kernel) on the tiny, GPT-2 and
+    hidden-size-sweep shapes: wall-clock median of 3 runs of fw + bw, with every host thread
+    the process may use and with one, as rows/s and algorithmic GB/s (same byte formulas as
+    the GPU lines, at the storage dtype)."""
+    import oracle
+    from layernorm_reduction_amd import workloads as W
+
+    affinity = len(os.sched_getaffinity(0))
+    model = cpu_model()
+    cases = []
+    [s1], [l1] = W.workload1()
+    [s2], [l2] = W.workload2()
+    cases += [("w1", s1), ("w1", l1), ("w2", s2), ("w2", l2)]
+    cases += [("w4", W.workload4_case(C)) for C in W.LAYERNORM_C_SWEEP]
+    for tag, case in cases:
+        st = W.dtype_size(case.dtype)
+        if hasattr(case, "Tk"):
+            what = f"softmax [{case.B},{case.H},{case.Tq},{case.Tk}]"
+            rows = case.B * case.H * case.Tq
+            nbytes = (W.softmax_fw_bytes(case.B, case.H, case.Tq, case.Tk, st, has_mask=case.mask is not None)
+                      + W.softmax_bw_bytes(case.B, case.H, case.Tq, case.Tk, st))
+
+            def run(c=case):
+                y = oracle.softmax_fw(c.x, c.mask, c.causal)
+                oracle.softmax_bw(y, c.dy)
+        else:
+            what = f"layernorm [{case.N},{case.C}]"
+            rows = case.N
+            nbytes = W.layernorm_fw_bytes(case.N, case.C, st) + W.layernorm_bw_bytes(case.N, case.C, st)
+
+            def run(c=case):
+                oracle.layernorm_fw(c.x, c.gamma, c.beta, c.eps)
+                oracle.layernorm_bw(c.x, c.dy, c.gamma, c.eps)
+        for nthreads in (affinity, 1):
+            oracle.set_threads(nthreads)
+            times = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                run()
+                times.append(time.perf_counter() - t0)
+            t = statistics.median(times)
+            rec = {"case": f"{tag} {what} fw+bw", "threads": oracle.threads(), "seconds": round(t, 4),
+                   "rows_per_s": round(rows / t), "GBps": round(nbytes / t / 1e9, 3),
+                   "cpu_model": model, "kind": "oracle",
+                   "note": "fp64 correctness oracle, not a tuned CPU kernel"}
+            print(json.dumps(rec), flush=True)
+            log(f"{rec['case']:44s} {nthreads:3d} threads {t * 1e3:10.1f} ms  {rec['GBps']:8.3f} GB/s")
+    oracle.set_threads(affinity)
 
 
 def main():
     args = parse()
     if args.table:
         run_table()
+        return
+    if args.cpu_table:
+        run_cpu_table()
         return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload)
@@ -460,6 +565,30 @@ def main():
         ops["copy_1GiB"] = {"bytes": 2 * n, "call_median_us": round(cus, 1),
                             "GBps": round(2 * n / (cus * 1e-6) / 1e9, 1)}
         del src, dst
+        # Same-size streaming ceilings, back to back over rotating buffers like the step: a
+        # copy of one op tensor (the forward pattern) and read-two-write-one (the backward).
+        torch.cuda.empty_cache()
+        for op, nb, pattern in (("attn_softmax_fw", sc.x.numel() * s, "copy"),
+                                ("attn_softmax_bw", sc.x.numel() * s, "read2write1"),
+                                ("layernorm_fw", lc.x.numel() * s, "copy"),
+                                ("layernorm_bw", lc.x.numel() * s, "read2write1")):
+            nbuf = max(2, math.ceil(MIN_FOOTPRINT / (3 * nb)))
+            bufs = [[torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(3)] for _ in range(nbuf)]
+            go = ((lambda b: lnr.copy_bytes(b[2], b[0])) if pattern == "copy"
+                  else (lambda b: lnr.xor_bytes(b[2], b[0], b[1])))
+            for i in range(3):
+                go(bufs[i % nbuf])
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(reps):
+                go(bufs[i % nbuf])
+            b.record()
+            torch.cuda.synchronize()
+            cu = a.elapsed_time(b) * 1e3 / reps
+            ops[op]["same_size_ceiling"] = {"pattern": pattern, "tensor_bytes": nb, "b2b_us": round(cu, 2)}
+            del bufs
+            torch.cuda.empty_cache()
         for k, v in ops.items():
             log(f"  {k:16s} call {v['call_median_us']:9.1f} us  {v['GBps']:8.1f} GB/s"
                 + (f"  | kernel {v['kernel_median_us']:8.1f} us" if "kernel_median_us" in v else ""))
@@ -509,6 +638,7 @@ def main():
                 break
         tmed = statistics.median(times)
         cpu = {"value": round(step_bytes * frac / tmed / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+               "cpu_model": cpu_model(),
                "kind": "oracle", "sample": sample, "seconds_per_sample": round(tmed, 3),
                "repeats": len(times), "note": "fp64 correctness oracle, not a tuned CPU kernel"}
         log(f"oracle: {tmed:.2f} s per sample on {cpu['cores']} threads -> {cpu['value']} GB/s")

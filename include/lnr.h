@@ -165,6 +165,15 @@ LNR_API int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, co
 LNR_API int lnr_copy(void *dst, const void *src, size_t bytes, void *stream);
 
 /*
+ * lnr_xor2 -- measurement helper, not part of the method: writes dst = a XOR b over `bytes`
+ * bytes, reading two buffers and writing one (the traffic pattern of both backward kernels)
+ * with the same 128-bit non-temporal accesses as lnr_copy. It gives the achievable streaming
+ * ceiling for that pattern at a given size. dst must not overlap a or b (a and b may be the
+ * same buffer); bytes must be a multiple of 16 and all pointers 16-byte aligned.
+ */
+LNR_API int lnr_xor2(void *dst, const void *a, const void *b, size_t bytes, void *stream);
+
+/*
  * lnr_time_next_launch -- measurement helper, not part of the method: the next kernel that
  * the calling thread launches through this library records `start_event` when that kernel
  * begins and `stop_event` when it ends (both hipEvent_t, created by the caller with timing

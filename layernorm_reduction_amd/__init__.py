@@ -21,7 +21,7 @@ import os
 
 __all__ = [
     "LnrError", "load", "library_path", "attn_softmax_fw", "attn_softmax_bw", "layernorm_fw",
-    "layernorm_bw", "layernorm_bw_workspace_bytes", "copy_bytes", "softmax_plan",
+    "layernorm_bw", "layernorm_bw_workspace_bytes", "copy_bytes", "xor_bytes", "softmax_plan",
     "layernorm_plan", "LNR_F32", "LNR_F16", "SOFTMAX_MAX_TK", "LAYERNORM_MAX_C",
 ]
 
@@ -70,6 +70,7 @@ def load():
     lib.layernorm_bw_workspace_bytes.restype = sz
     lib.layernorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
     lib.lnr_copy.argtypes = [vp, vp, sz, vp]
+    lib.lnr_xor2.argtypes = [vp, vp, vp, sz, vp]
     lib.lnr_time_next_launch.argtypes = [vp, vp]
     lib.lnr_time_next_launch.restype = ci
     lib.lnr_strerror.argtypes = [ci]
@@ -79,7 +80,7 @@ def load():
     lib.lnr_softmax_plan.argtypes = [i64, ci, ci, ip, ip, ip]
     lib.lnr_layernorm_plan.argtypes = [i64, i64, ci, ci, ip, ip, ip, ip, ctypes.POINTER(i64)]
     for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw", "lnr_copy",
-              "lnr_softmax_plan", "lnr_layernorm_plan"):
+              "lnr_xor2", "lnr_softmax_plan", "lnr_layernorm_plan"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -279,6 +280,17 @@ def copy_bytes(dst, src):
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst is smaller than src")
     _check(load().lnr_copy(_ptr(dst), _ptr(src), n, _stream(src)), "lnr_copy")
+    return dst
+
+
+def xor_bytes(dst, a, b):
+    """dst = a XOR b bytewise: reads two buffers, writes one (measurement helper)."""
+    for t, nm in ((a, "a"), (b, "b"), (dst, "dst")):
+        _dev(t, nm)
+    n = a.numel() * a.element_size()
+    if b.numel() * b.element_size() < n or dst.numel() * dst.element_size() < n:
+        raise ValueError("b and dst must be at least as large as a")
+    _check(load().lnr_xor2(_ptr(dst), _ptr(a), _ptr(b), n, _stream(a)), "lnr_xor2")
     return dst
 
 

@@ -1,5 +1,6 @@
-// lnr_abi.hip -- status strings, build information and the streaming-copy helper used to
-// measure the achievable HBM ceiling that the row kernels are compared with.
+// lnr_abi.hip -- status strings, build information and the streaming helpers (copy, and
+// read-two-write-one) used to measure the achievable HBM ceiling that the row kernels are
+// compared with.
 #include "lnr_common.h"
 #include "lnr_prims.h"
 
@@ -26,6 +27,29 @@ __global__ __launch_bounds__(kCopyWG) void copy16(f32x4 *__restrict__ dst,
     }
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Read two, write one (the access pattern of both backward kernels): dst = a XOR b, 16 bytes
+// per access, the same one-shot grid and non-temporal policy as copy16.
+__global__ __launch_bounds__(kCopyWG) void xor16(u32x4 *__restrict__ dst, const u32x4 *__restrict__ a,
+                                                  const u32x4 *__restrict__ b, int64_t n) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyWG * kCopyUnroll + threadIdx.x;
+    u32x4 va[kCopyUnroll], vb[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kCopyWG;
+        if (i < n) {
+            va[u] = __builtin_nontemporal_load(a + i);
+            vb[u] = __builtin_nontemporal_load(b + i);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * kCopyWG;
+        if (i < n) __builtin_nontemporal_store(va[u] ^ vb[u], dst + i);
+    }
+}
+
 }  // namespace lnr
 
 using namespace lnr;
@@ -43,6 +67,21 @@ extern "C" int lnr_copy(void *dst, const void *src, size_t bytes, void *stream) 
     return status_of(launch(copy16, dim3(static_cast<uint32_t>(blocks)), dim3(kCopyWG),
                             static_cast<hipStream_t>(stream), static_cast<f32x4 *>(dst),
                             static_cast<const f32x4 *>(src), n));
+}
+
+extern "C" int lnr_xor2(void *dst, const void *a, const void *b, size_t bytes, void *stream) {
+    if (bytes == 0) return LNR_OK;
+    if (dst == nullptr || a == nullptr || b == nullptr) return LNR_ERR_NULL;
+    if (bytes % 16 != 0) return LNR_ERR_SHAPE;
+    if (!aligned_to(dst, 16) || !aligned_to(a, 16) || !aligned_to(b, 16)) return LNR_ERR_ALIGN;
+    if (overlap(dst, bytes, a, bytes) || overlap(dst, bytes, b, bytes)) return LNR_ERR_ALIAS;
+    const int64_t n = static_cast<int64_t>(bytes / 16);
+    const int64_t per_block = static_cast<int64_t>(kCopyWG) * kCopyUnroll;
+    const int64_t blocks = (n + per_block - 1) / per_block;
+    if (blocks > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    return status_of(launch(xor16, dim3(static_cast<uint32_t>(blocks)), dim3(kCopyWG),
+                            static_cast<hipStream_t>(stream), static_cast<u32x4 *>(dst),
+                            static_cast<const u32x4 *>(a), static_cast<const u32x4 *>(b), n));
 }
 
 extern "C" int lnr_time_next_launch(void *start_event, void *stop_event) {

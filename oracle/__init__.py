@@ -74,6 +74,8 @@ def _load():
     lib.lnr_oracle_layernorm_bw_given_stats.restype = None
     lib.lnr_oracle_threads.argtypes = []
     lib.lnr_oracle_threads.restype = ctypes.c_int
+    lib.lnr_oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.lnr_oracle_set_threads.restype = None
     for f in (lib.lnr_oracle_softmax_fw, lib.lnr_oracle_softmax_fw_rows, lib.lnr_oracle_softmax_bw,
               lib.lnr_oracle_layernorm_fw, lib.lnr_oracle_layernorm_bw_dx,
               lib.lnr_oracle_layernorm_bw_dgamma_dbeta, lib.lnr_oracle_rmsnorm_fw,
@@ -86,6 +88,12 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle's loops use."""
     return int(_load().lnr_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use n OpenMP threads from now on (timing only: each output element is computed by one
+    thread in a fixed order, so results do not depend on n)."""
+    _load().lnr_oracle_set_threads(int(n))
 
 
 def _f64(a) -> np.ndarray:

@@ -352,3 +352,13 @@ ORACLE_API int lnr_oracle_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the parallel loops that follow (timing only; results do not depend on it). */
+ORACLE_API void lnr_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

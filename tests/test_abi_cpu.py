@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -162,6 +162,15 @@ def test_copy_validation(lib):
     assert lib.lnr_copy(A, A + 16, 64, None) == ALIAS
     assert lib.lnr_copy(None, A, 16, None) == NULL
     assert lib.lnr_copy(A, A + 2 ** 30, 0, None) == OK
+
+
+def test_xor2_validation(lib):
+    B2 = A + 2 ** 30
+    assert lib.lnr_xor2(A, B2, B2, 15, None) == SHAPE
+    assert lib.lnr_xor2(A, B2 + 8, B2, 16, None) == ALIGN
+    assert lib.lnr_xor2(A, B2, A + 16, 64, None) == ALIAS
+    assert lib.lnr_xor2(A, None, B2, 16, None) == NULL
+    assert lib.lnr_xor2(A, B2, B2, 0, None) == OK
 
 
 # ------------------------------------------------------------------------- dispatcher

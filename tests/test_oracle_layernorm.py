@@ -219,3 +219,19 @@ def test_rmsnorm_backward_matches_autograd_and_finite_differences():
     fd = (np.sum(dy * oracle.rmsnorm_fw(xp, g, RMS_EPS)[0]) -
           np.sum(dy * oracle.rmsnorm_fw(xm, g, RMS_EPS)[0])) / (2 * h)
     assert abs(fd - dx[i, j]) <= 1e-7
+
+
+def test_results_do_not_depend_on_the_thread_count():
+    """The CPU baseline times the oracle at several thread counts; every output element is
+    computed by one thread in a fixed order, so the values must be bitwise identical."""
+    x, g, b, dy = _case(300, 96, 14, offset_std=1.0)
+    n0 = oracle.threads()
+    try:
+        ref = [*oracle.layernorm_fw(x, g, b), *oracle.layernorm_bw(x, dy, g)]
+        oracle.set_threads(1)
+        assert oracle.threads() == 1
+        one = [*oracle.layernorm_fw(x, g, b), *oracle.layernorm_bw(x, dy, g)]
+    finally:
+        oracle.set_threads(n0)
+    for u, v in zip(ref, one):
+        assert np.array_equal(u, v)
