@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--table", action="store_true",
                    help="time every op at every workload shape (row-length sweep, hidden-size sweep, "
                         "encoder layer fp16/fp32); one JSON line per case")
+    p.add_argument("--match", default="", metavar="TEXT",
+                   help="with --table: only the cases whose name contains TEXT")
     p.add_argument("--cpu-table", action="store_true",
                    help="CPU only: time the oracle's fw+bw on the tiny, GPT-2 and hidden-size-sweep "
                         "shapes with all host threads and with one thread; one JSON line per case")
@@ -216,7 +218,7 @@ def table_cases():
     return cases
 
 
-def run_table():
+def run_table(match: str = ""):
     """Back-to-back launches of each op over rotating buffers (>= 1 GiB footprint): average
     per launch from one event pair around the batch, plus the kernel's own min / median / p90
     duration from events the kernel records (first kernel only for layernorm_bw).
@@ -283,6 +285,8 @@ def run_table():
         return out
 
     for name, kind, shape, dt, extra in table_cases():
+        if match not in name:
+            continue
         s = W.dtype_size(dt)
         if kind == "softmax":
             B, H, T, _ = shape
@@ -412,7 +416,7 @@ def run_cpu_table():
 def main():
     args = parse()
     if args.table:
-        run_table()
+        run_table(args.match)
         return
     if args.cpu_table:
         run_cpu_table()

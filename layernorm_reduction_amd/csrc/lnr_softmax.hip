@@ -21,25 +21,33 @@
 #include <math.h>
 
 #include "lnr_common.h"
+#include "lnr_fastdiv.h"
 #include "lnr_prims.h"
 
 namespace lnr {
+
+// The forward vector kernel indexes rows in 32 bits (multiply-shift division for the batch and
+// query indices); larger row counts take the element-wise kernel.
+constexpr int64_t kVecMaxRows = int64_t{UINT32_MAX} - 4096;
 
 // ------------------------------------------------------------------------------------------
 // Vector kernels.
 // ------------------------------------------------------------------------------------------
 template <typename T, int G, int IT, int WG>
 __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
-                                                     const T *__restrict__ mask, int64_t rows,
-                                                     int32_t Tq, int32_t Tk,
-                                                     int64_t rows_per_batch, int32_t causal) {
+                                                     const T *__restrict__ mask, uint32_t rows,
+                                                     int32_t Tk, DivU32 per_batch,
+                                                     DivU32 per_query, int32_t causal) {
     constexpr int V = Vec16<T>::N;
     constexpr int RPB = WG / G;
     const int lane = threadIdx.x % G;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / G;
+    // rows < 2^32 - 4096 (checked by the host), so the row index and the one past the last
+    // workgroup fit in 32 bits, and the batch and query indices come from multiply-shift
+    // division: short rows leave few elements per lane to amortise the index math over.
+    const uint32_t row = blockIdx.x * static_cast<uint32_t>(RPB) + threadIdx.x / G;
     const bool live = row < rows;
     const int nvec = Tk / V;
-    const int64_t base = (live ? row : 0) * static_cast<int64_t>(Tk);
+    const int64_t base = static_cast<int64_t>(live ? row : 0u) * Tk;
 
     float z[IT][V];
 #pragma unroll
@@ -53,7 +61,7 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
         }
     }
     if (mask != nullptr) {
-        const T *mrow = mask + (live ? row / rows_per_batch : 0) * static_cast<int64_t>(Tk);
+        const T *mrow = mask + static_cast<int64_t>(divu32(live ? row : 0u, per_batch)) * Tk;
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int c = k * G + lane;
@@ -66,7 +74,7 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
         }
     }
     if (causal) {
-        const int qi = static_cast<int>(row % Tq);
+        const int qi = static_cast<int>(row - divu32(row, per_query) * per_query.d);
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
 #pragma unroll
@@ -92,7 +100,9 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
             s += z[k][e];
         }
     s = group_allreduce<G>(s, OpSum());
-    const float inv = s > 0.f ? 1.0f / s : 0.f;
+    // v_rcp_f32 (1 ulp) instead of the IEEE divide sequence: s >= 1 (the max term is 1), and
+    // the result is far inside the tolerance.
+    const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
 
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
@@ -218,8 +228,10 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 // table for the forward and one for the backward. Capacity G * IT * V equals the bucket
 // length; rows shorter than their bucket leave the trailing vectors idle. The bucket lengths
 // are the HW4 page's template list. Measured on MI355X: the forward (mask add, max, exp,
-// sum, scale) runs best with 2-4 vectors per lane; the backward (one product sum) with one
-// vector per lane and as many lanes per row as the row allows.
+// sum, scale) runs best with 2-4 vectors per lane from 256 columns up, and with 1-2 vectors
+// per lane on short rows, where fewer, wider groups keep each load instruction on whole
+// 128-byte lines; the backward (one product sum) with one vector per lane and as many lanes
+// per row as the row allows.
 // ------------------------------------------------------------------------------------------
 struct Plan {
     int bucket;  // longest row this instantiation takes; 0 = element-wise fallback
@@ -230,12 +242,12 @@ struct Plan {
 
 template <typename T> struct SoftmaxFwTable;
 template <> struct SoftmaxFwTable<f16> {   // V = 8
-    static constexpr Plan plans[] = {{32, 4, 1, 256},   {64, 4, 2, 256},   {128, 4, 4, 256},
+    static constexpr Plan plans[] = {{32, 4, 1, 512},   {64, 8, 1, 512},   {128, 8, 2, 256},
                                      {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 32, 2, 256},
                                      {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
 };
 template <> struct SoftmaxFwTable<float> { // V = 4
-    static constexpr Plan plans[] = {{32, 4, 2, 256},   {64, 4, 4, 256},   {128, 8, 4, 256},
+    static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 8, 4, 256},
                                      {256, 16, 4, 256}, {384, 32, 3, 256}, {512, 32, 4, 256},
                                      {768, 64, 3, 256}, {1024, 64, 4, 256}, {2048, 64, 8, 256}};
 };
@@ -274,7 +286,9 @@ static hipError_t launch_fw_vec(const SoftmaxFwArgs &a, hipStream_t st) {
     const int64_t blocks = (a.rows + RPB - 1) / RPB;
     return launch(softmax_fw_vec<T, G, IT, WG>, dim3(static_cast<uint32_t>(blocks)),
                   dim3(WG), st, static_cast<T *>(a.out), static_cast<const T *>(a.inp),
-                  static_cast<const T *>(a.mask), a.rows, a.Tq, a.Tk, a.rows_per_batch, a.causal);
+                  static_cast<const T *>(a.mask), static_cast<uint32_t>(a.rows), a.Tk,
+                  make_divu32(static_cast<uint32_t>(a.rows_per_batch)),
+                  make_divu32(static_cast<uint32_t>(a.Tq)), a.causal);
 }
 
 template <typename T, int G, int IT, int WG>
@@ -320,6 +334,8 @@ static int check_common(const void *a, const void *b, const void *c, int64_t B, 
     if (B < 0 || H < 0 || Tq < 0 || Tk < 1) return LNR_ERR_SHAPE;
     if (Tk > LNR_SOFTMAX_MAX_TK) return LNR_ERR_UNSUPPORTED;
     if (Tq > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    // B * H * Tq must not overflow (the grid limit below is far smaller than INT64_MAX).
+    if (H > 0 && Tq > 0 && B > INT64_MAX / H / Tq) return LNR_ERR_UNSUPPORTED;
     const int64_t rows = B * H * Tq;
     if (rows == 0) return LNR_OK;
     if (a == nullptr || b == nullptr || c == nullptr) return LNR_ERR_NULL;
@@ -353,7 +369,8 @@ extern "C" int attn_softmax_fw(void *out, const void *inp, const void *mask, int
     SoftmaxFwArgs a{out, inp, mask, rows, static_cast<int32_t>(Tq), static_cast<int32_t>(Tk),
                     H * Tq, causal ? 1 : 0};
     const bool vec = (static_cast<size_t>(Tk) * es) % 16 == 0 && aligned_to(out, 16) &&
-                     aligned_to(inp, 16) && (mask == nullptr || aligned_to(mask, 16));
+                     aligned_to(inp, 16) && (mask == nullptr || aligned_to(mask, 16)) &&
+                     rows <= kVecMaxRows;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (vec) {
