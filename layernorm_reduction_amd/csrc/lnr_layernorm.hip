@@ -319,33 +319,48 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
 
 // ------------------------------------------------------------------------------------------
 // Column finalize: dgamma/dbeta = fixed-order sums of the P partial rows.
-// Block = 16 columns x 16 slices; slice s sums partials p = s, s+16, s+32, ... in order,
-// then slice 0 adds the 16 slice sums in slice order.
+// Block = TILE columns x SLICES slices; slice s sums partials p = s, s+SLICES, s+2*SLICES, ...
+// in that order (with BATCH > 1, BATCH loads in flight at a time, added in order), then slice 0 adds the
+// slice sums in slice order. Two shapes, measured on MI355X: 16 x 16 up to 1024 columns
+// (the kernel sits at its launch floor there), 32 x 32 with 8 loads in flight above (C=4096:
+// 4.1 -> 3.3 us).
 // ------------------------------------------------------------------------------------------
-constexpr int kColTile = 16;
-constexpr int kColSlices = 16;
-
-template <typename T>
-__global__ __launch_bounds__(kColTile *kColSlices) void layernorm_bw_colsum(
+template <typename T, int TILE, int SLICES, int BATCH>
+__global__ __launch_bounds__(TILE *SLICES) void layernorm_bw_colsum(
     T *__restrict__ dgamma, T *__restrict__ dbeta, const typename Accum<T>::type *__restrict__ part,
     int32_t P, int32_t C) {
     using A = typename Accum<T>::type;
-    __shared__ A slab[kColSlices][kColTile];
-    const int cl = threadIdx.x % kColTile;
-    const int sl = threadIdx.x / kColTile;
+    __shared__ A slab[SLICES][TILE];
+    const int cl = threadIdx.x % TILE;
+    const int sl = threadIdx.x / TILE;
     const int which = blockIdx.y;
-    const int col = blockIdx.x * kColTile + cl;
+    const int col = blockIdx.x * TILE + cl;
     A s = A(0);
     if (col < C) {
+        if constexpr (BATCH == 1) {
 #pragma unroll 8
-        for (int p = sl; p < P; p += kColSlices) s += part[(static_cast<int64_t>(p) * 2 + which) * C + col];
+            for (int p = sl; p < P; p += SLICES)
+                s += part[(static_cast<int64_t>(p) * 2 + which) * C + col];
+        } else {
+            for (int p0 = sl; p0 < P; p0 += SLICES * BATCH) {
+                A v[BATCH];
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u) {
+                    const int p = p0 + u * SLICES;
+                    v[u] = p < P ? part[(static_cast<int64_t>(p) * 2 + which) * C + col] : A(0);
+                }
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u)
+                    if (p0 + u * SLICES < P) s += v[u];
+            }
+        }
     }
     slab[sl][cl] = s;
     __syncthreads();
     if (sl == 0 && col < C) {
         A t = slab[0][cl];
 #pragma unroll
-        for (int k = 1; k < kColSlices; ++k) t += slab[k][cl];
+        for (int k = 1; k < SLICES; ++k) t += slab[k][cl];
         (which == 0 ? dgamma : dbeta)[col] = from_f32<T>(static_cast<float>(t));
     }
 }
@@ -560,10 +575,17 @@ static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
 template <typename T>
 static hipError_t launch_colsum(void *dgamma, void *dbeta, const void *part, int64_t P, int32_t C,
                                 hipStream_t st) {
-    const dim3 grid(static_cast<uint32_t>((C + kColTile - 1) / kColTile), 2);
-    return launch(layernorm_bw_colsum<T>, grid, dim3(kColTile * kColSlices), st,
-                  static_cast<T *>(dgamma), static_cast<T *>(dbeta),
-                  static_cast<const typename Accum<T>::type *>(part), static_cast<int32_t>(P), C);
+    using A = typename Accum<T>::type;
+    if (C <= 1024) {
+        const dim3 grid(static_cast<uint32_t>((C + 15) / 16), 2);
+        return launch(layernorm_bw_colsum<T, 16, 16, 1>, grid, dim3(16 * 16), st,
+                      static_cast<T *>(dgamma), static_cast<T *>(dbeta),
+                      static_cast<const A *>(part), static_cast<int32_t>(P), C);
+    }
+    const dim3 grid(static_cast<uint32_t>((C + 31) / 32), 2);
+    return launch(layernorm_bw_colsum<T, 32, 32, 8>, grid, dim3(32 * 32), st,
+                  static_cast<T *>(dgamma), static_cast<T *>(dbeta), static_cast<const A *>(part),
+                  static_cast<int32_t>(P), C);
 }
 
 static size_t accum_size(lnr_dtype d) { return d == LNR_F16 ? sizeof(float) : sizeof(double); }
