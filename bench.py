@@ -114,13 +114,20 @@ def summarize_profiles(root_dir: str, workload: str):
     with open(os.path.join(out_dir, f"{workload}_kernel_trace.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
+    # The 1 GiB calibration copy: 2^30 / 16 bytes per thread-vector / 4 vectors per thread.
+    calib_grid = str((1 << 30) // 64)
+
     def per_kernel(kind):
         path = os.path.join(root_dir, f"pmc_{kind}_{workload}", f"{workload}_counter_collection.csv")
         if not os.path.exists(path):
             return None
         by = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
-            by[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
+            name = r["Kernel_Name"]
+            if COPY in name:  # the same kernel also measures same-size ceilings: keep 1 GiB only
+                if r["Grid_Size"] != calib_grid:
+                    continue
+            by[name].append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
         return {k: statistics.mean(v) for k, v in by.items()}
 
     fetch, write = per_kernel("fetch"), per_kernel("write")
