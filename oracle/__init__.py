@@ -18,7 +18,8 @@ Citations (page titles and sections; see ``lnr_oracle.c`` for the formulas):
   * LayerNorm forward/backward: L10 "Technique 2" (mu(x), mu(x^2); the two backward sums),
     HW4 "Problem structure and scoring" (eps = 1e-8 inside the root; dgamma/dbeta summed
     across rows).
-  * RMSNorm: "FastTransformer: Breaking the Compiler Ceiling ...", section 5.4.
+  * RMSNorm: "FastTransformer: Breaking the Compiler Ceiling ...", section 5.4 (forward,
+    backward recomputing rstd from x, and backward from a given rstd).
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against closed forms,
 invariants, finite differences and independent fp64 library routines.
@@ -70,6 +71,7 @@ def _load():
     lib.lnr_oracle_layernorm_bw_dgamma_dbeta.argtypes = [d, d, i64, i64, ctypes.c_double, d, d, d, d]
     lib.lnr_oracle_rmsnorm_fw.argtypes = [d, d, i64, i64, ctypes.c_double, d, d]
     lib.lnr_oracle_rmsnorm_bw.argtypes = [d, d, d, i64, i64, ctypes.c_double, d, d]
+    lib.lnr_oracle_rmsnorm_bw_given_rstd.argtypes = [d, d, d, d, i64, i64, d, d]
     lib.lnr_oracle_layernorm_bw_given_stats.argtypes = [d, d, d, d, d, i64, i64, d, d, d]
     lib.lnr_oracle_layernorm_bw_given_stats.restype = None
     lib.lnr_oracle_threads.argtypes = []
@@ -79,7 +81,7 @@ def _load():
     for f in (lib.lnr_oracle_softmax_fw, lib.lnr_oracle_softmax_fw_rows, lib.lnr_oracle_softmax_bw,
               lib.lnr_oracle_layernorm_fw, lib.lnr_oracle_layernorm_bw_dx,
               lib.lnr_oracle_layernorm_bw_dgamma_dbeta, lib.lnr_oracle_rmsnorm_fw,
-              lib.lnr_oracle_rmsnorm_bw):
+              lib.lnr_oracle_rmsnorm_bw, lib.lnr_oracle_rmsnorm_bw_given_rstd):
         f.restype = None
     _lib = lib
     return lib
@@ -214,6 +216,20 @@ def rmsnorm_fw(x, gamma, eps: float = 1e-6):
     r = np.empty(N, np.float64)
     _load().lnr_oracle_rmsnorm_fw(_p(x), _p(g), N, C, float(eps), _p(y), _p(r))
     return y, r
+
+
+def rmsnorm_bw_given_rstd(x, dy, gamma, rstd):
+    """RMSNorm backward from a saved rstd per row (e.g. the fp32 values a forward kernel
+    stored). Returns (dx, dgamma) as float64."""
+    x = _f64(x)
+    dy = _f64(dy)
+    N, C = x.shape
+    g = _f64(gamma).reshape(C)
+    r = _f64(rstd).reshape(N)
+    dx = np.empty_like(x)
+    dg = np.empty(C, np.float64)
+    _load().lnr_oracle_rmsnorm_bw_given_rstd(_p(x), _p(dy), _p(g), _p(r), N, C, _p(dx), _p(dg))
+    return dx, dg
 
 
 def rmsnorm_bw(x, dy, gamma, eps: float = 1e-6):

@@ -30,6 +30,7 @@
  * of softmax (diag(y) - y y^T) applied to dy, and it is pinned by finite differences.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 
 #define ORACLE_API __attribute__((visibility("default")))
@@ -313,30 +314,71 @@ ORACLE_API void lnr_oracle_rmsnorm_bw(const double *x, const double *dy, const d
                                       int64_t N, int64_t C, double eps, double *dx,
                                       double *dgamma)
 {
+    double *rms = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    if (rms == NULL)
+        abort();
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N; ++i) {
         const double *xr = x + i * C, *dyr = dy + i * C;
         double q = 0.0;
         for (int64_t j = 0; j < C; ++j)
             q += xr[j] * xr[j];
-        const double rms = sqrt(q / (double)C + eps);
+        rms[i] = sqrt(q / (double)C + eps);
         double sum_gx = 0.0;
         for (int64_t j = 0; j < C; ++j)
-            sum_gx += gamma[j] * dyr[j] * (xr[j] / rms);
+            sum_gx += gamma[j] * dyr[j] * (xr[j] / rms[i]);
         const double b = sum_gx / (double)C;
         for (int64_t j = 0; j < C; ++j)
-            dx[i * C + j] = (gamma[j] * dyr[j] - (xr[j] / rms) * b) / rms;
+            dx[i * C + j] = (gamma[j] * dyr[j] - (xr[j] / rms[i]) * b) / rms[i];
     }
-    for (int64_t j = 0; j < C; ++j)
-        dgamma[j] = 0.0;
+    /* dgamma_j = sum over rows in row order, columns spread over threads. */
+    const int64_t blk = 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t jb = 0; jb < C; jb += blk) {
+        const int64_t je = (jb + blk < C) ? jb + blk : C;
+        for (int64_t j = jb; j < je; ++j)
+            dgamma[j] = 0.0;
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = jb; j < je; ++j)
+                dgamma[j] += dy[i * C + j] * (x[i * C + j] / rms[i]);
+    }
+    free(rms);
+}
+
+/* ---------------------------------------------------------------------------------------
+ * RMSNorm backward from a given rstd. [FT section 5.4]
+ * The chain rule through y_ij = gamma_j * x_ij * r_i with r_i = (mean_k x_ik^2 + eps)^(-1/2),
+ * whose derivative is dr_i/dx_ik = -r_i^3 x_ik / C, evaluated with r_i taken from rstd[i]
+ * (the value a forward pass saved) instead of recomputed from x:
+ *   xhat_ij = x_ij * rstd_i,  g_ij = gamma_j * dy_ij
+ *   dx_ij   = rstd_i * ( g_ij - xhat_ij * (1/C) sum_k g_ik xhat_ik )
+ *   dgamma_j = sum_i dy_ij * xhat_ij
+ * With the exact rstd it equals lnr_oracle_rmsnorm_bw.
+ * ------------------------------------------------------------------------------------- */
+ORACLE_API void lnr_oracle_rmsnorm_bw_given_rstd(const double *x, const double *dy,
+                                                 const double *gamma, const double *rstd,
+                                                 int64_t N, int64_t C, double *dx,
+                                                 double *dgamma)
+{
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N; ++i) {
-        const double *xr = x + i * C;
-        double q = 0.0;
+        const double *xr = x + i * C, *dyr = dy + i * C;
+        double sum_gx = 0.0;
         for (int64_t j = 0; j < C; ++j)
-            q += xr[j] * xr[j];
-        const double rms = sqrt(q / (double)C + eps);
+            sum_gx += gamma[j] * dyr[j] * (xr[j] * rstd[i]);
+        const double b = sum_gx / (double)C;
         for (int64_t j = 0; j < C; ++j)
-            dgamma[j] += dy[i * C + j] * (xr[j] / rms);
+            dx[i * C + j] = rstd[i] * (gamma[j] * dyr[j] - (xr[j] * rstd[i]) * b);
+    }
+    const int64_t blk = 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t jb = 0; jb < C; jb += blk) {
+        const int64_t je = (jb + blk < C) ? jb + blk : C;
+        for (int64_t j = jb; j < je; ++j)
+            dgamma[j] = 0.0;
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = jb; j < je; ++j)
+                dgamma[j] += dy[i * C + j] * (x[i * C + j] * rstd[i]);
     }
 }
 

@@ -221,6 +221,44 @@ def test_rmsnorm_backward_matches_autograd_and_finite_differences():
     assert abs(fd - dx[i, j]) <= 1e-7
 
 
+def test_rmsnorm_backward_given_rstd_pins():
+    """Backward from a saved rstd (what the GPU kernel receives):
+    (1) with the exact fp64 rstd it equals the recomputing backward (itself pinned to autograd
+        and finite differences above);
+    (2) with an fp32-rounded rstd (not the exact statistic) it equals aten's LayerNorm
+        backward taking mean = 0 and that rstd as inputs, plus rstd_i * mean_j(gamma_j dy_ij):
+        RMSNorm's gradient is LayerNorm's with the mean removed and without the sum_k g_ik
+        term that the mean's derivative contributes;
+    (3) C = 1 closed form: xhat = x*r and dx = r*g*(1 - xhat^2)."""
+    N, C = 41, 37
+    x, g, _, dy = _case(N, C, 15, offset_std=1.0)
+    _, rr = oracle.rmsnorm_fw(x, g, RMS_EPS)
+    dx_e, dg_e = oracle.rmsnorm_bw_given_rstd(x, dy, g, rr)
+    dx_r, dg_r = oracle.rmsnorm_bw(x, dy, g, RMS_EPS)
+    np.testing.assert_allclose(dx_e, dx_r, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dg_e, dg_r, rtol=1e-12, atol=1e-13)
+
+    r32 = rr.astype(np.float32).astype(np.float64)
+    dx_t, dg_t, _ = torch.ops.aten.native_layer_norm_backward(
+        torch.from_numpy(dy), torch.from_numpy(x), [C], torch.zeros(N, 1, dtype=torch.float64),
+        torch.from_numpy(r32).view(N, 1), torch.from_numpy(g), torch.zeros(C, dtype=torch.float64),
+        [True, True, False])
+    dx, dg = oracle.rmsnorm_bw_given_rstd(x, dy, g, r32)
+    gdy = g.reshape(1, C) * dy
+    np.testing.assert_allclose(dx, dx_t.numpy() + r32.reshape(N, 1) * gdy.mean(axis=1, keepdims=True),
+                               rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dg, dg_t.numpy(), rtol=1e-11, atol=1e-11)
+
+    x1 = np.array([[0.3], [-2.0], [1e-4]])
+    dy1 = np.array([[1.5], [-0.25], [2.0]])
+    g1 = np.array([0.8])
+    r1 = np.array([1.7, 0.4, 3.0])
+    dx1, dg1 = oracle.rmsnorm_bw_given_rstd(x1, dy1, g1, r1)
+    xh = x1[:, 0] * r1
+    np.testing.assert_allclose(dx1[:, 0], r1 * g1[0] * dy1[:, 0] * (1 - xh * xh), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(dg1, [np.sum(dy1[:, 0] * xh)], rtol=1e-14)
+
+
 def test_results_do_not_depend_on_the_thread_count():
     """The CPU baseline times the oracle at several thread counts; every output element is
     computed by one thread in a fixed order, so the values must be bitwise identical."""
