@@ -227,6 +227,14 @@ def table_cases():
         tag = "fp16" if dt == torch.float16 else "fp32"
         for C in (1024, 4096):
             cases.append((f"w5 layernorm [32768,{C}] {tag}", "layernorm", (32768, C), dt, {}))
+    # RMSNorm (the FastTransformer page's Pre-RMSNorm): its own model shape, then wider rows.
+    cases.append(("rmsnorm [8192,256] fp16", "rmsnorm", (8192, 256), torch.float16, {}))
+    for C in (1024, 4096, 8192):
+        cases.append((f"rmsnorm [16384,{C}] fp16", "rmsnorm", (16384, C), torch.float16, {}))
+    for dt in (torch.float16, torch.float32):
+        tag = "fp16" if dt == torch.float16 else "fp32"
+        for C in (1024, 4096):
+            cases.append((f"rmsnorm [32768,{C}] {tag}", "rmsnorm", (32768, C), dt, {}))
     return cases
 
 
@@ -320,7 +328,7 @@ def run_table(match: str = ""):
             bf = W.softmax_fw_bytes(B, H, T, T, s, has_mask=extra["mask"])
             bb = W.softmax_bw_bytes(B, H, T, T, s)
             rows, tensor = B * H * T, per
-        else:
+        elif kind == "layernorm":
             N, C = shape
             per = N * C * s
             n = max(2, math.ceil(MIN_FOOTPRINT / (4 * per)))
@@ -342,6 +350,27 @@ def run_table(match: str = ""):
                 keep += [x, dy, gm, bt, y, dx, mean, rstd, dg, db, ws]
             bf = W.layernorm_fw_bytes(N, C, s)
             bb = W.layernorm_bw_bytes(N, C, s)
+            rows, tensor = N, per
+        elif kind == "rmsnorm":
+            N, C = shape
+            per = N * C * s
+            n = max(2, math.ceil(MIN_FOOTPRINT / (4 * per)))
+            fw, bw = [], []
+            keep = []
+            wsb = lnr.rmsnorm_bw_workspace_bytes(N, C, lnr.LNR_F16 if dt == torch.float16 else lnr.LNR_F32)
+            for _ in range(n):
+                x = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                dy = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                gm = torch.rand(C, device=dev, dtype=dt, generator=g) + 0.5
+                y, dx = torch.empty_like(x), torch.empty_like(x)
+                rstd = torch.empty(N, device=dev, dtype=torch.float32)
+                dg = torch.empty(C, device=dev, dtype=dt)
+                ws = torch.empty(max(wsb, 1), device=dev, dtype=torch.uint8)
+                fw.append(lnr.bind_rmsnorm_fw(x, gm, W.RMS_EPS, y, rstd))
+                bw.append(lnr.bind_rmsnorm_bw(dy, x, gm, rstd, dx, dg, ws))
+                keep += [x, dy, gm, y, dx, rstd, dg, ws]
+            bf = W.rmsnorm_fw_bytes(N, C, s)
+            bb = W.rmsnorm_bw_bytes(N, C, s)
             rows, tensor = N, per
         torch.cuda.synchronize()
         f_b2b, f_k = timed(fw)

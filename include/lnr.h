@@ -157,6 +157,54 @@ LNR_API int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, co
                  void *stream);
 
 /*
+ * rmsnorm_fw -- RMSNorm forward: per row, one reduction of the sum of squares, then
+ * y = gamma * x * rstd with rstd = 1 / sqrt(mean_j(x_j^2) + eps). No mean, no bias.
+ * ["FastTransformer: Breaking the Compiler Ceiling via Architectural Co-Design", section 5.4
+ *  "Vectorized Pre-RMSNorm": LayerNorm with the mean-centering removed; the page's module
+ *  uses eps = 1e-6 and a learned weight only.]
+ *
+ *   y     [N, C] dtype, written. May equal x (in place); no other overlap.
+ *   rstd  [N] float32, written (the saved statistic for rmsnorm_bw), or NULL.
+ *   x     [N, C] dtype, read.   gamma  [C] dtype, read.
+ *   eps   added to mean(x^2) inside the square root; must be >= 0.
+ *   Limits: 1 <= C <= LNR_LAYERNORM_MAX_C; N >= 0. Same kernels, buckets and fallbacks as
+ *   layernorm_fw.
+ */
+LNR_API int rmsnorm_fw(void *y, float *rstd, const void *x, const void *gamma, int64_t N,
+                       int64_t C, float eps, lnr_dtype dtype, void *stream);
+
+/*
+ * rmsnorm_bw_workspace_bytes -- device workspace that rmsnorm_bw needs for (N, C, dtype):
+ * per-block column partial sums of dgamma. Returns 0 for N = 0 and for an invalid
+ * shape/dtype.
+ */
+LNR_API size_t rmsnorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype);
+
+/*
+ * rmsnorm_bw -- RMSNorm backward: input gradient and gamma gradient.
+ * [Same page and section as rmsnorm_fw; the gradient is the chain rule through
+ *  y = gamma * x * rstd(x).]
+ *
+ *   With xhat_ij = x_ij * rstd_i and g_ij = gamma_j * dy_ij:
+ *     dx_ij    = rstd_i * ( g_ij - xhat_ij * (1/C) sum_k g_ik xhat_ik )
+ *     dgamma_j = sum_i dy_ij * xhat_ij
+ *   One row reduction (the LayerNorm backward's second sum; the first, sum_k g_ik, is absent
+ *   because RMSNorm subtracts no mean). Column partials and their fixed-order sum as in
+ *   layernorm_bw: bitwise reproducible.
+ *
+ *   dx      [N, C] dtype, written. Must not overlap x, dy, gamma or rstd (LNR_ERR_ALIAS).
+ *   dgamma  [C] dtype, written.
+ *   dy, x   [N, C] dtype, read.  gamma [C] dtype, read.
+ *   rstd    [N] float32, read: the values rmsnorm_fw wrote for this x.
+ *   workspace  device buffer of at least rmsnorm_bw_workspace_bytes(N, C, dtype) bytes,
+ *              8-byte aligned, owned by the caller; its contents on entry do not matter.
+ *   Limits: 1 <= C <= LNR_LAYERNORM_MAX_C; N >= 0.
+ */
+LNR_API int rmsnorm_bw(void *dx, void *dgamma, const void *dy, const void *x, const void *gamma,
+                       const float *rstd, int64_t N, int64_t C, lnr_dtype dtype, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
  * lnr_copy -- measurement helper, not part of the method: copies `bytes` bytes from src to
  * dst with the same 128-bit load/store pattern as the row kernels, giving the achievable
  * streaming ceiling that the kernels' bandwidth is compared with. dst and src must not

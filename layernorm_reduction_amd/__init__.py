@@ -13,6 +13,9 @@ Functions mirror the C entry points:
     layernorm_bw(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None,
                  workspace=None) -> (dx, dgamma, dbeta)
     layernorm_bw_workspace_bytes(N, C, dtype) -> int
+    rmsnorm_fw(x, gamma, eps=1e-6, y=None, rstd=None) -> (y, rstd)
+    rmsnorm_bw(dy, x, gamma, rstd, dx=None, dgamma=None, workspace=None) -> (dx, dgamma)
+    rmsnorm_bw_workspace_bytes(N, C, dtype) -> int
 """
 from __future__ import annotations
 
@@ -21,7 +24,8 @@ import os
 
 __all__ = [
     "LnrError", "load", "library_path", "attn_softmax_fw", "attn_softmax_bw", "layernorm_fw",
-    "layernorm_bw", "layernorm_bw_workspace_bytes", "copy_bytes", "xor_bytes", "softmax_plan",
+    "layernorm_bw", "layernorm_bw_workspace_bytes", "rmsnorm_fw", "rmsnorm_bw",
+    "rmsnorm_bw_workspace_bytes", "copy_bytes", "xor_bytes", "softmax_plan",
     "layernorm_plan", "LNR_F32", "LNR_F16", "SOFTMAX_MAX_TK", "LAYERNORM_MAX_C",
 ]
 
@@ -69,6 +73,10 @@ def load():
     lib.layernorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
     lib.layernorm_bw_workspace_bytes.restype = sz
     lib.layernorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
+    lib.rmsnorm_fw.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, ci, vp]
+    lib.rmsnorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
+    lib.rmsnorm_bw_workspace_bytes.restype = sz
+    lib.rmsnorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
     lib.lnr_copy.argtypes = [vp, vp, sz, vp]
     lib.lnr_xor2.argtypes = [vp, vp, vp, sz, vp]
     lib.lnr_time_next_launch.argtypes = [vp, vp]
@@ -79,7 +87,8 @@ def load():
     ip = ctypes.POINTER(ctypes.c_int)
     lib.lnr_softmax_plan.argtypes = [i64, ci, ci, ip, ip, ip]
     lib.lnr_layernorm_plan.argtypes = [i64, i64, ci, ci, ip, ip, ip, ip, ctypes.POINTER(i64)]
-    for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw", "lnr_copy",
+    for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw", "rmsnorm_fw",
+              "rmsnorm_bw", "lnr_copy",
               "lnr_xor2", "lnr_softmax_plan", "lnr_layernorm_plan"):
         getattr(lib, f).restype = ci
     _lib = lib
@@ -272,6 +281,77 @@ def layernorm_bw(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None, wor
     return dx, dgamma, dbeta
 
 
+def rmsnorm_fw(x, gamma, eps: float = 1e-6, y=None, rstd=None):
+    """RMSNorm over the last axis of x [N, C]; returns (y, rstd) (fp32 rstd)."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [N, C]")
+    N, C = x.shape
+    _dev(gamma, "gamma", like=x)
+    if gamma.numel() != C:
+        raise ValueError("gamma must have C elements")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _dev(y, "y", like=x)
+        if y.shape != x.shape:
+            raise ValueError("y must have the shape of x")
+    if rstd is None:
+        rstd = torch.empty(N, dtype=torch.float32, device=x.device)
+    _f32(rstd, "rstd", x)
+    if rstd.numel() != N:
+        raise ValueError("rstd must have N elements")
+    st = load().rmsnorm_fw(_ptr(y), _ptr(rstd), _ptr(x), _ptr(gamma), N, C, float(eps),
+                           _dtype_code(x), _stream(x))
+    _check(st, "rmsnorm_fw")
+    return y, rstd
+
+
+def rmsnorm_bw_workspace_bytes(N: int, C: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (LNR_F16 if str(dtype).endswith("float16") else LNR_F32)
+    return int(load().rmsnorm_bw_workspace_bytes(int(N), int(C), code))
+
+
+def rmsnorm_bw(dy, x, gamma, rstd, dx=None, dgamma=None, workspace=None):
+    """RMSNorm backward; returns (dx, dgamma).
+
+    workspace: a uint8 GPU tensor of at least rmsnorm_bw_workspace_bytes(N, C, dtype) bytes;
+    allocated here when not given.
+    """
+    torch = _torch()
+    _dev(x, "x")
+    _dev(dy, "dy", like=x)
+    if x.dim() != 2 or dy.shape != x.shape:
+        raise ValueError("x and dy must both be [N, C]")
+    N, C = x.shape
+    _dev(gamma, "gamma", like=x)
+    if gamma.numel() != C:
+        raise ValueError("gamma must have C elements")
+    _f32(rstd, "rstd", x)
+    if rstd.numel() != N:
+        raise ValueError("rstd must have N elements")
+    if dx is None:
+        dx = torch.empty_like(x)
+    else:
+        _dev(dx, "dx", like=x)
+    if dgamma is None:
+        dgamma = torch.empty(C, dtype=x.dtype, device=x.device)
+    else:
+        _dev(dgamma, "dgamma", like=x)
+    code = _dtype_code(x)
+    need = int(load().rmsnorm_bw_workspace_bytes(N, C, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    else:
+        _dev(workspace, "workspace")
+    st = load().rmsnorm_bw(_ptr(dx), _ptr(dgamma), _ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), N, C,
+                           code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(x))
+    _check(st, "rmsnorm_bw")
+    return dx, dgamma
+
+
 def copy_bytes(dst, src):
     """Streaming 16-byte-vector copy of src into dst (measurement helper)."""
     _dev(src, "src")
@@ -365,3 +445,20 @@ def bind_layernorm_bw(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace):
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(x))
     return BoundCall("layernorm_bw", load().layernorm_bw, args,
                      (dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace))
+
+
+def bind_rmsnorm_fw(x, gamma, eps, y, rstd):
+    rmsnorm_fw(x, gamma, eps, y, rstd)
+    N, C = x.shape
+    args = (y.data_ptr(), rstd.data_ptr(), x.data_ptr(), gamma.data_ptr(), N, C, float(eps),
+            _dtype_code(x), _stream(x))
+    return BoundCall("rmsnorm_fw", load().rmsnorm_fw, args, (x, gamma, y, rstd))
+
+
+def bind_rmsnorm_bw(dy, x, gamma, rstd, dx, dgamma, workspace):
+    rmsnorm_bw(dy, x, gamma, rstd, dx, dgamma, workspace)
+    N, C = x.shape
+    args = (dx.data_ptr(), dgamma.data_ptr(), dy.data_ptr(), x.data_ptr(), gamma.data_ptr(),
+            rstd.data_ptr(), N, C, _dtype_code(x), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(x))
+    return BoundCall("rmsnorm_bw", load().rmsnorm_bw, args, (dy, x, gamma, rstd, dx, dgamma, workspace))

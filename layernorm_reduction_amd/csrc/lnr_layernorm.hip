@@ -13,14 +13,18 @@
 //     crossing waves through LDS with one barrier pair). 128-bit loads and stores.
 //   * Forward: one read of x, one write of y, per-row mean and rstd in fp32. The variance
 //     from the one-pass sums is clamped at 0 before eps is added.
-//   * Backward, fused: each workgroup walks a contiguous chunk of rows. Because a lane owns
-//     the same columns in every row, it accumulates dgamma/dbeta column partials in
+//   * Backward, fused: each workgroup walks every P-th row (P workgroups). Because a lane
+//     owns the same columns in every row, it accumulates dgamma/dbeta column partials in
 //     registers while it computes dx, so x and dy are read from HBM exactly once. At the
 //     end the workgroup's row groups are combined through an LDS column tile, in group
 //     order, and one partial row per workgroup goes to the workspace. A second small kernel
 //     sums the partials in a fixed order. No atomics: results are bitwise reproducible.
 //     Partials are fp32 for fp16 storage and fp64 for fp32 storage, so the long column sums
 //     over tens of thousands of rows add no rounding beyond the per-element products.
+//   * RMSNorm ("FastTransformer: Breaking the Compiler Ceiling via Architectural
+//     Co-Design", section 5.4: the LayerNorm without the mean, y = x * rsqrt(mean(x^2) +
+//     eps) * weight, no bias) is the same kernels with the RMS flag: no shift or mean, one
+//     reduction (sum of x^2 forward, sum of gamma*dy*xhat backward), no beta and no dbeta.
 #include <math.h>
 
 #include "lnr_common.h"
@@ -45,6 +49,12 @@ __device__ __forceinline__ float ln_stats(float s1, float s2, int C, float eps, 
     return 1.0f / sqrtf(var + eps);
 }
 
+// RMSNorm statistic: rstd = 1 / sqrt(mean(x^2) + eps), from the one sum of squares.
+__device__ __forceinline__ float rms_stats(float s2, int C, float eps) {
+#pragma clang fp contract(off)
+    return 1.0f / sqrtf(s2 / static_cast<float>(C) + eps);
+}
+
 // ------------------------------------------------------------------------------------------
 // Forward, vector path. Workgroup b normalises rows [b*R, (b+1)*R) with R = rows_per_block;
 // group g of the workgroup takes rows b*R + g, b*R + g + NG, ... gamma and beta are loaded
@@ -53,7 +63,7 @@ __device__ __forceinline__ float ln_stats(float s1, float s2, int C, float eps, 
 // the fetch is issued unconditionally (an idle lane reads a vector that always exists) so
 // that no branch makes the compiler drain the loads early.
 // ------------------------------------------------------------------------------------------
-template <typename T, int G, int IT, int WG>
+template <typename T, int G, int IT, int WG, bool RMS>
 __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__ mean,
                                                        float *__restrict__ rstd, const T *x,
                                                        const T *__restrict__ gamma,
@@ -71,13 +81,13 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
     const int64_t r1 = (r0 + rows_per_block < N) ? r0 + rows_per_block : N;
     const RV zero = {};
 
-    float gm[IT][V], bt[IT][V];
+    float gm[IT][V], bt[IT][RMS ? 1 : V];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
         const int cc = c < nvec ? c : 0;
         widen<T>(load_keep_raw<T>(gamma + cc * V), gm[k]);
-        widen<T>(load_keep_raw<T>(beta + cc * V), bt[k]);
+        if constexpr (!RMS) widen<T>(load_keep_raw<T>(beta + cc * V), bt[k]);
     }
 
     const int64_t iters = (rows_per_block + NG - 1) / NG;
@@ -92,8 +102,12 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
             const RV l = load_stream_raw<T>(x + rbase + (ok ? static_cast<int64_t>(c) * V : 0));
             xn[k] = ok ? l : zero;
         }
-        const float kl = to_f32(x[rbase]);  // the shift: one broadcast load per group
-        Kn = live ? kl : 0.f;
+        if constexpr (!RMS) {
+            const float kl = to_f32(x[rbase]);  // the shift: one broadcast load per group
+            Kn = live ? kl : 0.f;
+        } else {
+            Kn = 0.f;
+        }
     };
     fetch(r0 + grp, r0 + grp < r1);
     for (int64_t it = 0; it < iters; ++it) {
@@ -114,13 +128,18 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 d[k][e] = ok ? d[k][e] - K : 0.f;
-                s1 += d[k][e];
+                if constexpr (!RMS) s1 += d[k][e];
                 s2 += d[k][e] * d[k][e];
             }
         }
-        row_allreduce_sum2<G>(s1, s2, red);
-        float m1;
-        const float rs = ln_stats(s1, s2, C, eps, m1);
+        float m1 = 0.f, rs;
+        if constexpr (RMS) {
+            s2 = row_allreduce<G>(s2, OpSum(), red);
+            rs = rms_stats(s2, C, eps);
+        } else {
+            row_allreduce_sum2<G>(s1, s2, red);
+            rs = ln_stats(s1, s2, C, eps, m1);
+        }
         const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
@@ -128,12 +147,17 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
             if (live && c < nvec) {
                 float o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e) o[e] = (d[k][e] - m1) * rs * gm[k][e] + bt[k][e];
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (RMS)
+                        o[e] = d[k][e] * rs * gm[k][e];
+                    else
+                        o[e] = (d[k][e] - m1) * rs * gm[k][e] + bt[k][e];
+                }
                 store_stream<T>(y + base + static_cast<int64_t>(c) * V, o);
             }
         }
-        if (live && lane == 0 && mean != nullptr) {
-            mean[row] = K + m1;
+        if (live && lane == 0 && rstd != nullptr) {
+            if constexpr (!RMS) mean[row] = K + m1;
             rstd[row] = rs;
         }
     }
@@ -141,9 +165,9 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
 
 // ------------------------------------------------------------------------------------------
 // Backward, vector path: dx plus per-workgroup dgamma/dbeta column partials.
-// part layout: [P][2][C] of Accum<T>; slot 0 = dgamma, slot 1 = dbeta.
+// part layout: [P][2][C] of Accum<T>; slot 0 = dgamma, slot 1 = dbeta (unused for RMSNorm).
 // ------------------------------------------------------------------------------------------
-template <typename T, int G, int IT, int WG, int DEPTH>
+template <typename T, int G, int IT, int WG, int DEPTH, bool RMS>
 __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>::type *part,
                                                        const T *dy, const T *x,
                                                        const T *__restrict__ gamma,
@@ -174,14 +198,17 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     const RV zero = {};
 
     RV gmr[IT];  // gamma, kept as stored (16 bytes per vector) to save registers
-    A adg[IT][V], adb[IT][V];
+    A adg[IT][V], adb[IT][RMS ? 1 : V];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
         const RV gl = load_keep_raw<T>(gamma + (c < nvec ? c : 0) * V);
         gmr[k] = c < nvec ? gl : zero;
 #pragma unroll
-        for (int e = 0; e < V; ++e) adg[k][e] = adb[k][e] = A(0);
+        for (int e = 0; e < V; ++e) {
+            adg[k][e] = A(0);
+            if constexpr (!RMS) adb[k][e] = A(0);
+        }
     }
 
     // A row buffer holds one row's x and dy vectors (as stored) plus its mean and rstd.
@@ -213,8 +240,13 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
             b.dv[k] = ok ? dl : zero;
         }
         const int64_t srow = live ? row : first_row;
-        const float ml = mean[srow], rl = rstd[srow];
-        b.mu = live ? ml : 0.f;
+        const float rl = rstd[srow];
+        if constexpr (!RMS) {
+            const float ml = mean[srow];
+            b.mu = live ? ml : 0.f;
+        } else {
+            b.mu = 0.f;
+        }
         b.rs = live ? rl : 0.f;
     };
     auto process = [&](const RowBuf &b, int64_t it) {
@@ -235,16 +267,22 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
             widen<T>(gmr[k], gmf);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                xh[k][e] = (xf[e] - mu) * rs;
+                if constexpr (RMS)
+                    xh[k][e] = xf[e] * rs;
+                else
+                    xh[k][e] = (xf[e] - mu) * rs;
                 gv[k][e] = gmf[e] * df[e];
-                sg += gv[k][e];
+                if constexpr (!RMS) sg += gv[k][e];
                 sgx = __builtin_fmaf(gv[k][e], xh[k][e], sgx);
                 adg[k][e] += static_cast<A>(df[e] * xh[k][e]);
-                adb[k][e] += static_cast<A>(df[e]);
+                if constexpr (!RMS) adb[k][e] += static_cast<A>(df[e]);
             }
         }
-        row_allreduce_sum2<G>(sg, sgx, red);
-        const float a = sg * invC, bb = sgx * invC;
+        if constexpr (RMS)
+            sgx = row_allreduce<G>(sgx, OpSum(), red);
+        else
+            row_allreduce_sum2<G>(sg, sgx, red);
+        const float a = sg * invC, bb = sgx * invC;  // a = 0 for RMSNorm
         const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
@@ -252,7 +290,12 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
             if (live && c < nvec) {
                 float o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e) o[e] = rs * __builtin_fmaf(-xh[k][e], bb, gv[k][e] - a);
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (RMS)
+                        o[e] = rs * __builtin_fmaf(-xh[k][e], bb, gv[k][e]);
+                    else
+                        o[e] = rs * __builtin_fmaf(-xh[k][e], bb, gv[k][e] - a);
+                }
                 store_stream<T>(dx + base + static_cast<int64_t>(c) * V, o);
             }
         }
@@ -290,7 +333,7 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     pg[c * V + e] = adg[k][e];
-                    pb[c * V + e] = adb[k][e];
+                    if constexpr (!RMS) pb[c * V + e] = adb[k][e];
                 }
             }
         }
@@ -300,9 +343,14 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
 #pragma unroll
-            for (int which = 0; which < 2; ++which) {
+            for (int which = 0; which < (RMS ? 1 : 2); ++which) {
 #pragma unroll
-                for (int e = 0; e < V; ++e) tile[grp][lane * V + e] = which == 0 ? adg[k][e] : adb[k][e];
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (RMS)
+                        tile[grp][lane * V + e] = adg[k][e];
+                    else
+                        tile[grp][lane * V + e] = which == 0 ? adg[k][e] : adb[k][e];
+                }
                 __syncthreads();
                 for (int cc = threadIdx.x; cc < G * V; cc += WG) {
                     A s = tile[0][cc];
@@ -370,33 +418,42 @@ __global__ __launch_bounds__(TILE *SLICES) void layernorm_bw_colsum(
 // ------------------------------------------------------------------------------------------
 constexpr int kLnGenericWG = 256;
 
-template <typename T>
+template <typename T, bool RMS>
 __global__ __launch_bounds__(kLnGenericWG) void layernorm_fw_generic(
     T *y, float *__restrict__ mean, float *__restrict__ rstd, const T *x,
     const T *__restrict__ gamma, const T *__restrict__ beta, int64_t N, int32_t C, float eps) {
     __shared__ float red[2 * (kLnGenericWG / 64)];
     const int64_t row = blockIdx.x;
     const T *xr = x + row * static_cast<int64_t>(C);
-    const float K = to_f32(xr[0]);
+    const float K = RMS ? 0.f : to_f32(xr[0]);
     float s1 = 0.f, s2 = 0.f;
     for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
         const float d = to_f32(xr[j]) - K;
         s1 += d;
         s2 += d * d;
     }
-    row_allreduce_sum2<kLnGenericWG>(s1, s2, red);
-    float m1;
-    const float rs = ln_stats(s1, s2, C, eps, m1);
+    float m1 = 0.f, rs;
+    if constexpr (RMS) {
+        s2 = row_allreduce<kLnGenericWG>(s2, OpSum(), red);
+        rs = rms_stats(s2, C, eps);
+    } else {
+        row_allreduce_sum2<kLnGenericWG>(s1, s2, red);
+        rs = ln_stats(s1, s2, C, eps, m1);
+    }
     T *yr = y + row * static_cast<int64_t>(C);
-    for (int j = threadIdx.x; j < C; j += kLnGenericWG)
-        yr[j] = from_f32<T>(((to_f32(xr[j]) - K) - m1) * rs * to_f32(gamma[j]) + to_f32(beta[j]));
-    if (threadIdx.x == 0 && mean != nullptr) {
-        mean[row] = K + m1;
+    for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
+        if constexpr (RMS)
+            yr[j] = from_f32<T>(to_f32(xr[j]) * rs * to_f32(gamma[j]));
+        else
+            yr[j] = from_f32<T>(((to_f32(xr[j]) - K) - m1) * rs * to_f32(gamma[j]) + to_f32(beta[j]));
+    }
+    if (threadIdx.x == 0 && rstd != nullptr) {
+        if constexpr (!RMS) mean[row] = K + m1;
         rstd[row] = rs;
     }
 }
 
-template <typename T>
+template <typename T, bool RMS>
 __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_dx_generic(
     T *dx, const T *dy, const T *x, const T *__restrict__ gamma, const float *__restrict__ mean,
     const float *__restrict__ rstd, int64_t N, int32_t C) {
@@ -404,25 +461,30 @@ __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_dx_generic(
     __shared__ float red[2 * (kLnGenericWG / 64)];
     const int64_t row = blockIdx.x;
     const int64_t base = row * static_cast<int64_t>(C);
-    const float mu = mean[row], rs = rstd[row];
+    const float mu = RMS ? 0.f : mean[row], rs = rstd[row];
+    auto xhat = [&](int j) {
+        const float xv = to_f32(x[base + j]);
+        return RMS ? xv * rs : (xv - mu) * rs;
+    };
     float sg = 0.f, sgx = 0.f;
     for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
-        const float xh = (to_f32(x[base + j]) - mu) * rs;
         const float g = to_f32(gamma[j]) * to_f32(dy[base + j]);
         sg += g;
-        sgx = __builtin_fmaf(g, xh, sgx);
+        sgx = __builtin_fmaf(g, xhat(j), sgx);
     }
-    row_allreduce_sum2<kLnGenericWG>(sg, sgx, red);
+    if constexpr (RMS)
+        sgx = row_allreduce<kLnGenericWG>(sgx, OpSum(), red);
+    else
+        row_allreduce_sum2<kLnGenericWG>(sg, sgx, red);
     const float invC = 1.0f / static_cast<float>(C);
-    const float a = sg * invC, b = sgx * invC;
+    const float a = RMS ? 0.f : sg * invC, b = sgx * invC;
     for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
-        const float xh = (to_f32(x[base + j]) - mu) * rs;
         const float g = to_f32(gamma[j]) * to_f32(dy[base + j]);
-        dx[base + j] = from_f32<T>(rs * __builtin_fmaf(-xh, b, g - a));
+        dx[base + j] = from_f32<T>(rs * __builtin_fmaf(-xhat(j), b, RMS ? g : g - a));
     }
 }
 
-template <typename T>
+template <typename T, bool RMS>
 __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_colpart_generic(
     typename Accum<T>::type *part, const T *dy, const T *x, const float *__restrict__ mean,
     const float *__restrict__ rstd, int64_t N, int32_t C, int64_t rows_per_block) {
@@ -434,12 +496,13 @@ __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_colpart_generic(
     A sg = A(0), sb = A(0);
     for (int64_t r = r0; r < r1; ++r) {
         const float d = to_f32(dy[r * C + col]);
-        const float xh = (to_f32(x[r * C + col]) - mean[r]) * rstd[r];
+        const float xv = to_f32(x[r * C + col]);
+        const float xh = RMS ? xv * rstd[r] : (xv - mean[r]) * rstd[r];
         sg += static_cast<A>(d * xh);
         sb += static_cast<A>(d);
     }
     part[(static_cast<int64_t>(blockIdx.y) * 2 + 0) * C + col] = sg;
-    part[(static_cast<int64_t>(blockIdx.y) * 2 + 1) * C + col] = sb;
+    if constexpr (!RMS) part[(static_cast<int64_t>(blockIdx.y) * 2 + 1) * C + col] = sb;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -520,121 +583,82 @@ static void bw_partials(int64_t N, int64_t C, lnr_dtype dtype, int64_t &p_vec, i
 
 struct LnFwArgs {
     void *y;
-    float *mean;
+    float *mean;  // NULL for RMSNorm
     float *rstd;
-    const void *x, *gamma, *beta;
+    const void *x, *gamma, *beta;  // beta NULL for RMSNorm
     int64_t N;
     int32_t C;
     float eps;
 };
 struct LnBwArgs {
     void *dx;
+    void *dgamma, *dbeta;  // dbeta NULL for RMSNorm
     void *part;
     const void *dy, *x, *gamma;
-    const float *mean, *rstd;
+    const float *mean, *rstd;  // mean NULL for RMSNorm
     int64_t N;
     int32_t C;
     int64_t rows_per_block;
     int64_t blocks;
 };
 
-template <typename T, int I>
+template <typename T, bool RMS, int I>
 static hipError_t dispatch_ln_fw(const LnFwArgs &a, hipStream_t st) {
     constexpr LnPlan p = LnFwTable<T>::plans[I];
     if (a.C <= p.bucket) {
         static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && p.R >= 1, "bad forward plan");
         constexpr int64_t RPB = static_cast<int64_t>(p.WG / p.G) * p.R;
         const int64_t blocks = (a.N + RPB - 1) / RPB;
-        return launch(layernorm_fw_vec<T, p.G, p.IT, p.WG>, dim3(static_cast<uint32_t>(blocks)),
+        return launch(layernorm_fw_vec<T, p.G, p.IT, p.WG, RMS>, dim3(static_cast<uint32_t>(blocks)),
                       dim3(p.WG), st, static_cast<T *>(a.y), a.mean, a.rstd,
                       static_cast<const T *>(a.x), static_cast<const T *>(a.gamma),
                       static_cast<const T *>(a.beta), a.N, a.C, a.eps, RPB);
     }
     if constexpr (I + 1 < static_cast<int>(sizeof(LnFwTable<T>::plans) / sizeof(LnPlan)))
-        return dispatch_ln_fw<T, I + 1>(a, st);
+        return dispatch_ln_fw<T, RMS, I + 1>(a, st);
     return hipErrorInvalidValue;
 }
 
-template <typename T, int I>
-static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
-    constexpr LnPlan p = LnBwTable<T>::plans[I];
-    if (a.C <= p.bucket) {
-        static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && (p.R == 1 || p.R == 2), "bad backward plan");
-        static_assert(2 * (p.WG / 64) >= 2, "reduction slots");
-        return launch(layernorm_bw_vec<T, p.G, p.IT, p.WG, p.R>, dim3(static_cast<uint32_t>(a.blocks)),
-                      dim3(p.WG), st, static_cast<T *>(a.dx),
-                      static_cast<typename Accum<T>::type *>(a.part), static_cast<const T *>(a.dy),
-                      static_cast<const T *>(a.x), static_cast<const T *>(a.gamma), a.mean, a.rstd,
-                      a.N, a.C, a.rows_per_block);
-    }
-    if constexpr (I + 1 < static_cast<int>(sizeof(LnBwTable<T>::plans) / sizeof(LnPlan)))
-        return dispatch_ln_bw<T, I + 1>(a, st);
-    return hipErrorInvalidValue;
-}
-
+// dgamma (and, for LayerNorm, dbeta) from the P partial rows; `slots` = 2 for LayerNorm,
+// 1 for RMSNorm (only the dgamma slot of each partial row is written).
 template <typename T>
 static hipError_t launch_colsum(void *dgamma, void *dbeta, const void *part, int64_t P, int32_t C,
-                                hipStream_t st) {
+                                int slots, hipStream_t st) {
     using A = typename Accum<T>::type;
     if (C <= 1024) {
-        const dim3 grid(static_cast<uint32_t>((C + 15) / 16), 2);
+        const dim3 grid(static_cast<uint32_t>((C + 15) / 16), static_cast<uint32_t>(slots));
         return launch(layernorm_bw_colsum<T, 16, 16, 1>, grid, dim3(16 * 16), st,
                       static_cast<T *>(dgamma), static_cast<T *>(dbeta),
                       static_cast<const A *>(part), static_cast<int32_t>(P), C);
     }
-    const dim3 grid(static_cast<uint32_t>((C + 31) / 32), 2);
+    const dim3 grid(static_cast<uint32_t>((C + 31) / 32), static_cast<uint32_t>(slots));
     return launch(layernorm_bw_colsum<T, 32, 32, 8>, grid, dim3(32 * 32), st,
                   static_cast<T *>(dgamma), static_cast<T *>(dbeta), static_cast<const A *>(part),
                   static_cast<int32_t>(P), C);
 }
 
-static size_t accum_size(lnr_dtype d) { return d == LNR_F16 ? sizeof(float) : sizeof(double); }
-
-}  // namespace lnr
-
-using namespace lnr;
-
-extern "C" int layernorm_fw(void *y, float *mean, float *rstd, const void *x, const void *gamma,
-                            const void *beta, int64_t N, int64_t C, float eps, lnr_dtype dtype,
-                            void *stream) {
-    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
-    if (N < 0 || C < 1) return LNR_ERR_SHAPE;
-    if (C > LNR_LAYERNORM_MAX_C) return LNR_ERR_UNSUPPORTED;
-    if (!(eps >= 0.f) || !isfinite(eps)) return LNR_ERR_SHAPE;
-    if ((mean == nullptr) != (rstd == nullptr)) return LNR_ERR_NULL;
-    if (N == 0) return LNR_OK;
-    if (N > INT32_MAX) return LNR_ERR_UNSUPPORTED;
-    if (y == nullptr || x == nullptr || gamma == nullptr || beta == nullptr) return LNR_ERR_NULL;
-    const size_t es = dtype_size(dtype);
-    if (!aligned_to(y, es) || !aligned_to(x, es) || !aligned_to(gamma, es) || !aligned_to(beta, es) ||
-        !aligned_to(mean, 4) || !aligned_to(rstd, 4))
-        return LNR_ERR_ALIGN;
-    const size_t nbytes = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
-    if (bad_alias(y, x, nbytes) || overlap(y, nbytes, gamma, C * es) || overlap(y, nbytes, beta, C * es) ||
-        overlap(y, nbytes, mean, N * 4) || overlap(y, nbytes, rstd, N * 4) ||
-        overlap(mean, N * 4, rstd, N * 4))
-        return LNR_ERR_ALIAS;
-
-    LnFwArgs a{y, mean, rstd, x, gamma, beta, N, static_cast<int32_t>(C), eps};
-    const bool vec = (static_cast<size_t>(C) * es) % 16 == 0 && aligned_to(y, 16) &&
-                     aligned_to(x, 16) && aligned_to(gamma, 16) && aligned_to(beta, 16);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (vec) {
-        e = dtype == LNR_F16 ? dispatch_ln_fw<f16, 0>(a, s) : dispatch_ln_fw<float, 0>(a, s);
-    } else if (dtype == LNR_F16) {
-        e = launch(layernorm_fw_generic<f16>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), s,
-                   static_cast<f16 *>(y), mean, rstd, static_cast<const f16 *>(x),
-                   static_cast<const f16 *>(gamma), static_cast<const f16 *>(beta), N, a.C, eps);
-    } else {
-        e = launch(layernorm_fw_generic<float>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), s,
-                   static_cast<float *>(y), mean, rstd, static_cast<const float *>(x),
-                   static_cast<const float *>(gamma), static_cast<const float *>(beta), N, a.C, eps);
+template <typename T, bool RMS, int I>
+static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
+    constexpr LnPlan p = LnBwTable<T>::plans[I];
+    if (a.C <= p.bucket) {
+        static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && (p.R == 1 || p.R == 2), "bad backward plan");
+        static_assert(2 * (p.WG / 64) >= 2, "reduction slots");
+        const hipError_t e = launch(
+            layernorm_bw_vec<T, p.G, p.IT, p.WG, p.R, RMS>, dim3(static_cast<uint32_t>(a.blocks)),
+            dim3(p.WG), st, static_cast<T *>(a.dx), static_cast<typename Accum<T>::type *>(a.part),
+            static_cast<const T *>(a.dy), static_cast<const T *>(a.x),
+            static_cast<const T *>(a.gamma), a.mean, a.rstd, a.N, a.C, a.rows_per_block);
+        if (e != hipSuccess) return e;
+        return launch_colsum<T>(a.dgamma, a.dbeta, a.part, a.blocks, a.C, RMS ? 1 : 2, st);
     }
-    return status_of(e);
+    if constexpr (I + 1 < static_cast<int>(sizeof(LnBwTable<T>::plans) / sizeof(LnPlan)))
+        return dispatch_ln_bw<T, RMS, I + 1>(a, st);
+    return hipErrorInvalidValue;
 }
 
-extern "C" size_t layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype) {
+static size_t accum_size(lnr_dtype d) { return d == LNR_F16 ? sizeof(float) : sizeof(double); }
+
+static size_t bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype) {
     if (!valid_dtype(dtype) || N < 0 || C < 1 || C > LNR_LAYERNORM_MAX_C) return 0;
     int64_t pv, pg, rv, rg;
     bw_partials(N, C, dtype, pv, pg, rv, rg);
@@ -642,24 +666,68 @@ extern "C" size_t layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype d
     return static_cast<size_t>(P) * 2 * static_cast<size_t>(C) * accum_size(dtype);
 }
 
-extern "C" int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const void *x,
-                            const void *gamma, const float *mean, const float *rstd, int64_t N,
-                            int64_t C, lnr_dtype dtype, void *workspace, size_t workspace_bytes,
-                            void *stream) {
+// Forward of either norm. LayerNorm: beta required; mean and rstd both given or both NULL.
+// RMSNorm (rms): beta and mean are NULL; rstd optional.
+template <bool RMS>
+static int norm_fw(void *y, float *mean, float *rstd, const void *x, const void *gamma,
+                   const void *beta, int64_t N, int64_t C, float eps, lnr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (N < 0 || C < 1) return LNR_ERR_SHAPE;
+    if (C > LNR_LAYERNORM_MAX_C) return LNR_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || !isfinite(eps)) return LNR_ERR_SHAPE;
+    if (!RMS && (mean == nullptr) != (rstd == nullptr)) return LNR_ERR_NULL;
+    if (N == 0) return LNR_OK;
+    if (N > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    if (y == nullptr || x == nullptr || gamma == nullptr || (!RMS && beta == nullptr)) return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned_to(y, es) || !aligned_to(x, es) || !aligned_to(gamma, es) ||
+        (!RMS && !aligned_to(beta, es)) || !aligned_to(mean, 4) || !aligned_to(rstd, 4))
+        return LNR_ERR_ALIGN;
+    const size_t nbytes = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
+    const size_t cbytes = static_cast<size_t>(C) * es;
+    if (bad_alias(y, x, nbytes) || overlap(y, nbytes, gamma, cbytes) ||
+        overlap(y, nbytes, beta, cbytes) || overlap(y, nbytes, mean, N * 4) ||
+        overlap(y, nbytes, rstd, N * 4) || overlap(mean, N * 4, rstd, N * 4))
+        return LNR_ERR_ALIAS;
+
+    LnFwArgs a{y, mean, rstd, x, gamma, beta, N, static_cast<int32_t>(C), eps};
+    const bool vec = (static_cast<size_t>(C) * es) % 16 == 0 && aligned_to(y, 16) &&
+                     aligned_to(x, 16) && aligned_to(gamma, 16) && (RMS || aligned_to(beta, 16));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (vec) {
+        e = dtype == LNR_F16 ? dispatch_ln_fw<f16, RMS, 0>(a, s) : dispatch_ln_fw<float, RMS, 0>(a, s);
+    } else if (dtype == LNR_F16) {
+        e = launch(layernorm_fw_generic<f16, RMS>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), s,
+                   static_cast<f16 *>(y), mean, rstd, static_cast<const f16 *>(x),
+                   static_cast<const f16 *>(gamma), static_cast<const f16 *>(beta), N, a.C, eps);
+    } else {
+        e = launch(layernorm_fw_generic<float, RMS>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), s,
+                   static_cast<float *>(y), mean, rstd, static_cast<const float *>(x),
+                   static_cast<const float *>(gamma), static_cast<const float *>(beta), N, a.C, eps);
+    }
+    return status_of(e);
+}
+
+// Backward of either norm. RMSNorm (rms): dbeta and mean are NULL.
+template <bool RMS>
+static int norm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const void *x,
+                   const void *gamma, const float *mean, const float *rstd, int64_t N, int64_t C,
+                   lnr_dtype dtype, void *workspace, size_t workspace_bytes, void *stream) {
     if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
     if (N < 0 || C < 1) return LNR_ERR_SHAPE;
     if (C > LNR_LAYERNORM_MAX_C) return LNR_ERR_UNSUPPORTED;
     if (N > INT32_MAX) return LNR_ERR_UNSUPPORTED;
-    if (dgamma == nullptr || dbeta == nullptr) return LNR_ERR_NULL;
+    if (dgamma == nullptr || (!RMS && dbeta == nullptr)) return LNR_ERR_NULL;
     if (N > 0 && (dx == nullptr || dy == nullptr || x == nullptr || gamma == nullptr ||
-                  mean == nullptr || rstd == nullptr))
+                  (!RMS && mean == nullptr) || rstd == nullptr))
         return LNR_ERR_NULL;
     const size_t es = dtype_size(dtype);
     if (!aligned_to(dx, es) || !aligned_to(dgamma, es) || !aligned_to(dbeta, es) ||
         !aligned_to(dy, es) || !aligned_to(x, es) || !aligned_to(gamma, es) ||
         !aligned_to(mean, 4) || !aligned_to(rstd, 4))
         return LNR_ERR_ALIGN;
-    const size_t need = layernorm_bw_workspace_bytes(N, C, dtype);
+    const size_t need = bw_workspace_bytes(N, C, dtype);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LNR_ERR_WORKSPACE;
     if (need > 0 && !aligned_to(workspace, 8)) return LNR_ERR_ALIGN;
     const size_t nbytes = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
@@ -677,51 +745,84 @@ extern "C" int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy,
             return LNR_ERR_ALIAS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const int slots = RMS ? 1 : 2;
     int64_t pv, pg, rv, rg;
     bw_partials(N, C, dtype, pv, pg, rv, rg);
     const int32_t C32 = static_cast<int32_t>(C);
     hipError_t e = hipSuccess;
-    int64_t P = 0;
-    if (N > 0) {
-        const bool vec = (static_cast<size_t>(C) * es) % 16 == 0 && aligned_to(dx, 16) &&
-                         aligned_to(dy, 16) && aligned_to(x, 16) && aligned_to(gamma, 16);
-        if (vec) {
-            P = pv;
-            LnBwArgs a{dx, workspace, dy, x, gamma, mean, rstd, N, C32, rv, pv};
-            e = dtype == LNR_F16 ? dispatch_ln_bw<f16, 0>(a, s) : dispatch_ln_bw<float, 0>(a, s);
-        } else {
-            P = pg;
-            if (dtype == LNR_F16) {
-                e = launch(layernorm_bw_dx_generic<f16>, dim3(static_cast<uint32_t>(N)),
-                           dim3(kLnGenericWG), s, static_cast<f16 *>(dx),
-                           static_cast<const f16 *>(dy), static_cast<const f16 *>(x),
-                           static_cast<const f16 *>(gamma), mean, rstd, N, C32);
-                if (e == hipSuccess)
-                    e = launch(layernorm_bw_colpart_generic<f16>,
-                               dim3(static_cast<uint32_t>((C + kLnGenericWG - 1) / kLnGenericWG),
-                                    static_cast<uint32_t>(pg)),
-                               dim3(kLnGenericWG), s, static_cast<float *>(workspace),
-                               static_cast<const f16 *>(dy), static_cast<const f16 *>(x), mean,
-                               rstd, N, C32, rg);
-            } else {
-                e = launch(layernorm_bw_dx_generic<float>, dim3(static_cast<uint32_t>(N)),
-                           dim3(kLnGenericWG), s, static_cast<float *>(dx),
-                           static_cast<const float *>(dy), static_cast<const float *>(x),
-                           static_cast<const float *>(gamma), mean, rstd, N, C32);
-                if (e == hipSuccess)
-                    e = launch(layernorm_bw_colpart_generic<float>,
-                               dim3(static_cast<uint32_t>((C + kLnGenericWG - 1) / kLnGenericWG),
-                                    static_cast<uint32_t>(pg)),
-                               dim3(kLnGenericWG), s, static_cast<double *>(workspace),
-                               static_cast<const float *>(dy), static_cast<const float *>(x), mean,
-                               rstd, N, C32, rg);
-            }
-        }
+    if (N == 0) {
+        // No rows: the column sums are empty, and the column-sum kernel writes zeros.
+        e = dtype == LNR_F16 ? launch_colsum<f16>(dgamma, dbeta, workspace, 0, C32, slots, s)
+                             : launch_colsum<float>(dgamma, dbeta, workspace, 0, C32, slots, s);
+        return status_of(e);
     }
-    if (e == hipSuccess)
-        e = dtype == LNR_F16 ? launch_colsum<f16>(dgamma, dbeta, workspace, P, C32, s)
-                             : launch_colsum<float>(dgamma, dbeta, workspace, P, C32, s);
+    const bool vec = (static_cast<size_t>(C) * es) % 16 == 0 && aligned_to(dx, 16) &&
+                     aligned_to(dy, 16) && aligned_to(x, 16) && aligned_to(gamma, 16);
+    if (vec) {
+        LnBwArgs a{dx, dgamma, dbeta, workspace, dy, x, gamma, mean, rstd, N, C32, rv, pv};
+        e = dtype == LNR_F16 ? dispatch_ln_bw<f16, RMS, 0>(a, s) : dispatch_ln_bw<float, RMS, 0>(a, s);
+    } else if (dtype == LNR_F16) {
+        e = launch(layernorm_bw_dx_generic<f16, RMS>, dim3(static_cast<uint32_t>(N)),
+                   dim3(kLnGenericWG), s, static_cast<f16 *>(dx), static_cast<const f16 *>(dy),
+                   static_cast<const f16 *>(x), static_cast<const f16 *>(gamma), mean, rstd, N, C32);
+        if (e == hipSuccess)
+            e = launch(layernorm_bw_colpart_generic<f16, RMS>,
+                       dim3(static_cast<uint32_t>((C + kLnGenericWG - 1) / kLnGenericWG),
+                            static_cast<uint32_t>(pg)),
+                       dim3(kLnGenericWG), s, static_cast<float *>(workspace),
+                       static_cast<const f16 *>(dy), static_cast<const f16 *>(x), mean, rstd, N, C32, rg);
+        if (e == hipSuccess) e = launch_colsum<f16>(dgamma, dbeta, workspace, pg, C32, slots, s);
+    } else {
+        e = launch(layernorm_bw_dx_generic<float, RMS>, dim3(static_cast<uint32_t>(N)),
+                   dim3(kLnGenericWG), s, static_cast<float *>(dx), static_cast<const float *>(dy),
+                   static_cast<const float *>(x), static_cast<const float *>(gamma), mean, rstd, N, C32);
+        if (e == hipSuccess)
+            e = launch(layernorm_bw_colpart_generic<float, RMS>,
+                       dim3(static_cast<uint32_t>((C + kLnGenericWG - 1) / kLnGenericWG),
+                            static_cast<uint32_t>(pg)),
+                       dim3(kLnGenericWG), s, static_cast<double *>(workspace),
+                       static_cast<const float *>(dy), static_cast<const float *>(x), mean, rstd, N, C32, rg);
+        if (e == hipSuccess) e = launch_colsum<float>(dgamma, dbeta, workspace, pg, C32, slots, s);
+    }
     return status_of(e);
+}
+
+}  // namespace lnr
+
+using namespace lnr;
+
+extern "C" int layernorm_fw(void *y, float *mean, float *rstd, const void *x, const void *gamma,
+                            const void *beta, int64_t N, int64_t C, float eps, lnr_dtype dtype,
+                            void *stream) {
+    return norm_fw<false>(y, mean, rstd, x, gamma, beta, N, C, eps, dtype, stream);
+}
+
+extern "C" size_t layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype) {
+    return bw_workspace_bytes(N, C, dtype);
+}
+
+extern "C" int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const void *x,
+                            const void *gamma, const float *mean, const float *rstd, int64_t N,
+                            int64_t C, lnr_dtype dtype, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    return norm_bw<false>(dx, dgamma, dbeta, dy, x, gamma, mean, rstd, N, C, dtype, workspace,
+                          workspace_bytes, stream);
+}
+
+extern "C" int rmsnorm_fw(void *y, float *rstd, const void *x, const void *gamma, int64_t N,
+                          int64_t C, float eps, lnr_dtype dtype, void *stream) {
+    return norm_fw<true>(y, nullptr, rstd, x, gamma, nullptr, N, C, eps, dtype, stream);
+}
+
+extern "C" size_t rmsnorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype) {
+    return bw_workspace_bytes(N, C, dtype);
+}
+
+extern "C" int rmsnorm_bw(void *dx, void *dgamma, const void *dy, const void *x, const void *gamma,
+                          const float *rstd, int64_t N, int64_t C, lnr_dtype dtype, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return norm_bw<true>(dx, dgamma, nullptr, dy, x, gamma, nullptr, rstd, N, C, dtype, workspace,
+                         workspace_bytes, stream);
 }
 
 // Introspection: the bucket, lanes per row, vectors per lane and workgroup size of the

@@ -30,6 +30,9 @@ import torch
 SOFTMAX_TK_SWEEP = (32, 64, 128, 256, 384, 512, 768, 1024, 2048)
 LAYERNORM_C_SWEEP = (256, 768, 1024, 4096, 8192)
 LN_EPS = 1e-8
+# RMSNorm: the FastTransformer page's module (section 5.4) uses eps = 1e-6 and d_model = 256
+# with the GPT-2 batch of section 1 (B = 32, T = 256, so 8192 rows).
+RMS_EPS = 1e-6
 
 K_SCORES, K_LENGTHS, K_SDY, K_X, K_OFFSET, K_GAMMA, K_BETA, K_LNDY = range(8)
 
@@ -187,6 +190,24 @@ def workload5_layernorm(C: int, dtype=torch.float16) -> LayerNormCase:
                           seed_base=seed_of(5, 0, v), gamma_uniform=False, beta_var=1.0)
 
 
+def rmsnorm_gpt2_case(dtype=torch.float16) -> LayerNormCase:
+    """RMSNorm [8192, 256]: the FastTransformer page's Pre-RMSNorm at its own model width and
+    batch. x, dy ~ N(0,1); weight ~ U(0.5,1.5) (the page initialises it to ones; a random
+    weight exercises the product); no bias."""
+    tag = "f16" if dtype == torch.float16 else "f32"
+    return layernorm_case(f"rms-8192x256-{tag}", 8192, 256, dtype=dtype,
+                          seed_base=seed_of(6, 0), eps=RMS_EPS)
+
+
+def rmsnorm_sweep_case(N: int, C: int, dtype=torch.float16) -> LayerNormCase:
+    """RMSNorm at the LayerNorm sweep's shapes, x with a per-row N(0,4) offset (so mean(x^2)
+    is dominated by the offset in some rows), dy ~ N(0,1)."""
+    tag = "f16" if dtype == torch.float16 else "f32"
+    return layernorm_case(f"rms-{N}x{C}-offset-{tag}", N, C, dtype=dtype,
+                          seed_base=seed_of(6, 0, 1 + (LAYERNORM_C_SWEEP.index(C) if C in LAYERNORM_C_SWEEP else 9)),
+                          row_offset_var=4.0, eps=RMS_EPS)
+
+
 # ------------------------------------------------------------------------------------------
 # Algorithmic bytes: each tensor read or written once, dense (masked positions included).
 # ------------------------------------------------------------------------------------------
@@ -209,6 +230,16 @@ def softmax_bw_bytes(B, H, Tq, Tk, s) -> int:
 def layernorm_fw_bytes(N, C, s) -> int:
     """Read x, write y, write fp32 mean and rstd, read gamma and beta."""
     return 2 * N * C * s + 8 * N + 2 * C * s
+
+
+def rmsnorm_fw_bytes(N, C, s) -> int:
+    """Read x, write y, write rstd (fp32), read gamma."""
+    return 2 * N * C * s + 4 * N + C * s
+
+
+def rmsnorm_bw_bytes(N, C, s) -> int:
+    """Read x, dy, rstd (fp32) and gamma; write dx and dgamma."""
+    return 3 * N * C * s + 4 * N + 2 * C * s
 
 
 def layernorm_bw_bytes(N, C, s) -> int:

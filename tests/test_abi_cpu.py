@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -142,6 +142,48 @@ def test_layernorm_bw_validation(lib):
     assert lbw(lib, dx=A + 2 ** 30 + 64) == ALIAS            # dx over dy
     assert lbw(lib, db=A + 2 ** 33 + 2) == ALIAS             # dbeta over dgamma
     assert lbw(lib, ws=A + 2 ** 30) == ALIAS                 # workspace over dy
+
+
+def rfw(lib, y=A, rstd=A + 2 ** 32, x=A + 2 ** 30, g=A + 2 ** 31, N=64, C=64, eps=1e-6, dtype=F16):
+    return lib.rmsnorm_fw(y, rstd, x, g, N, C, eps, dtype, None)
+
+
+def test_rmsnorm_fw_validation(lib):
+    assert rfw(lib, dtype=5) == DTYPE
+    assert rfw(lib, C=0) == SHAPE
+    assert rfw(lib, N=-1) == SHAPE
+    assert rfw(lib, C=8193) == UNSUP
+    assert rfw(lib, eps=-1.0) == SHAPE
+    assert rfw(lib, g=None) == NULL
+    assert rfw(lib, x=None) == NULL
+    assert rfw(lib, x=A + 2 ** 30 + 1) == ALIGN
+    assert rfw(lib, rstd=A + 2 ** 32 + 2) == ALIGN
+    assert rfw(lib, x=A + 256) == ALIAS                      # partial overlap of y and x
+    assert rfw(lib, rstd=A + 64) == ALIAS                    # rstd inside y
+    assert rfw(lib, N=0) == OK
+
+
+def rbw(lib, dx=A, dg=A + 2 ** 33, dy=A + 2 ** 30, x=A + 2 ** 31, g=A + 2 ** 32,
+        rstd=A + 2 ** 32 + 2 ** 21, N=64, C=64, dtype=F16, ws=A + 2 ** 34, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.rmsnorm_bw_workspace_bytes(N, C, dtype)
+    return lib.rmsnorm_bw(dx, dg, dy, x, g, rstd, N, C, dtype, ws, ws_bytes, None)
+
+
+def test_rmsnorm_bw_validation(lib):
+    assert rbw(lib, dtype=9) == DTYPE
+    assert rbw(lib, C=0) == SHAPE
+    assert rbw(lib, C=10000) == UNSUP
+    assert rbw(lib, dg=None) == NULL
+    assert rbw(lib, rstd=None) == NULL
+    assert rbw(lib, x=A + 2 ** 31 + 1) == ALIGN
+    need = lib.rmsnorm_bw_workspace_bytes(64, 64, F16)
+    assert need > 0
+    assert rbw(lib, ws_bytes=need - 1) == WS
+    assert rbw(lib, dx=A + 2 ** 31) == ALIAS                 # dx over x
+    assert rbw(lib, dg=A + 2 ** 30 + 2) == ALIAS             # dgamma over dy
+    assert rbw(lib, ws=A + 2 ** 31) == ALIAS                 # workspace over x
+    assert lib.rmsnorm_bw_workspace_bytes(0, 64, F16) == 0
 
 
 def test_workspace_bytes(lib):
