@@ -20,6 +20,9 @@ Citations (page titles and sections; see ``lnr_oracle.c`` for the formulas):
     across rows).
   * RMSNorm: "FastTransformer: Breaking the Compiler Ceiling ...", section 5.4 (forward,
     backward recomputing rstd from x, and backward from a given rstd).
+  * Softmax cross-entropy over a vocabulary: L10 "Technique 1" names the reduce kernel and
+    the inference section the whole-vocabulary softmax; no formula is printed, so this is
+    the textbook definition (lse - z_target; gradient softmax - onehot), no label smoothing.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against closed forms,
 invariants, finite differences and independent fp64 library routines.
@@ -74,6 +77,11 @@ def _load():
     lib.lnr_oracle_rmsnorm_bw_given_rstd.argtypes = [d, d, d, d, i64, i64, d, d]
     lib.lnr_oracle_layernorm_bw_given_stats.argtypes = [d, d, d, d, d, i64, i64, d, d, d]
     lib.lnr_oracle_layernorm_bw_given_stats.restype = None
+    pi64 = ctypes.POINTER(ctypes.c_int64)
+    lib.lnr_oracle_xent_fw.argtypes = [d, pi64, i64, i64, i64, d, d]
+    lib.lnr_oracle_xent_fw.restype = None
+    lib.lnr_oracle_xent_bw_given_lse.argtypes = [d, pi64, d, d, i64, i64, i64, d]
+    lib.lnr_oracle_xent_bw_given_lse.restype = None
     lib.lnr_oracle_threads.argtypes = []
     lib.lnr_oracle_threads.restype = ctypes.c_int
     lib.lnr_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -242,3 +250,40 @@ def rmsnorm_bw(x, dy, gamma, eps: float = 1e-6):
     dg = np.empty(C, np.float64)
     _load().lnr_oracle_rmsnorm_bw(_p(x), _p(dy), _p(g), N, C, float(eps), _p(dx), _p(dg))
     return dx, dg
+
+
+def _i64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # a CPU torch tensor
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int64)
+
+
+def xent_fw(z, target, ignore_index: int = -100):
+    """Softmax cross-entropy per row: returns (loss, lse) as float64. z [N, V]; target [N]."""
+    z = _f64(z)
+    N, V = z.shape
+    t = _i64(target).reshape(N)
+    loss = np.empty(N, np.float64)
+    lse = np.empty(N, np.float64)
+    _load().lnr_oracle_xent_fw(_p(z), t.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), N, V,
+                               int(ignore_index), _p(loss), _p(lse))
+    return loss, lse
+
+
+def xent_bw_given_lse(z, target, lse, dloss, ignore_index: int = -100):
+    """Gradient of sum_i dloss_i * loss_i with respect to z, from a given lse per row."""
+    z = _f64(z)
+    N, V = z.shape
+    t = _i64(target).reshape(N)
+    l = _f64(lse).reshape(N)
+    g = _f64(dloss).reshape(N)
+    dz = np.empty_like(z)
+    _load().lnr_oracle_xent_bw_given_lse(_p(z), t.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         _p(l), _p(g), N, V, int(ignore_index), _p(dz))
+    return dz
+
+
+def xent_bw(z, target, dloss, ignore_index: int = -100):
+    """Gradient with lse recomputed from z in fp64."""
+    _, lse = xent_fw(z, target, ignore_index)
+    return xent_bw_given_lse(z, target, lse, dloss, ignore_index)

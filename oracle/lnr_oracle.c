@@ -1,6 +1,6 @@
 /*
- * lnr_oracle.c -- fp64 CPU oracle for masked/causal attention softmax and LayerNorm,
- * forward and backward.
+ * lnr_oracle.c -- fp64 CPU oracle for masked/causal attention softmax, LayerNorm, RMSNorm
+ * and softmax cross-entropy over a vocabulary, forward and backward.
  *
  * TEST INFRASTRUCTURE ONLY. The product library never links, loads or calls this file.
  * Only the test suite, the smoke check and the CPU-baseline leg of the benchmark use it,
@@ -26,6 +26,10 @@
  *          softmax(inp + mask) baseline, i.e. an additive mask).
  *   [FT]   "FastTransformer: Breaking the Compiler Ceiling via Architectural Co-Design",
  *          section 5.4 "Vectorized Pre-RMSNorm" (RMSNorm: no mean, one sum of squares).
+ *   [L10]  section "Technique 1: kernel fusion, leaving only GEMMs to cuBLAS" (cross entropy
+ *          is one of the custom reduce kernels) and "Inference: making beam search skip a
+ *          sort" (a softmax over the whole vocabulary). The pages give no formula; the
+ *          oracle is the textbook softmax cross-entropy (no label smoothing).
  * The softmax backward formula is never printed on the pages; it is the textbook Jacobian
  * of softmax (diag(y) - y y^T) applied to dy, and it is pinned by finite differences.
  */
@@ -379,6 +383,63 @@ ORACLE_API void lnr_oracle_rmsnorm_bw_given_rstd(const double *x, const double *
         for (int64_t i = 0; i < N; ++i)
             for (int64_t j = jb; j < je; ++j)
                 dgamma[j] += dy[i * C + j] * (x[i * C + j] * rstd[i]);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Softmax cross-entropy over a vocabulary. [L10 "Technique 1"; textbook definition]
+ * For row i with logits z_i[0..V) and target t_i:
+ *   M_i   = max_j z_ij,   lse_i = M_i + log( sum_j exp(z_ij - M_i) )
+ *   loss_i = lse_i - z_i,t_i
+ * A row whose target equals ignore_index has loss 0 (its lse is still computed). A target
+ * outside [0, V) that is not ignore_index gives loss NaN.
+ * ------------------------------------------------------------------------------------- */
+ORACLE_API void lnr_oracle_xent_fw(const double *z, const int64_t *target, int64_t N, int64_t V,
+                                   int64_t ignore_index, double *loss, double *lse)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        const double *zr = z + i * V;
+        double M = -INFINITY;
+        for (int64_t j = 0; j < V; ++j)
+            if (zr[j] > M) M = zr[j];
+        double S = 0.0;
+        for (int64_t j = 0; j < V; ++j)
+            S += exp(zr[j] - M);
+        lse[i] = M + log(S);
+        const int64_t t = target[i];
+        if (t == ignore_index)
+            loss[i] = 0.0;
+        else if (t < 0 || t >= V)
+            loss[i] = NAN;
+        else
+            loss[i] = lse[i] - zr[t];
+    }
+}
+
+/* Cross-entropy backward from a given lse (the value a forward pass saved) and the upstream
+ * gradient dloss_i of each row's loss:
+ *   dz_ij = dloss_i * ( exp(z_ij - lse_i) - [j == t_i] )
+ * (the derivative of lse - z_t: softmax minus the one-hot target). Rows whose target is
+ * ignore_index get dz = 0; a target outside [0, V) otherwise gives a row of NaN. */
+ORACLE_API void lnr_oracle_xent_bw_given_lse(const double *z, const int64_t *target,
+                                             const double *lse, const double *dloss, int64_t N,
+                                             int64_t V, int64_t ignore_index, double *dz)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        const double *zr = z + i * V;
+        const int64_t t = target[i];
+        for (int64_t j = 0; j < V; ++j) {
+            double d;
+            if (t == ignore_index)
+                d = 0.0;
+            else if (t < 0 || t >= V)
+                d = NAN;
+            else
+                d = dloss[i] * (exp(zr[j] - lse[i]) - (j == t ? 1.0 : 0.0));
+            dz[i * V + j] = d;
+        }
     }
 }
 
