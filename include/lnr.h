@@ -205,6 +205,51 @@ LNR_API int rmsnorm_bw(void *dx, void *dgamma, const void *dy, const void *x, co
                        size_t workspace_bytes, void *stream);
 
 /*
+ * cross_entropy_fw_workspace_bytes -- device workspace cross_entropy_fw needs for (N, V,
+ * dtype): per-chunk partial (max, sum) pairs when there are too few rows to fill the GPU and
+ * each row is split over several workgroups; 0 when rows are not split (the common case of
+ * thousands of rows) and for an invalid shape/dtype.
+ */
+LNR_API size_t cross_entropy_fw_workspace_bytes(int64_t N, int64_t V, lnr_dtype dtype);
+
+/*
+ * cross_entropy_fw -- softmax cross-entropy over a vocabulary, per row.
+ * ["CMU 11-868 L10 ...", section "Technique 1": cross entropy is one of the custom reduce
+ *  kernels; the inference section: a softmax over the whole vocabulary. No formula is
+ *  printed; this is the textbook one, without label smoothing.]
+ *
+ *   lse_i  = log sum_j exp(z_ij)          (one streaming pass over the row)
+ *   loss_i = lse_i - z_i,target_i
+ *   loss   [N] float32, written.  lse [N] float32, written (saved for cross_entropy_bw).
+ *   logits [N, V] dtype, read; any V >= 1 (odd V included; rows need not be 16-byte aligned).
+ *   target [N] int64, read: a class in [0, V), or ignore_index (loss 0). Any other value
+ *          gives loss NaN for that row (the kernel cannot raise an error).
+ *   workspace  cross_entropy_fw_workspace_bytes(N, V, dtype) bytes (may be NULL when that
+ *          is 0), 8-byte aligned, owned by the caller; contents on entry do not matter.
+ *   Limits: N <= INT32_MAX, 1 <= V <= INT32_MAX / 2.
+ */
+LNR_API int cross_entropy_fw(float *loss, float *lse, const void *logits, const int64_t *target,
+                             int64_t N, int64_t V, int64_t ignore_index, lnr_dtype dtype,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * cross_entropy_bw -- gradient of sum_i scale * dloss_i * loss_i with respect to the logits.
+ * [Same passages as cross_entropy_fw; the derivative of lse - z_t is softmax - onehot.]
+ *
+ *   dlogits_ij = scale * dloss_i * ( exp(z_ij - lse_i) - [j == target_i] )
+ *   dlogits [N, V] dtype, written; may equal logits (in place), no other overlap.
+ *   logits  [N, V] dtype, read.  target [N] int64, read.
+ *   lse     [N] float32, read: the values cross_entropy_fw wrote.
+ *   dloss   [N] float32 upstream gradient of each row's loss, or NULL for all ones.
+ *   scale   a finite factor on every row (for a mean over rows: 1 / number of rows counted).
+ *   Rows whose target is ignore_index get a zero gradient row; any other target outside
+ *   [0, V) gives a row of NaN.
+ */
+LNR_API int cross_entropy_bw(void *dlogits, const void *logits, const int64_t *target,
+                             const float *lse, const float *dloss, float scale, int64_t N,
+                             int64_t V, int64_t ignore_index, lnr_dtype dtype, void *stream);
+
+/*
  * lnr_copy -- measurement helper, not part of the method: copies `bytes` bytes from src to
  * dst with the same 128-bit load/store pattern as the row kernels, giving the achievable
  * streaming ceiling that the kernels' bandwidth is compared with. dst and src must not

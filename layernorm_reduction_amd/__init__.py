@@ -16,6 +16,11 @@ Functions mirror the C entry points:
     rmsnorm_fw(x, gamma, eps=1e-6, y=None, rstd=None) -> (y, rstd)
     rmsnorm_bw(dy, x, gamma, rstd, dx=None, dgamma=None, workspace=None) -> (dx, dgamma)
     rmsnorm_bw_workspace_bytes(N, C, dtype) -> int
+    cross_entropy_fw(logits, target, ignore_index=-100, loss=None, lse=None,
+                     workspace=None) -> (loss, lse)
+    cross_entropy_bw(logits, target, lse, dloss=None, scale=1.0, ignore_index=-100,
+                     dlogits=None) -> dlogits
+    cross_entropy_fw_workspace_bytes(N, V, dtype) -> int
 """
 from __future__ import annotations
 
@@ -25,7 +30,8 @@ import os
 __all__ = [
     "LnrError", "load", "library_path", "attn_softmax_fw", "attn_softmax_bw", "layernorm_fw",
     "layernorm_bw", "layernorm_bw_workspace_bytes", "rmsnorm_fw", "rmsnorm_bw",
-    "rmsnorm_bw_workspace_bytes", "copy_bytes", "xor_bytes", "softmax_plan",
+    "rmsnorm_bw_workspace_bytes", "cross_entropy_fw", "cross_entropy_bw",
+    "cross_entropy_fw_workspace_bytes", "copy_bytes", "xor_bytes", "softmax_plan",
     "layernorm_plan", "LNR_F32", "LNR_F16", "SOFTMAX_MAX_TK", "LAYERNORM_MAX_C",
 ]
 
@@ -77,6 +83,10 @@ def load():
     lib.rmsnorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
     lib.rmsnorm_bw_workspace_bytes.restype = sz
     lib.rmsnorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
+    lib.cross_entropy_fw_workspace_bytes.argtypes = [i64, i64, ci]
+    lib.cross_entropy_fw_workspace_bytes.restype = sz
+    lib.cross_entropy_fw.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, sz, vp]
+    lib.cross_entropy_bw.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, i64, ci, vp]
     lib.lnr_copy.argtypes = [vp, vp, sz, vp]
     lib.lnr_xor2.argtypes = [vp, vp, vp, sz, vp]
     lib.lnr_time_next_launch.argtypes = [vp, vp]
@@ -88,7 +98,7 @@ def load():
     lib.lnr_softmax_plan.argtypes = [i64, ci, ci, ip, ip, ip]
     lib.lnr_layernorm_plan.argtypes = [i64, i64, ci, ci, ip, ip, ip, ip, ctypes.POINTER(i64)]
     for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw", "rmsnorm_fw",
-              "rmsnorm_bw", "lnr_copy",
+              "rmsnorm_bw", "cross_entropy_fw", "cross_entropy_bw", "lnr_copy",
               "lnr_xor2", "lnr_softmax_plan", "lnr_layernorm_plan"):
         getattr(lib, f).restype = ci
     _lib = lib
@@ -352,6 +362,71 @@ def rmsnorm_bw(dy, x, gamma, rstd, dx=None, dgamma=None, workspace=None):
     return dx, dgamma
 
 
+def _targets(target, N, like):
+    torch = _torch()
+    if not target.is_cuda or target.device != like.device:
+        raise ValueError("target must be on the same GPU as the logits")
+    if target.dtype != torch.int64 or not target.is_contiguous() or target.numel() != N:
+        raise ValueError("target must be a contiguous int64 tensor of N elements")
+
+
+def cross_entropy_fw_workspace_bytes(N: int, V: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (LNR_F16 if str(dtype).endswith("float16") else LNR_F32)
+    return int(load().cross_entropy_fw_workspace_bytes(int(N), int(V), code))
+
+
+def cross_entropy_fw(logits, target, ignore_index: int = -100, loss=None, lse=None, workspace=None):
+    """Softmax cross-entropy per row of logits [N, V]; returns (loss, lse), both fp32 [N]."""
+    torch = _torch()
+    _dev(logits, "logits")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [N, V]")
+    N, V = logits.shape
+    _targets(target, N, logits)
+    if loss is None:
+        loss = torch.empty(N, dtype=torch.float32, device=logits.device)
+    if lse is None:
+        lse = torch.empty(N, dtype=torch.float32, device=logits.device)
+    _f32(loss, "loss", logits)
+    _f32(lse, "lse", logits)
+    if loss.numel() != N or lse.numel() != N:
+        raise ValueError("loss and lse must have N elements")
+    code = _dtype_code(logits)
+    need = int(load().cross_entropy_fw_workspace_bytes(N, V, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().cross_entropy_fw(_ptr(loss), _ptr(lse), _ptr(logits), _ptr(target), N, V,
+                                 int(ignore_index), code, _ptr(workspace), wb, _stream(logits))
+    _check(st, "cross_entropy_fw")
+    return loss, lse
+
+
+def cross_entropy_bw(logits, target, lse, dloss=None, scale: float = 1.0, ignore_index: int = -100,
+                     dlogits=None):
+    """Gradient of sum_i scale * dloss_i * loss_i with respect to logits (dloss None: ones)."""
+    torch = _torch()
+    _dev(logits, "logits")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [N, V]")
+    N, V = logits.shape
+    _targets(target, N, logits)
+    _f32(lse, "lse", logits)
+    if dloss is not None:
+        _f32(dloss, "dloss", logits)
+        if dloss.numel() != N:
+            raise ValueError("dloss must have N elements")
+    if dlogits is None:
+        dlogits = torch.empty_like(logits)
+    else:
+        _dev(dlogits, "dlogits", like=logits)
+    st = load().cross_entropy_bw(_ptr(dlogits), _ptr(logits), _ptr(target), _ptr(lse), _ptr(dloss),
+                                 float(scale), N, V, int(ignore_index), _dtype_code(logits),
+                                 _stream(logits))
+    _check(st, "cross_entropy_bw")
+    return dlogits
+
+
 def copy_bytes(dst, src):
     """Streaming 16-byte-vector copy of src into dst (measurement helper)."""
     _dev(src, "src")
@@ -445,6 +520,25 @@ def bind_layernorm_bw(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace):
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(x))
     return BoundCall("layernorm_bw", load().layernorm_bw, args,
                      (dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace))
+
+
+def bind_cross_entropy_fw(logits, target, ignore_index, loss, lse, workspace):
+    cross_entropy_fw(logits, target, ignore_index, loss, lse, workspace)
+    N, V = logits.shape
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (loss.data_ptr(), lse.data_ptr(), logits.data_ptr(), target.data_ptr(), N, V,
+            int(ignore_index), _dtype_code(logits), _ptr(workspace), wb, _stream(logits))
+    return BoundCall("cross_entropy_fw", load().cross_entropy_fw, args,
+                     (logits, target, loss, lse, workspace))
+
+
+def bind_cross_entropy_bw(logits, target, lse, dloss, scale, ignore_index, dlogits):
+    cross_entropy_bw(logits, target, lse, dloss, scale, ignore_index, dlogits)
+    N, V = logits.shape
+    args = (dlogits.data_ptr(), logits.data_ptr(), target.data_ptr(), lse.data_ptr(), _ptr(dloss),
+            float(scale), N, V, int(ignore_index), _dtype_code(logits), _stream(logits))
+    return BoundCall("cross_entropy_bw", load().cross_entropy_bw, args,
+                     (logits, target, lse, dloss, dlogits))
 
 
 def bind_rmsnorm_fw(x, gamma, eps, y, rstd):

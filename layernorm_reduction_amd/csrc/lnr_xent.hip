@@ -1,0 +1,361 @@
+// lnr_xent.hip -- softmax cross-entropy over a vocabulary, forward and backward, for gfx950.
+//
+// Method: "CMU 11-868 L10 ...", section "Technique 1: kernel fusion, leaving only GEMMs to
+// cuBLAS" (cross entropy is one of the custom reduce kernels) and the inference section (a
+// softmax over the whole vocabulary). The pages print no formula; this is the textbook one:
+//   forward   lse_i = log sum_j exp(z_ij),  loss_i = lse_i - z_i,t_i
+//   backward  dz_ij = dloss_i * scale * (exp(z_ij - lse_i) - [j == t_i])
+// Rows whose target is ignore_index give loss 0 and a zero gradient row; a target outside
+// [0, V) otherwise gives NaN (a visible result; a kernel cannot raise).
+//
+// Design on CDNA4:
+//   * Rows are long (10^4 - 10^5 logits, 20-400 KB): a workgroup streams one row (or one
+//     chunk of a row when there are too few rows to fill the chip), 16-byte non-temporal
+//     loads, U vectors in flight per thread per iteration.
+//   * Forward, one pass: each thread keeps a running maximum m and a sum s of exp(z - m);
+//     per iteration it takes the maximum of its U*VE new logits and rescales s once, so the
+//     cost is one exp per logit plus one per U*VE. Then the workgroup reduces (m, s): the
+//     block maximum first, then the sum of the rescaled s. Split rows write (m, s) partials
+//     and a small kernel combines them in chunk order.
+//   * Any V and any row alignment: a row is a scalar head up to the first 16-byte boundary,
+//     16-byte vectors, and a scalar tail, so a vocabulary of odd size (every row starting at
+//     a different phase) still streams at full width.
+//   * Backward, one pass: each logit is read once and its gradient written once.
+#include <math.h>
+
+#include "lnr_common.h"
+#include "lnr_prims.h"
+
+namespace lnr {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Elements [0, head) and [tail, V) one at a time, [head, tail) as nvec 16-byte vectors.
+struct RowSplit {
+    int32_t head, nvec, tail;
+};
+
+template <typename T>
+__device__ __forceinline__ RowSplit split_row(const T *row, int32_t V, bool vec_ok) {
+    constexpr int VE = Vec16<T>::N;
+    if (!vec_ok) return {V, 0, V};
+    const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
+    int32_t head = static_cast<int32_t>(((16u - phase) & 15u) / sizeof(T));
+    if (head > V) head = V;
+    const int32_t nvec = (V - head) / VE;
+    return {head, nvec, head + nvec * VE};
+}
+
+// Vectors [v0, v1) of chunk c out of S (contiguous, in order).
+__device__ __forceinline__ void chunk_range(int32_t nvec, int32_t c, int32_t S, int32_t &v0,
+                                            int32_t &v1) {
+    v0 = static_cast<int32_t>(static_cast<int64_t>(nvec) * c / S);
+    v1 = static_cast<int32_t>(static_cast<int64_t>(nvec) * (c + 1) / S);
+}
+
+// Fold logits whose maximum is vm and whose exp-sum relative to that maximum is acc into
+// the running (m, s).
+__device__ __forceinline__ void ms_fold(float &m, float &s, float vm, float acc) {
+    const float mn = fmaxf(m, vm);
+    if (mn == -INFINITY) return;  // nothing finite yet
+    const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+    const float b = vm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((vm - mn) * kLog2e);
+    s = s * a + acc * b;
+    m = mn;
+}
+
+// ------------------------------------------------------------------------------------------
+// Forward statistics of row blockIdx.x, chunk blockIdx.y of S: (m, s) with s = sum exp(z - m).
+// S == 1: writes lse and loss. S > 1: writes the chunk's (m, s) to part[(row*S + chunk)*2].
+// ------------------------------------------------------------------------------------------
+template <typename T, int WG, int U>
+__global__ __launch_bounds__(WG) void xent_fw_kernel(float *__restrict__ loss,
+                                                     float *__restrict__ lse,
+                                                     float *__restrict__ part, const T *z,
+                                                     const int64_t *__restrict__ target,
+                                                     int32_t V, int64_t ignore_index,
+                                                     int32_t S, int32_t vec_ok) {
+    using RV = RawVec<T>;
+    constexpr int VE = Vec16<T>::N;
+    __shared__ float red[WG / 64];
+    const int64_t row = blockIdx.x;
+    const int32_t chunk = blockIdx.y;
+    const T *zr = z + row * static_cast<int64_t>(V);
+    const RowSplit sp = split_row(zr, V, vec_ok != 0);
+    int32_t v0, v1;
+    chunk_range(sp.nvec, chunk, S, v0, v1);
+    const RV *zv = reinterpret_cast<const RV *>(zr + sp.head);
+
+    float m = -INFINITY, s = 0.f;
+    // Scalar edges: the head with chunk 0, the tail with the last chunk.
+    if (chunk == 0)
+        for (int32_t j = threadIdx.x; j < sp.head; j += WG) ms_fold(m, s, to_f32(zr[j]), 1.f);
+    if (chunk == S - 1)
+        for (int32_t j = sp.tail + threadIdx.x; j < V; j += WG) ms_fold(m, s, to_f32(zr[j]), 1.f);
+
+    for (int32_t base = v0; base < v1; base += WG * U) {
+        float x[U][VE];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t v = base + u * WG + threadIdx.x;
+            const bool ok = v < v1;
+            const RV raw = load_stream_raw<T>(reinterpret_cast<const T *>(zv + (ok ? v : v0)));
+            widen<T>(raw, x[u]);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) x[u][e] = ok ? x[u][e] : -INFINITY;
+        }
+        float vm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) vm = fmaxf(vm, x[u][e]);
+        if (vm != -INFINITY) {
+            float acc = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc += __builtin_amdgcn_exp2f((x[u][e] - vm) * kLog2e);
+            ms_fold(m, s, vm, acc);
+        }
+    }
+
+    const float M = row_allreduce<WG>(m, OpMax(), red);
+    const float sc = (m == -INFINITY || M == -INFINITY) ? 0.f
+                                                        : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+    const float Ssum = row_allreduce<WG>(sc, OpSum(), red);
+    if (threadIdx.x != 0) return;
+    if (S > 1) {
+        part[(row * S + chunk) * 2 + 0] = M;
+        part[(row * S + chunk) * 2 + 1] = Ssum;
+        return;
+    }
+    const float logS = logf(Ssum);
+    lse[row] = M + logS;
+    const int64_t t = target[row];
+    // loss = (M - z_t) + log S rather than lse - z_t: M and z_t are exact inputs, so their
+    // difference rounds once, where lse - z_t would cancel two large numbers (|z| ~ 1e4).
+    if (t == ignore_index)
+        loss[row] = 0.f;
+    else if (t < 0 || t >= V)
+        loss[row] = NAN;
+    else
+        loss[row] = (M - to_f32(zr[t])) + logS;
+}
+
+// Combine the S chunk partials of each row in chunk order: M = max M_c, S = sum S_c *
+// exp(M_c - M); then lse and loss. One thread per row.
+template <typename T>
+__global__ __launch_bounds__(256) void xent_fw_finish(float *__restrict__ loss,
+                                                      float *__restrict__ lse,
+                                                      const float *__restrict__ part, const T *z,
+                                                      const int64_t *__restrict__ target,
+                                                      int64_t N, int32_t V, int64_t ignore_index,
+                                                      int32_t S) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (row >= N) return;
+    const float *pr = part + row * S * 2;
+    float M = -INFINITY;
+    for (int32_t c = 0; c < S; ++c) M = fmaxf(M, pr[2 * c]);
+    float Ssum = 0.f;
+    if (M != -INFINITY)
+        for (int32_t c = 0; c < S; ++c)
+            if (pr[2 * c] != -INFINITY)
+                Ssum += pr[2 * c + 1] * __builtin_amdgcn_exp2f((pr[2 * c] - M) * kLog2e);
+    const float logS = logf(Ssum);
+    lse[row] = M + logS;
+    const int64_t t = target[row];
+    if (t == ignore_index)
+        loss[row] = 0.f;
+    else if (t < 0 || t >= V)
+        loss[row] = NAN;
+    else
+        loss[row] = (M - to_f32(z[row * static_cast<int64_t>(V) + t])) + logS;
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward: dz = g * (exp(z - lse) - onehot), g = dloss[row] * scale (dloss NULL: 1).
+// Row blockIdx.x, chunk blockIdx.y of S. vec_ok also requires z and dz rows to share their
+// 16-byte phase (checked by the host).
+// ------------------------------------------------------------------------------------------
+template <typename T, int WG, int U>
+__global__ __launch_bounds__(WG) void xent_bw_kernel(T *dz, const T *z,
+                                                     const int64_t *__restrict__ target,
+                                                     const float *__restrict__ lse,
+                                                     const float *__restrict__ dloss, float scale,
+                                                     int32_t V, int64_t ignore_index, int32_t S,
+                                                     int32_t vec_ok) {
+    using RV = RawVec<T>;
+    constexpr int VE = Vec16<T>::N;
+    const int64_t row = blockIdx.x;
+    const int32_t chunk = blockIdx.y;
+    const int64_t rbase = row * static_cast<int64_t>(V);
+    const T *zr = z + rbase;
+    T *dr = dz + rbase;
+    const RowSplit sp = split_row(zr, V, vec_ok != 0);
+    int32_t v0, v1;
+    chunk_range(sp.nvec, chunk, S, v0, v1);
+
+    const int64_t t = target[row];
+    const bool ignored = t == ignore_index;
+    const bool invalid = !ignored && (t < 0 || t >= V);
+    // Ignored rows: gradient 0; invalid target: NaN. Both as a factor on every element.
+    const float g = ignored ? 0.f : (invalid ? NAN : (dloss != nullptr ? dloss[row] : 1.f) * scale);
+    const float l = lse[row];
+    const int32_t tt = (ignored || invalid) ? -1 : static_cast<int32_t>(t);
+    auto grad = [&](float zv, int32_t j) {
+        const float p = __builtin_amdgcn_exp2f((zv - l) * kLog2e);
+        return g * (j == tt ? p - 1.f : p);
+    };
+
+    if (chunk == 0)
+        for (int32_t j = threadIdx.x; j < sp.head; j += WG) dr[j] = from_f32<T>(grad(to_f32(zr[j]), j));
+    if (chunk == S - 1)
+        for (int32_t j = sp.tail + threadIdx.x; j < V; j += WG) dr[j] = from_f32<T>(grad(to_f32(zr[j]), j));
+
+    const RV *zv = reinterpret_cast<const RV *>(zr + sp.head);
+    T *dv = dr + sp.head;
+    for (int32_t base = v0; base < v1; base += WG * U) {
+        RV raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t v = base + u * WG + threadIdx.x;
+            raw[u] = load_stream_raw<T>(reinterpret_cast<const T *>(zv + (v < v1 ? v : v0)));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t v = base + u * WG + threadIdx.x;
+            if (v < v1) {
+                float x[VE], o[VE];
+                widen<T>(raw[u], x);
+                const int32_t j0 = sp.head + v * VE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) o[e] = grad(x[e], j0 + e);
+                store_stream<T>(dv + static_cast<int64_t>(v) * VE, o);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launch geometry.
+// ------------------------------------------------------------------------------------------
+constexpr int kXentWG = 256;
+constexpr int kXentU = 4;
+constexpr int64_t kXentTargetBlocks = 1024;  // split rows until about this many workgroups
+
+// Chunks per row: 1 when there are enough rows, else enough to reach kXentTargetBlocks
+// workgroups while every chunk keeps at least one full iteration (WG * U vectors).
+static int32_t xent_chunks(int64_t N, int64_t V, size_t es) {
+    if (N <= 0) return 1;
+    if (N >= kXentTargetBlocks / 2) return 1;
+    const int64_t nvec = static_cast<int64_t>(V) * static_cast<int64_t>(es) / 16;
+    int64_t S = (kXentTargetBlocks + N - 1) / N;
+    const int64_t maxS = nvec / (kXentWG * kXentU);
+    if (S > maxS) S = maxS;
+    if (S < 1) S = 1;
+    if (S > 1024) S = 1024;
+    return static_cast<int32_t>(S);
+}
+
+static bool xent_shape_ok(int64_t N, int64_t V) {
+    return N >= 0 && N <= INT32_MAX && V >= 1 && V <= INT32_MAX / 2;
+}
+
+}  // namespace lnr
+
+using namespace lnr;
+
+extern "C" size_t cross_entropy_fw_workspace_bytes(int64_t N, int64_t V, lnr_dtype dtype) {
+    if (!valid_dtype(dtype) || !xent_shape_ok(N, V)) return 0;
+    const int32_t S = xent_chunks(N, V, dtype_size(dtype));
+    return S > 1 ? static_cast<size_t>(N) * static_cast<size_t>(S) * 2 * sizeof(float) : 0;
+}
+
+extern "C" int cross_entropy_fw(float *loss, float *lse, const void *logits, const int64_t *target,
+                                int64_t N, int64_t V, int64_t ignore_index, lnr_dtype dtype,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (N < 0 || V < 1) return LNR_ERR_SHAPE;
+    if (!xent_shape_ok(N, V)) return LNR_ERR_UNSUPPORTED;
+    if (N == 0) return LNR_OK;
+    if (loss == nullptr || lse == nullptr || logits == nullptr || target == nullptr)
+        return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned_to(logits, es) || !aligned_to(loss, 4) || !aligned_to(lse, 4) ||
+        !aligned_to(target, 8))
+        return LNR_ERR_ALIGN;
+    const size_t need = cross_entropy_fw_workspace_bytes(N, V, dtype);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LNR_ERR_WORKSPACE;
+    if (need > 0 && !aligned_to(workspace, 8)) return LNR_ERR_ALIGN;
+    const size_t zb = static_cast<size_t>(N) * static_cast<size_t>(V) * es;
+    const size_t nb = static_cast<size_t>(N) * 4;
+    if (overlap(loss, nb, lse, nb) || overlap(loss, nb, logits, zb) || overlap(lse, nb, logits, zb) ||
+        overlap(loss, nb, target, N * 8) || overlap(lse, nb, target, N * 8) ||
+        overlap(workspace, need, logits, zb) || overlap(workspace, need, loss, nb) ||
+        overlap(workspace, need, lse, nb) || overlap(workspace, need, target, N * 8))
+        return LNR_ERR_ALIAS;
+
+    const int32_t S = xent_chunks(N, V, es);
+    const int32_t V32 = static_cast<int32_t>(V);
+    float *part = static_cast<float *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid(static_cast<uint32_t>(N), static_cast<uint32_t>(S));
+    hipError_t e;
+    if (dtype == LNR_F16)
+        e = launch(xent_fw_kernel<f16, kXentWG, kXentU>, grid, dim3(kXentWG), s, loss, lse, part,
+                   static_cast<const f16 *>(logits), target, V32, ignore_index, S, 1);
+    else
+        e = launch(xent_fw_kernel<float, kXentWG, kXentU>, grid, dim3(kXentWG), s, loss, lse, part,
+                   static_cast<const float *>(logits), target, V32, ignore_index, S, 1);
+    if (e == hipSuccess && S > 1) {
+        const dim3 g2(static_cast<uint32_t>((N + 255) / 256));
+        if (dtype == LNR_F16)
+            e = launch(xent_fw_finish<f16>, g2, dim3(256), s, loss, lse,
+                       static_cast<const float *>(part), static_cast<const f16 *>(logits), target, N,
+                       V32, ignore_index, S);
+        else
+            e = launch(xent_fw_finish<float>, g2, dim3(256), s, loss, lse,
+                       static_cast<const float *>(part), static_cast<const float *>(logits), target,
+                       N, V32, ignore_index, S);
+    }
+    return status_of(e);
+}
+
+extern "C" int cross_entropy_bw(void *dlogits, const void *logits, const int64_t *target,
+                                const float *lse, const float *dloss, float scale, int64_t N,
+                                int64_t V, int64_t ignore_index, lnr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (N < 0 || V < 1) return LNR_ERR_SHAPE;
+    if (!xent_shape_ok(N, V)) return LNR_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return LNR_ERR_SHAPE;
+    if (N == 0) return LNR_OK;
+    if (dlogits == nullptr || logits == nullptr || target == nullptr || lse == nullptr)
+        return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned_to(dlogits, es) || !aligned_to(logits, es) || !aligned_to(lse, 4) ||
+        !aligned_to(dloss, 4) || !aligned_to(target, 8))
+        return LNR_ERR_ALIGN;
+    const size_t zb = static_cast<size_t>(N) * static_cast<size_t>(V) * es;
+    const size_t nb = static_cast<size_t>(N) * 4;
+    if (bad_alias(dlogits, logits, zb) || overlap(dlogits, zb, target, N * 8) ||
+        overlap(dlogits, zb, lse, nb) || overlap(dlogits, zb, dloss, nb))
+        return LNR_ERR_ALIAS;
+
+    // Bandwidth needs enough workgroups: split rows as the forward does.
+    const int32_t S = xent_chunks(N, V, es);
+    const int32_t vec_ok =
+        ((reinterpret_cast<uintptr_t>(dlogits) - reinterpret_cast<uintptr_t>(logits)) & 15u) == 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid(static_cast<uint32_t>(N), static_cast<uint32_t>(S));
+    const int32_t V32 = static_cast<int32_t>(V);
+    hipError_t e;
+    if (dtype == LNR_F16)
+        e = launch(xent_bw_kernel<f16, kXentWG, kXentU>, grid, dim3(kXentWG), s,
+                   static_cast<f16 *>(dlogits), static_cast<const f16 *>(logits), target, lse, dloss,
+                   scale, V32, ignore_index, S, vec_ok);
+    else
+        e = launch(xent_bw_kernel<float, kXentWG, kXentU>, grid, dim3(kXentWG), s,
+                   static_cast<float *>(dlogits), static_cast<const float *>(logits), target, lse,
+                   dloss, scale, V32, ignore_index, S, vec_ok);
+    return status_of(e);
+}

@@ -209,6 +209,55 @@ def rmsnorm_sweep_case(N: int, C: int, dtype=torch.float16) -> LayerNormCase:
 
 
 # ------------------------------------------------------------------------------------------
+# Softmax cross-entropy over a vocabulary (the L10 page's third reduce kernel). The pages give
+# no shapes; these stand in for a language-model head: the GPT-2 batch of [FT] section 1
+# (B = 32, T = 256: 8192 tokens) over vocabularies of 10^4 - 10^5 entries, one a multiple of
+# 8 (every fp16 row 16-byte aligned) and one odd (rows start at every 16-byte phase).
+# ------------------------------------------------------------------------------------------
+XENT_VOCABS = (32000, 50001)
+XENT_IGNORE = -100
+
+
+@dataclass
+class XentCase:
+    name: str
+    N: int
+    V: int
+    dtype: torch.dtype
+    logits: torch.Tensor
+    target: torch.Tensor
+    dloss: torch.Tensor
+    ignore_index: int = XENT_IGNORE
+
+
+def xent_case(name, N, V, *, dtype, seed_base, logit_std=2.0, ignore_frac=0.05) -> XentCase:
+    """logits ~ N(0, logit_std^2); targets uniform over [0, V) with about ignore_frac of the
+    rows set to the ignore index (padding tokens); dloss ~ N(0, 1) per row."""
+    logits = normal((N, V), seed_base + K_SCORES, var=logit_std * logit_std)
+    target = torch.randint(0, V, (N,), generator=_gen(seed_base + K_LENGTHS), dtype=torch.int64)
+    pad = torch.rand(N, generator=_gen(seed_base + K_OFFSET)) < ignore_frac
+    target[pad] = XENT_IGNORE
+    dloss = normal((N,), seed_base + K_SDY)
+    return XentCase(name, N, V, dtype, logits.to(dtype), target, dloss)
+
+
+def xent_tokens_case(V: int, dtype=torch.float16, N: int = 8192) -> XentCase:
+    tag = "f16" if dtype == torch.float16 else "f32"
+    v = XENT_VOCABS.index(V) if V in XENT_VOCABS else 9
+    return xent_case(f"xent-{N}x{V}-{tag}", N, V, dtype=dtype, seed_base=seed_of(7, 0, v))
+
+
+def xent_fw_bytes(N, V, s) -> int:
+    """Read logits and int64 targets; write fp32 loss and lse."""
+    return N * V * s + 8 * N + 8 * N
+
+
+def xent_bw_bytes(N, V, s) -> int:
+    """Read logits, int64 targets, fp32 lse and dloss; write dlogits."""
+    return 2 * N * V * s + 8 * N + 8 * N
+
+
+# ------------------------------------------------------------------------------------------
 # Algorithmic bytes: each tensor read or written once, dense (masked positions included).
 # ------------------------------------------------------------------------------------------
 

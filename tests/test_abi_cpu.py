@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -184,6 +184,49 @@ def test_rmsnorm_bw_validation(lib):
     assert rbw(lib, dg=A + 2 ** 30 + 2) == ALIAS             # dgamma over dy
     assert rbw(lib, ws=A + 2 ** 31) == ALIAS                 # workspace over x
     assert lib.rmsnorm_bw_workspace_bytes(0, 64, F16) == 0
+
+
+def xfw(lib, loss=A, lse=A + 2 ** 20, z=A + 2 ** 30, t=A + 2 ** 32, N=64, V=1000, ign=-100,
+        dtype=F16, ws=A + 2 ** 34, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.cross_entropy_fw_workspace_bytes(N, V, dtype)
+    return lib.cross_entropy_fw(loss, lse, z, t, N, V, ign, dtype, ws, ws_bytes, None)
+
+
+def test_cross_entropy_fw_validation(lib):
+    assert xfw(lib, dtype=7) == DTYPE
+    assert xfw(lib, V=0) == SHAPE
+    assert xfw(lib, N=-1) == SHAPE
+    assert xfw(lib, V=2 ** 31) == UNSUP
+    assert xfw(lib, loss=None) == NULL
+    assert xfw(lib, t=None) == NULL
+    assert xfw(lib, t=A + 2 ** 32 + 4) == ALIGN              # int64 targets
+    assert xfw(lib, z=A + 2 ** 30 + 1) == ALIGN
+    assert xfw(lib, lse=A + 64) == ALIAS                     # lse over loss
+    assert xfw(lib, z=A + 2 ** 20 + 8) == ALIAS              # logits over lse
+    need = lib.cross_entropy_fw_workspace_bytes(64, 32000, F16)
+    assert need > 0                                          # 64 rows: split over workgroups
+    assert xfw(lib, V=32000, ws_bytes=need - 8) == WS
+    assert xfw(lib, V=32000, ws=None) == WS
+    assert lib.cross_entropy_fw_workspace_bytes(8192, 32000, F16) == 0   # one workgroup per row
+    assert xfw(lib, N=0) == OK
+
+
+def xbw(lib, dz=A, z=A + 2 ** 30, t=A + 2 ** 32, lse=A + 2 ** 33, dl=None, scale=1.0, N=64,
+        V=1000, ign=-100, dtype=F16):
+    return lib.cross_entropy_bw(dz, z, t, lse, dl, scale, N, V, ign, dtype, None)
+
+
+def test_cross_entropy_bw_validation(lib):
+    assert xbw(lib, dtype=2) == DTYPE
+    assert xbw(lib, V=0) == SHAPE
+    assert xbw(lib, scale=float("inf")) == SHAPE
+    assert xbw(lib, lse=None) == NULL
+    assert xbw(lib, dz=None) == NULL
+    assert xbw(lib, dl=A + 2 ** 33 + 2 ** 20 + 2) == ALIGN
+    assert xbw(lib, z=A + 64) == ALIAS                       # partial overlap of dlogits, logits
+    assert xbw(lib, lse=A + 128) == ALIAS                    # lse inside dlogits
+    assert xbw(lib, N=0) == OK
 
 
 def test_workspace_bytes(lib):
