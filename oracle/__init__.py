@@ -20,6 +20,9 @@ Citations (page titles and sections; see ``lnr_oracle.c`` for the formulas):
     across rows).
   * RMSNorm: "FastTransformer: Breaking the Compiler Ceiling ...", section 5.4 (forward,
     backward recomputing rstd from x, and backward from a given rstd).
+  * Bias + dropout + residual feeding LayerNorm: L10 "Technique 1" (the elementwise kernel
+    "bias + dropout + residual", then the LayerNorm reduce kernel); the dropout keep-mask is
+    an input bit mask.
   * Softmax cross-entropy over a vocabulary: L10 "Technique 1" names the reduce kernel and
     the inference section the whole-vocabulary softmax; no formula is printed, so this is
     the textbook definition (lse - z_target; gradient softmax - onehot), no label smoothing.
@@ -82,6 +85,13 @@ def _load():
     lib.lnr_oracle_xent_fw.restype = None
     lib.lnr_oracle_xent_bw_given_lse.argtypes = [d, pi64, d, d, i64, i64, i64, d]
     lib.lnr_oracle_xent_bw_given_lse.restype = None
+    pu8 = ctypes.POINTER(ctypes.c_uint8)
+    lib.lnr_oracle_bdr_ln_fw.argtypes = [d, d, d, pu8, ctypes.c_double, d, d, i64, i64,
+                                         ctypes.c_double, d, d, d, d]
+    lib.lnr_oracle_bdr_ln_fw.restype = None
+    lib.lnr_oracle_bdr_ln_bw.argtypes = [d, d, d, pu8, ctypes.c_double, d, d, d, i64, i64,
+                                         d, d, d, d, d]
+    lib.lnr_oracle_bdr_ln_bw.restype = None
     lib.lnr_oracle_threads.argtypes = []
     lib.lnr_oracle_threads.restype = ctypes.c_int
     lib.lnr_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -287,3 +297,51 @@ def xent_bw(z, target, dloss, ignore_index: int = -100):
     """Gradient with lse recomputed from z in fp64."""
     _, lse = xent_fw(z, target, ignore_index)
     return xent_bw_given_lse(z, target, lse, dloss, ignore_index)
+
+
+def _u8(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=np.uint8)
+
+
+def bdr_ln_fw(x, residual, bias, mask_bits, p, gamma, beta, eps: float = 1e-8):
+    """s = residual + keep * (x + bias) / (1 - p), y = LayerNorm(s). mask_bits: uint8
+    [N, ceil(C/8)], bit j % 8 of byte j / 8 keeps element j. Returns (s, y, mean, rstd)."""
+    x = _f64(x)
+    N, C = x.shape
+    r = _f64(residual).reshape(N, C)
+    b = _f64(bias).reshape(C)
+    m = _u8(mask_bits).reshape(N, (C + 7) // 8)
+    g = _f64(gamma).reshape(C)
+    be = _f64(beta).reshape(C)
+    s = np.empty_like(x)
+    y = np.empty_like(x)
+    mean = np.empty(N, np.float64)
+    rstd = np.empty(N, np.float64)
+    _load().lnr_oracle_bdr_ln_fw(_p(x), _p(r), _p(b), m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                 float(p), _p(g), _p(be), N, C, float(eps), _p(s), _p(y), _p(mean),
+                                 _p(rstd))
+    return s, y, mean, rstd
+
+
+def bdr_ln_bw(s, dy, ds_extra, mask_bits, p, gamma, mean, rstd):
+    """Backward from the saved s, mean, rstd. ds_extra may be None. Returns
+    (dresidual, dx, dgamma, dbeta, dbias)."""
+    s = _f64(s)
+    N, C = s.shape
+    dy = _f64(dy).reshape(N, C)
+    de = None if ds_extra is None else _f64(ds_extra).reshape(N, C)
+    m = _u8(mask_bits).reshape(N, (C + 7) // 8)
+    g = _f64(gamma).reshape(C)
+    mu = _f64(mean).reshape(N)
+    rs = _f64(rstd).reshape(N)
+    dres = np.empty_like(s)
+    dx = np.empty_like(s)
+    dg = np.empty(C, np.float64)
+    db = np.empty(C, np.float64)
+    dbias = np.empty(C, np.float64)
+    _load().lnr_oracle_bdr_ln_bw(_p(s), _p(dy), None if de is None else _p(de),
+                                 m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), float(p), _p(g),
+                                 _p(mu), _p(rs), N, C, _p(dres), _p(dx), _p(dg), _p(db), _p(dbias))
+    return dres, dx, dg, db, dbias

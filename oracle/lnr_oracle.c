@@ -27,7 +27,8 @@
  *   [FT]   "FastTransformer: Breaking the Compiler Ceiling via Architectural Co-Design",
  *          section 5.4 "Vectorized Pre-RMSNorm" (RMSNorm: no mean, one sum of squares).
  *   [L10]  section "Technique 1: kernel fusion, leaving only GEMMs to cuBLAS" (cross entropy
- *          is one of the custom reduce kernels) and "Inference: making beam search skip a
+ *          is one of the custom reduce kernels; "bias + dropout + residual" one of the
+ *          elementwise kernels, followed by LayerNorm) and "Inference: making beam search skip a
  *          sort" (a softmax over the whole vocabulary). The pages give no formula; the
  *          oracle is the textbook softmax cross-entropy (no label smoothing).
  * The softmax backward formula is never printed on the pages; it is the textbook Jacobian
@@ -383,6 +384,79 @@ ORACLE_API void lnr_oracle_rmsnorm_bw_given_rstd(const double *x, const double *
         for (int64_t i = 0; i < N; ++i)
             for (int64_t j = jb; j < je; ++j)
                 dgamma[j] += dy[i * C + j] * (x[i * C + j] * rstd[i]);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Bias + dropout + residual, then LayerNorm. [L10 "Technique 1": "bias + dropout + residual"
+ * is one of the elementwise kernels between the GEMMs, and LayerNorm follows it in the layer]
+ * The dropout draws are an input: keep_ij is bit (j % 8) of mask[i * ceil(C/8) + j / 8]
+ * (least significant bit first), p the drop probability (0 <= p < 1).
+ *   s_ij = residual_ij + keep_ij * (x_ij + bias_j) / (1 - p)
+ *   y    = LayerNorm(s) with gamma, beta, eps (two-pass statistics, as above)
+ * Outputs s, y and the per-row mean and 1/sigma of s.
+ * ------------------------------------------------------------------------------------- */
+static int keep_bit(const unsigned char *mask, int64_t i, int64_t j, int64_t C)
+{
+    const int64_t mb = (C + 7) / 8;
+    return (mask[i * mb + j / 8] >> (j % 8)) & 1;
+}
+
+ORACLE_API void lnr_oracle_bdr_ln_fw(const double *x, const double *residual, const double *bias,
+                                     const unsigned char *mask, double p, const double *gamma,
+                                     const double *beta, int64_t N, int64_t C, double eps,
+                                     double *s, double *y, double *mean, double *rstd)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i) {
+        double *sr = s + i * C;
+        for (int64_t j = 0; j < C; ++j)
+            sr[j] = residual[i * C + j] +
+                    (keep_bit(mask, i, j, C) ? (x[i * C + j] + bias[j]) / (1.0 - p) : 0.0);
+        double mu = 0.0;
+        for (int64_t j = 0; j < C; ++j)
+            mu += sr[j];
+        mu /= (double)C;
+        double q = 0.0;
+        for (int64_t j = 0; j < C; ++j)
+            q += (sr[j] - mu) * (sr[j] - mu);
+        const double sigma = sqrt(q / (double)C + eps);
+        for (int64_t j = 0; j < C; ++j)
+            y[i * C + j] = gamma[j] * ((sr[j] - mu) / sigma) + beta[j];
+        mean[i] = mu;
+        rstd[i] = 1.0 / sigma;
+    }
+}
+
+/* Backward of the fused op from the saved s, mean and rstd. dy is the gradient of y; ds_extra
+ * (may be NULL) is a gradient reaching s by another path. With ds the LayerNorm input
+ * gradient (the given-statistics formula above) plus ds_extra:
+ *   dresidual = ds,   dx_ij = ds_ij * keep_ij / (1 - p),   dbias_j = sum_i dx_ij,
+ *   dgamma_j = sum_i dy_ij * shat_ij,   dbeta_j = sum_i dy_ij,  shat = (s - mean) * rstd. */
+ORACLE_API void lnr_oracle_bdr_ln_bw(const double *s, const double *dy, const double *ds_extra,
+                                     const unsigned char *mask, double p, const double *gamma,
+                                     const double *mean, const double *rstd, int64_t N, int64_t C,
+                                     double *dresidual, double *dx, double *dgamma,
+                                     double *dbeta, double *dbias)
+{
+    /* ds from the LayerNorm backward on the saved statistics */
+    lnr_oracle_layernorm_bw_given_stats(s, dy, gamma, mean, rstd, N, C, dresidual, dgamma, dbeta);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t j = 0; j < C; ++j) {
+            const double ds = dresidual[i * C + j] + (ds_extra ? ds_extra[i * C + j] : 0.0);
+            dresidual[i * C + j] = ds;
+            dx[i * C + j] = keep_bit(mask, i, j, C) ? ds / (1.0 - p) : 0.0;
+        }
+    const int64_t blk = 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t jb = 0; jb < C; jb += blk) {
+        const int64_t je = (jb + blk < C) ? jb + blk : C;
+        for (int64_t j = jb; j < je; ++j)
+            dbias[j] = 0.0;
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = jb; j < je; ++j)
+                dbias[j] += dx[i * C + j];
     }
 }
 
