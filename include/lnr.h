@@ -205,6 +205,54 @@ LNR_API int rmsnorm_bw(void *dx, void *dgamma, const void *dy, const void *x, co
                        size_t workspace_bytes, void *stream);
 
 /*
+ * bdr_layernorm_fw -- bias + dropout + residual, then LayerNorm, in one pass over the rows.
+ * ["CMU 11-868 L10 ...", section "Technique 1": "bias + dropout + residual" is one of the
+ *  elementwise kernels between the GEMMs, and LayerNorm the reduce kernel that follows.
+ *  The page gives no RNG or dropout rule: the dropout draws are an input bit mask.]
+ *
+ *   s_ij = residual_ij + keep_ij * (x_ij + bias_j) / (1 - p)
+ *   y    = LayerNorm(s) with gamma, beta, eps (as layernorm_fw; s normalised in fp32)
+ *   keep_ij = bit (j % 8) of keep_mask[i * ceil(C/8) + j / 8], least significant bit first.
+ *
+ *   s      [N, C] dtype, written (the residual stream); may equal residual (in place).
+ *   y      [N, C] dtype, written. mean, rstd [N] float32 of s, written, or both NULL.
+ *   x, residual [N, C] dtype, read. bias, gamma, beta [C] dtype, read.
+ *   keep_mask [N, ceil(C/8)] bytes, read.  p  drop probability, 0 <= p < 1.
+ *   Vector path only: C a multiple of 8 (fp16) or 4 (fp32) -- else LNR_ERR_UNSUPPORTED --
+ *   and every [N, C] and [C] buffer 16-byte aligned -- else LNR_ERR_ALIGN. 1 <= C <= 8192.
+ */
+LNR_API int bdr_layernorm_fw(void *s, void *y, float *mean, float *rstd, const void *x,
+                             const void *residual, const void *bias, const uint8_t *keep_mask,
+                             float p, const void *gamma, const void *beta, int64_t N, int64_t C,
+                             float eps, lnr_dtype dtype, void *stream);
+
+/*
+ * bdr_layernorm_bw_workspace_bytes -- device workspace bdr_layernorm_bw needs: per-block
+ * column partials of dgamma, dbeta and dbias. 0 for N = 0 or an invalid shape/dtype.
+ */
+LNR_API size_t bdr_layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype);
+
+/*
+ * bdr_layernorm_bw -- backward of bdr_layernorm_fw from the saved s, mean and rstd.
+ *   ds        = LayerNorm input gradient of dy (as layernorm_bw) + ds_extra
+ *   dresidual = ds,   dx = keep * ds / (1 - p),   dbias_j = sum_i dx_ij,
+ *   dgamma_j = sum_i dy_ij * shat_ij,   dbeta_j = sum_i dy_ij,  shat = (s - mean) * rstd.
+ *
+ *   dresidual, dx [N, C] dtype, written; dresidual may equal dy or ds_extra (in place); dx
+ *   overlaps nothing.  dgamma, dbeta, dbias [C] dtype, written.
+ *   dy, s [N, C] dtype, read.  ds_extra [N, C] dtype, read, or NULL (no other path into s).
+ *   keep_mask, p as in the forward.  gamma [C] dtype; mean, rstd [N] float32, read.
+ *   workspace  bdr_layernorm_bw_workspace_bytes(N, C, dtype) bytes, 8-byte aligned, caller
+ *   owned; contents on entry do not matter. Same vector-path limits as the forward.
+ */
+LNR_API int bdr_layernorm_bw(void *dresidual, void *dx, void *dgamma, void *dbeta, void *dbias,
+                             const void *dy, const void *ds_extra, const void *s,
+                             const uint8_t *keep_mask, float p, const void *gamma,
+                             const float *mean, const float *rstd, int64_t N, int64_t C,
+                             lnr_dtype dtype, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
  * cross_entropy_fw_workspace_bytes -- device workspace cross_entropy_fw needs for (N, V,
  * dtype): per-chunk partial (max, sum) pairs when there are too few rows to fill the GPU and
  * each row is split over several workgroups; 0 when rows are not split (the common case of

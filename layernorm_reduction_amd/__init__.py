@@ -21,6 +21,11 @@ Functions mirror the C entry points:
     cross_entropy_bw(logits, target, lse, dloss=None, scale=1.0, ignore_index=-100,
                      dlogits=None) -> dlogits
     cross_entropy_fw_workspace_bytes(N, V, dtype) -> int
+    bdr_layernorm_fw(x, residual, bias, keep_mask, p, gamma, beta, eps=1e-8, s=None, y=None,
+                     mean=None, rstd=None) -> (s, y, mean, rstd)
+    bdr_layernorm_bw(dy, s, keep_mask, p, gamma, mean, rstd, ds_extra=None, ...)
+                     -> (dresidual, dx, dgamma, dbeta, dbias)
+    bdr_layernorm_bw_workspace_bytes(N, C, dtype) -> int
 """
 from __future__ import annotations
 
@@ -31,7 +36,8 @@ __all__ = [
     "LnrError", "load", "library_path", "attn_softmax_fw", "attn_softmax_bw", "layernorm_fw",
     "layernorm_bw", "layernorm_bw_workspace_bytes", "rmsnorm_fw", "rmsnorm_bw",
     "rmsnorm_bw_workspace_bytes", "cross_entropy_fw", "cross_entropy_bw",
-    "cross_entropy_fw_workspace_bytes", "copy_bytes", "xor_bytes", "softmax_plan",
+    "cross_entropy_fw_workspace_bytes", "bdr_layernorm_fw", "bdr_layernorm_bw",
+    "bdr_layernorm_bw_workspace_bytes", "copy_bytes", "xor_bytes", "softmax_plan",
     "layernorm_plan", "LNR_F32", "LNR_F16", "SOFTMAX_MAX_TK", "LAYERNORM_MAX_C",
 ]
 
@@ -83,6 +89,12 @@ def load():
     lib.rmsnorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
     lib.rmsnorm_bw_workspace_bytes.restype = sz
     lib.rmsnorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
+    fl = ctypes.c_float
+    lib.bdr_layernorm_fw.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, fl, vp, vp, i64, i64, fl, ci, vp]
+    lib.bdr_layernorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
+    lib.bdr_layernorm_bw_workspace_bytes.restype = sz
+    lib.bdr_layernorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, fl, vp, vp, vp, i64, i64,
+                                     ci, vp, sz, vp]
     lib.cross_entropy_fw_workspace_bytes.argtypes = [i64, i64, ci]
     lib.cross_entropy_fw_workspace_bytes.restype = sz
     lib.cross_entropy_fw.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, sz, vp]
@@ -98,7 +110,8 @@ def load():
     lib.lnr_softmax_plan.argtypes = [i64, ci, ci, ip, ip, ip]
     lib.lnr_layernorm_plan.argtypes = [i64, i64, ci, ci, ip, ip, ip, ip, ctypes.POINTER(i64)]
     for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw", "rmsnorm_fw",
-              "rmsnorm_bw", "cross_entropy_fw", "cross_entropy_bw", "lnr_copy",
+              "rmsnorm_bw", "cross_entropy_fw", "cross_entropy_bw", "bdr_layernorm_fw",
+              "bdr_layernorm_bw", "lnr_copy",
               "lnr_xor2", "lnr_softmax_plan", "lnr_layernorm_plan"):
         getattr(lib, f).restype = ci
     _lib = lib
@@ -362,6 +375,89 @@ def rmsnorm_bw(dy, x, gamma, rstd, dx=None, dgamma=None, workspace=None):
     return dx, dgamma
 
 
+def _keep_mask(keep_mask, N, C, like):
+    torch = _torch()
+    if not keep_mask.is_cuda or keep_mask.device != like.device:
+        raise ValueError("keep_mask must be on the same GPU as x")
+    if keep_mask.dtype != torch.uint8 or not keep_mask.is_contiguous() or \
+            keep_mask.numel() != N * ((C + 7) // 8):
+        raise ValueError("keep_mask must be a contiguous uint8 tensor of N * ceil(C/8) bytes")
+
+
+def bdr_layernorm_bw_workspace_bytes(N: int, C: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (LNR_F16 if str(dtype).endswith("float16") else LNR_F32)
+    return int(load().bdr_layernorm_bw_workspace_bytes(int(N), int(C), code))
+
+
+def bdr_layernorm_fw(x, residual, bias, keep_mask, p, gamma, beta, eps: float = 1e-8, s=None,
+                     y=None, mean=None, rstd=None):
+    """s = residual + keep * (x + bias) / (1 - p); y = LayerNorm(s). keep_mask: uint8
+    [N, ceil(C/8)], bit j % 8 of byte j / 8 keeps element j. Returns (s, y, mean, rstd)."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [N, C]")
+    N, C = x.shape
+    _dev(residual, "residual", like=x)
+    if residual.shape != x.shape:
+        raise ValueError("residual must have the shape of x")
+    for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        _dev(t, nm, like=x)
+        if t.numel() != C:
+            raise ValueError(f"{nm} must have C elements")
+    _keep_mask(keep_mask, N, C, x)
+    s = torch.empty_like(x) if s is None else s
+    y = torch.empty_like(x) if y is None else y
+    _dev(s, "s", like=x)
+    _dev(y, "y", like=x)
+    if mean is None:
+        mean = torch.empty(N, dtype=torch.float32, device=x.device)
+    if rstd is None:
+        rstd = torch.empty(N, dtype=torch.float32, device=x.device)
+    _f32(mean, "mean", x)
+    _f32(rstd, "rstd", x)
+    st = load().bdr_layernorm_fw(_ptr(s), _ptr(y), _ptr(mean), _ptr(rstd), _ptr(x), _ptr(residual),
+                                 _ptr(bias), _ptr(keep_mask), float(p), _ptr(gamma), _ptr(beta), N,
+                                 C, float(eps), _dtype_code(x), _stream(x))
+    _check(st, "bdr_layernorm_fw")
+    return s, y, mean, rstd
+
+
+def bdr_layernorm_bw(dy, s, keep_mask, p, gamma, mean, rstd, ds_extra=None, dresidual=None,
+                     dx=None, dgamma=None, dbeta=None, dbias=None, workspace=None):
+    """Backward of bdr_layernorm_fw from the saved s, mean, rstd; ds_extra is a gradient
+    reaching s by another path (None: none). Returns (dresidual, dx, dgamma, dbeta, dbias)."""
+    torch = _torch()
+    _dev(s, "s")
+    if s.dim() != 2:
+        raise ValueError("s must be [N, C]")
+    N, C = s.shape
+    _dev(dy, "dy", like=s)
+    if dy.shape != s.shape:
+        raise ValueError("dy must have the shape of s")
+    if ds_extra is not None:
+        _dev(ds_extra, "ds_extra", like=s)
+    _dev(gamma, "gamma", like=s)
+    _keep_mask(keep_mask, N, C, s)
+    _f32(mean, "mean", s)
+    _f32(rstd, "rstd", s)
+    dresidual = torch.empty_like(s) if dresidual is None else dresidual
+    dx = torch.empty_like(s) if dx is None else dx
+    dgamma = torch.empty(C, dtype=s.dtype, device=s.device) if dgamma is None else dgamma
+    dbeta = torch.empty(C, dtype=s.dtype, device=s.device) if dbeta is None else dbeta
+    dbias = torch.empty(C, dtype=s.dtype, device=s.device) if dbias is None else dbias
+    code = _dtype_code(s)
+    need = int(load().bdr_layernorm_bw_workspace_bytes(N, C, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s.device)
+    st = load().bdr_layernorm_bw(_ptr(dresidual), _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(dbias),
+                                 _ptr(dy), _ptr(ds_extra), _ptr(s), _ptr(keep_mask), float(p),
+                                 _ptr(gamma), _ptr(mean), _ptr(rstd), N, C, code, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(s))
+    _check(st, "bdr_layernorm_bw")
+    return dresidual, dx, dgamma, dbeta, dbias
+
+
 def _targets(target, N, like):
     torch = _torch()
     if not target.is_cuda or target.device != like.device:
@@ -520,6 +616,30 @@ def bind_layernorm_bw(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace):
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(x))
     return BoundCall("layernorm_bw", load().layernorm_bw, args,
                      (dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace))
+
+
+def bind_bdr_layernorm_fw(x, residual, bias, keep_mask, p, gamma, beta, eps, s, y, mean, rstd):
+    bdr_layernorm_fw(x, residual, bias, keep_mask, p, gamma, beta, eps, s, y, mean, rstd)
+    N, C = x.shape
+    args = (s.data_ptr(), y.data_ptr(), mean.data_ptr(), rstd.data_ptr(), x.data_ptr(),
+            residual.data_ptr(), bias.data_ptr(), keep_mask.data_ptr(), float(p), gamma.data_ptr(),
+            beta.data_ptr(), N, C, float(eps), _dtype_code(x), _stream(x))
+    return BoundCall("bdr_layernorm_fw", load().bdr_layernorm_fw, args,
+                     (x, residual, bias, keep_mask, gamma, beta, s, y, mean, rstd))
+
+
+def bind_bdr_layernorm_bw(dy, s, keep_mask, p, gamma, mean, rstd, ds_extra, dresidual, dx, dgamma,
+                          dbeta, dbias, workspace):
+    bdr_layernorm_bw(dy, s, keep_mask, p, gamma, mean, rstd, ds_extra, dresidual, dx, dgamma, dbeta,
+                     dbias, workspace)
+    N, C = s.shape
+    args = (dresidual.data_ptr(), dx.data_ptr(), dgamma.data_ptr(), dbeta.data_ptr(), dbias.data_ptr(),
+            dy.data_ptr(), _ptr(ds_extra), s.data_ptr(), keep_mask.data_ptr(), float(p),
+            gamma.data_ptr(), mean.data_ptr(), rstd.data_ptr(), N, C, _dtype_code(s),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(s))
+    return BoundCall("bdr_layernorm_bw", load().bdr_layernorm_bw, args,
+                     (dy, s, keep_mask, gamma, mean, rstd, ds_extra, dresidual, dx, dgamma, dbeta,
+                      dbias, workspace))
 
 
 def bind_cross_entropy_fw(logits, target, ignore_index, loss, lse, workspace):

@@ -27,6 +27,9 @@
 //     reduction (sum of x^2 forward, sum of gamma*dy*xhat backward), no beta and no dbeta.
 #include <math.h>
 
+#include <initializer_list>
+#include <type_traits>
+
 #include "lnr_common.h"
 #include "lnr_prims.h"
 
@@ -49,6 +52,26 @@ __device__ __forceinline__ float ln_stats(float s1, float s2, int C, float eps, 
     return 1.0f / sqrtf(var + eps);
 }
 
+// What the row kernels normalise.
+enum NormMode : int {
+    kLayerNorm = 0,     // y = LayerNorm(x)
+    kRmsNorm = 1,       // y = RMSNorm(x)
+    kBdrLayerNorm = 2,  // s = residual + keep * (x + bias) * keep_scale; y = LayerNorm(s)
+};
+
+// Keep bits of vector c of a row: mask bytes hold one bit per element, least significant
+// bit first; a 16-byte vector covers 8 fp16 elements (one byte) or 4 fp32 elements (half a
+// byte).
+template <typename T>
+__device__ __forceinline__ uint32_t keep_bits(const uint8_t *mrow, int c) {
+    if constexpr (Vec16<T>::N == 8) {
+        return mrow[c];
+    } else {
+        const uint32_t b = mrow[c >> 1];
+        return (c & 1) ? (b >> 4) : (b & 15u);
+    }
+}
+
 // RMSNorm statistic: rstd = 1 / sqrt(mean(x^2) + eps), from the one sum of squares.
 __device__ __forceinline__ float rms_stats(float s2, int C, float eps) {
 #pragma clang fp contract(off)
@@ -62,14 +85,23 @@ __device__ __forceinline__ float rms_stats(float s2, int C, float eps) {
 // current row is reduced, so each wave keeps a row of loads in flight while it computes;
 // the fetch is issued unconditionally (an idle lane reads a vector that always exists) so
 // that no branch makes the compiler drain the loads early.
+// kBdrLayerNorm: the row is s = residual + keep * (x + bias) * keep_scale, formed in fp32 from
+// x, residual and the row's mask bytes, written to s_out (the residual stream), and
+// normalised in fp32.
 // ------------------------------------------------------------------------------------------
-template <typename T, int G, int IT, int WG, bool RMS>
+template <typename T, int G, int IT, int WG, int MODE>
 __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__ mean,
                                                        float *__restrict__ rstd, const T *x,
                                                        const T *__restrict__ gamma,
                                                        const T *__restrict__ beta, int64_t N,
                                                        int32_t C, float eps,
-                                                       int64_t rows_per_block) {
+                                                       int64_t rows_per_block, T *s_out,
+                                                       const T *residual,
+                                                       const T *__restrict__ bias,
+                                                       const uint8_t *__restrict__ mask,
+                                                       float keep_scale) {
+    constexpr bool RMS = MODE == kRmsNorm;
+    constexpr bool BDR = MODE == kBdrLayerNorm;
     using RV = RawVec<T>;
     constexpr int V = Vec16<T>::N;
     constexpr int NG = WG / G;
@@ -81,28 +113,46 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
     const int64_t r1 = (r0 + rows_per_block < N) ? r0 + rows_per_block : N;
     const RV zero = {};
 
-    float gm[IT][V], bt[IT][RMS ? 1 : V];
+    const int64_t mb = (C + 7) / 8;  // mask bytes per row
+    float gm[IT][V], bt[IT][RMS ? 1 : V], bs[IT][BDR ? V : 1];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
         const int cc = c < nvec ? c : 0;
         widen<T>(load_keep_raw<T>(gamma + cc * V), gm[k]);
         if constexpr (!RMS) widen<T>(load_keep_raw<T>(beta + cc * V), bt[k]);
+        if constexpr (BDR) widen<T>(load_keep_raw<T>(bias + cc * V), bs[k]);
     }
+    // The shift K of a kBdrLayerNorm row is its first s element, formed from the inputs.
+    float b0 = 0.f;
+    if constexpr (BDR) b0 = to_f32(bias[0]);
 
     const int64_t iters = (rows_per_block + NG - 1) / NG;
-    RV xn[IT];
+    RV xn[IT], rn[BDR ? IT : 1];
+    uint32_t kn[BDR ? IT : 1];
     float Kn;
     auto fetch = [&](int64_t row, bool live) {
         const int64_t rbase = (live ? row : r0) * static_cast<int64_t>(C);
+        const uint8_t *mrow = BDR ? mask + (live ? row : r0) * mb : nullptr;
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int c = k * G + lane;
             const bool ok = live && c < nvec;
-            const RV l = load_stream_raw<T>(x + rbase + (ok ? static_cast<int64_t>(c) * V : 0));
+            const int64_t off = rbase + (ok ? static_cast<int64_t>(c) * V : 0);
+            const RV l = load_stream_raw<T>(x + off);
             xn[k] = ok ? l : zero;
+            if constexpr (BDR) {
+                const RV lr = load_stream_raw<T>(residual + off);
+                const uint32_t kb = keep_bits<T>(mrow, ok ? c : 0);
+                rn[k] = ok ? lr : zero;
+                kn[k] = ok ? kb : 0u;
+            }
         }
-        if constexpr (!RMS) {
+        if constexpr (BDR) {
+            const float x0 = to_f32(x[rbase]), r0v = to_f32(residual[rbase]);
+            const float s0 = r0v + ((mrow[0] & 1u) ? (x0 + b0) * keep_scale : 0.f);
+            Kn = live ? s0 : 0.f;
+        } else if constexpr (!RMS) {
             const float kl = to_f32(x[rbase]);  // the shift: one broadcast load per group
             Kn = live ? kl : 0.f;
         } else {
@@ -113,9 +163,16 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
     for (int64_t it = 0; it < iters; ++it) {
         const int64_t row = r0 + it * NG + grp;
         const bool live = row < r1;
-        RV xc[IT];
+        RV xc[IT], rc[BDR ? IT : 1];
+        uint32_t kc[BDR ? IT : 1];
 #pragma unroll
-        for (int k = 0; k < IT; ++k) xc[k] = xn[k];
+        for (int k = 0; k < IT; ++k) {
+            xc[k] = xn[k];
+            if constexpr (BDR) {
+                rc[k] = rn[k];
+                kc[k] = kn[k];
+            }
+        }
         const float K = Kn;
         fetch(row + NG, it + 1 < iters && row + NG < r1);
 
@@ -125,6 +182,16 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
         for (int k = 0; k < IT; ++k) {
             widen<T>(xc[k], d[k]);
             const bool ok = k * G + lane < nvec;
+            if constexpr (BDR) {
+                float rf[V];
+                widen<T>(rc[k], rf);
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    d[k][e] = rf[e] + (((kc[k] >> e) & 1u) ? (d[k][e] + bs[k][e]) * keep_scale : 0.f);
+                const int c = k * G + lane;
+                if (live && c < nvec)
+                    store_stream<T>(s_out + row * static_cast<int64_t>(C) + static_cast<int64_t>(c) * V, d[k]);
+            }
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 d[k][e] = ok ? d[k][e] - K : 0.f;
@@ -167,16 +234,25 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
 // Backward, vector path: dx plus per-workgroup dgamma/dbeta column partials.
 // part layout: [P][2][C] of Accum<T>; slot 0 = dgamma, slot 1 = dbeta (unused for RMSNorm).
 // ------------------------------------------------------------------------------------------
-template <typename T, int G, int IT, int WG, int DEPTH, bool RMS>
+template <typename T, int G, int IT, int WG, int DEPTH, int MODE>
 __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>::type *part,
                                                        const T *dy, const T *x,
                                                        const T *__restrict__ gamma,
                                                        const float *__restrict__ mean,
                                                        const float *__restrict__ rstd,
                                                        int64_t N, int32_t C,
-                                                       int64_t rows_per_block) {
+                                                       int64_t rows_per_block, T *dx2,
+                                                       const T *ds_extra,
+                                                       const uint8_t *__restrict__ mask,
+                                                       float keep_scale) {
 #pragma clang fp contract(off)
     static_assert(DEPTH == 1 || DEPTH == 2, "rows fetched ahead: 1 or 2");
+    // kBdrLayerNorm: x is the saved s; dx receives ds = (LayerNorm input gradient) + ds_extra
+    // (the residual gradient), dx2 = keep * ds * keep_scale (the gradient of x), and a third
+    // column partial accumulates dbias = sum over rows of dx2.
+    constexpr bool RMS = MODE == kRmsNorm;
+    constexpr bool BDR = MODE == kBdrLayerNorm;
+    constexpr int SLOTS = BDR ? 3 : 2;
     using A = typename Accum<T>::type;
     using RV = RawVec<T>;
     constexpr int V = Vec16<T>::N;
@@ -198,7 +274,7 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     const RV zero = {};
 
     RV gmr[IT];  // gamma, kept as stored (16 bytes per vector) to save registers
-    A adg[IT][V], adb[IT][RMS ? 1 : V];
+    A adg[IT][V], adb[IT][RMS ? 1 : V], adx[IT][BDR ? V : 1];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
@@ -208,8 +284,10 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
         for (int e = 0; e < V; ++e) {
             adg[k][e] = A(0);
             if constexpr (!RMS) adb[k][e] = A(0);
+            if constexpr (BDR) adx[k][e] = A(0);
         }
     }
+    const int64_t mb = (C + 7) / 8;  // mask bytes per row
 
     // A row buffer holds one row's x and dy vectors (as stored) plus its mean and rstd.
     // DEPTH rows are fetched ahead of the one being reduced, so every wave keeps DEPTH rows
@@ -221,6 +299,7 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     // can use barriers.
     struct RowBuf {
         RV xv[IT], dv[IT];
+        uint32_t kb[BDR ? IT : 1];
         float mu, rs;
     };
     const int64_t iters = (rows_per_block + NG - 1) / NG;
@@ -238,6 +317,10 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
             const RV dl = load_stream_raw<T>(dy + off);
             b.xv[k] = ok ? xl : zero;
             b.dv[k] = ok ? dl : zero;
+            if constexpr (BDR) {
+                const uint32_t kl = keep_bits<T>(mask + (live ? row : first_row) * mb, ok ? c : 0);
+                b.kb[k] = ok ? kl : 0u;
+            }
         }
         const int64_t srow = live ? row : first_row;
         const float rl = rstd[srow];
@@ -296,6 +379,21 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
                     else
                         o[e] = rs * __builtin_fmaf(-xh[k][e], bb, gv[k][e] - a);
                 }
+                if constexpr (BDR) {
+                    if (ds_extra != nullptr) {
+                        float ef[V];
+                        load_stream<T>(ds_extra + base + static_cast<int64_t>(c) * V, ef);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) o[e] += ef[e];
+                    }
+                    float o2[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        o2[e] = ((b.kb[k] >> e) & 1u) ? o[e] * keep_scale : 0.f;
+                        adx[k][e] += static_cast<A>(o2[e]);
+                    }
+                    store_stream<T>(dx2 + base + static_cast<int64_t>(c) * V, o2);
+                }
                 store_stream<T>(dx + base + static_cast<int64_t>(c) * V, o);
             }
         }
@@ -323,8 +421,9 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
         }
     }
 
-    A *pg = part + static_cast<int64_t>(blockIdx.x) * 2 * C;
+    A *pg = part + static_cast<int64_t>(blockIdx.x) * SLOTS * C;
     A *pb = pg + C;
+    A *px = pg + 2 * static_cast<int64_t>(C);  // kBdrLayerNorm only
     if constexpr (NG == 1) {
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
@@ -334,6 +433,7 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
                 for (int e = 0; e < V; ++e) {
                     pg[c * V + e] = adg[k][e];
                     if constexpr (!RMS) pb[c * V + e] = adb[k][e];
+                    if constexpr (BDR) px[c * V + e] = adx[k][e];
                 }
             }
         }
@@ -343,11 +443,13 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
 #pragma unroll
-            for (int which = 0; which < (RMS ? 1 : 2); ++which) {
+            for (int which = 0; which < (RMS ? 1 : SLOTS); ++which) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     if constexpr (RMS)
                         tile[grp][lane * V + e] = adg[k][e];
+                    else if constexpr (BDR)
+                        tile[grp][lane * V + e] = which == 0 ? adg[k][e] : (which == 1 ? adb[k][e] : adx[k][e]);
                     else
                         tile[grp][lane * V + e] = which == 0 ? adg[k][e] : adb[k][e];
                 }
@@ -357,7 +459,7 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
 #pragma unroll
                     for (int g = 1; g < NG; ++g) s += tile[g][cc];
                     const int col = k * G * V + cc;
-                    if (col < C) (which == 0 ? pg : pb)[col] = s;
+                    if (col < C) (which == 0 ? pg : (which == 1 ? pb : px))[col] = s;
                 }
                 __syncthreads();
             }
@@ -366,7 +468,8 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
 }
 
 // ------------------------------------------------------------------------------------------
-// Column finalize: dgamma/dbeta = fixed-order sums of the P partial rows.
+// Column finalize: dgamma/dbeta (and dbias) = fixed-order sums of the P partial rows; slot
+// `which` = blockIdx.y of partial row p is at part[(p * stride + which) * C].
 // Block = TILE columns x SLICES slices; slice s sums partials p = s, s+SLICES, s+2*SLICES, ...
 // in that order (with BATCH > 1, BATCH loads in flight at a time, added in order), then slice 0 adds the
 // slice sums in slice order. Two shapes, measured on MI355X: 16 x 16 up to 1024 columns
@@ -375,8 +478,8 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
 // ------------------------------------------------------------------------------------------
 template <typename T, int TILE, int SLICES, int BATCH>
 __global__ __launch_bounds__(TILE *SLICES) void layernorm_bw_colsum(
-    T *__restrict__ dgamma, T *__restrict__ dbeta, const typename Accum<T>::type *__restrict__ part,
-    int32_t P, int32_t C) {
+    T *__restrict__ dgamma, T *__restrict__ dbeta, T *__restrict__ dbias,
+    const typename Accum<T>::type *__restrict__ part, int32_t P, int32_t C, int32_t stride) {
     using A = typename Accum<T>::type;
     __shared__ A slab[SLICES][TILE];
     const int cl = threadIdx.x % TILE;
@@ -388,14 +491,14 @@ __global__ __launch_bounds__(TILE *SLICES) void layernorm_bw_colsum(
         if constexpr (BATCH == 1) {
 #pragma unroll 8
             for (int p = sl; p < P; p += SLICES)
-                s += part[(static_cast<int64_t>(p) * 2 + which) * C + col];
+                s += part[(static_cast<int64_t>(p) * stride + which) * C + col];
         } else {
             for (int p0 = sl; p0 < P; p0 += SLICES * BATCH) {
                 A v[BATCH];
 #pragma unroll
                 for (int u = 0; u < BATCH; ++u) {
                     const int p = p0 + u * SLICES;
-                    v[u] = p < P ? part[(static_cast<int64_t>(p) * 2 + which) * C + col] : A(0);
+                    v[u] = p < P ? part[(static_cast<int64_t>(p) * stride + which) * C + col] : A(0);
                 }
 #pragma unroll
                 for (int u = 0; u < BATCH; ++u)
@@ -409,7 +512,7 @@ __global__ __launch_bounds__(TILE *SLICES) void layernorm_bw_colsum(
         A t = slab[0][cl];
 #pragma unroll
         for (int k = 1; k < SLICES; ++k) t += slab[k][cl];
-        (which == 0 ? dgamma : dbeta)[col] = from_f32<T>(static_cast<float>(t));
+        (which == 0 ? dgamma : (which == 1 ? dbeta : dbias))[col] = from_f32<T>(static_cast<float>(t));
     }
 }
 
@@ -548,6 +651,24 @@ template <> struct LnBwTable<float> {
         {2048, 512, 1, 1024, 1}, {4096, 1024, 1, 1024, 1}, {8192, 1024, 2, 1024, 1}};
 };
 
+// Backward plans of the fused bias-dropout-residual LayerNorm: its third column partial
+// (dbias) does not fit two vectors per lane with two rows in flight at 4096-8192 fp16
+// columns, so those buckets take one vector per lane. fp32 at 8192 columns keeps two
+// vectors per lane at 1024 threads and spills part of its fp64 partials to scratch.
+template <typename T> struct BdrBwTable;
+template <> struct BdrBwTable<f16> {
+    static constexpr LnPlan plans[] = {
+        {64, 8, 1, 512, 1},      {128, 16, 1, 512, 1},    {256, 32, 1, 512, 1},
+        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 128, 1, 1024, 1},
+        {2048, 256, 1, 1024, 1}, {4096, 512, 1, 512, 1},  {8192, 1024, 1, 1024, 1}};
+};
+template <> struct BdrBwTable<float> {
+    static constexpr LnPlan plans[] = {
+        {64, 16, 1, 512, 1},     {128, 32, 1, 512, 1},    {256, 64, 1, 512, 1},
+        {512, 128, 1, 512, 1},   {768, 64, 3, 512, 1},    {1024, 256, 1, 1024, 1},
+        {2048, 512, 1, 1024, 1}, {4096, 1024, 1, 1024, 1}, {8192, 1024, 2, 1024, 1}};
+};
+
 constexpr int64_t kLnBwTargetBlocks = 256;  // one partial row per CU
 
 template <typename Table>
@@ -569,11 +690,16 @@ static int64_t bw_rows_per_block(int64_t N, int64_t groups) {
 
 static int64_t bw_blocks(int64_t N, int64_t rpb) { return N == 0 ? 0 : (N + rpb - 1) / rpb; }
 
-// Workgroups (= partial rows) of each backward path for this shape.
+// Workgroups (= partial rows) of each backward path for this shape (bdr: the fused
+// bias-dropout-residual LayerNorm's plan table).
 static void bw_partials(int64_t N, int64_t C, lnr_dtype dtype, int64_t &p_vec, int64_t &p_gen,
-                        int64_t &rpb_vec, int64_t &rpb_gen) {
+                        int64_t &rpb_vec, int64_t &rpb_gen, bool bdr = false) {
     LnPlan p{};
-    const bool ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, p) : find_plan<LnBwTable<float>>(C, p);
+    bool ok;
+    if (bdr)
+        ok = dtype == LNR_F16 ? find_plan<BdrBwTable<f16>>(C, p) : find_plan<BdrBwTable<float>>(C, p);
+    else
+        ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, p) : find_plan<LnBwTable<float>>(C, p);
     const int64_t groups = ok ? p.WG / p.G : 1;
     rpb_vec = bw_rows_per_block(N, groups);
     p_vec = bw_blocks(N, rpb_vec);
@@ -589,6 +715,11 @@ struct LnFwArgs {
     int64_t N;
     int32_t C;
     float eps;
+    // kBdrLayerNorm only
+    void *s_out = nullptr;
+    const void *residual = nullptr, *bias = nullptr;
+    const uint8_t *mask = nullptr;
+    float keep_scale = 1.f;
 };
 struct LnBwArgs {
     void *dx;
@@ -600,59 +731,72 @@ struct LnBwArgs {
     int32_t C;
     int64_t rows_per_block;
     int64_t blocks;
+    // kBdrLayerNorm only
+    void *dx2 = nullptr, *dbias = nullptr;
+    const void *ds_extra = nullptr;
+    const uint8_t *mask = nullptr;
+    float keep_scale = 1.f;
 };
 
-template <typename T, bool RMS, int I>
+template <typename T, int MODE, int I>
 static hipError_t dispatch_ln_fw(const LnFwArgs &a, hipStream_t st) {
     constexpr LnPlan p = LnFwTable<T>::plans[I];
     if (a.C <= p.bucket) {
         static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && p.R >= 1, "bad forward plan");
         constexpr int64_t RPB = static_cast<int64_t>(p.WG / p.G) * p.R;
         const int64_t blocks = (a.N + RPB - 1) / RPB;
-        return launch(layernorm_fw_vec<T, p.G, p.IT, p.WG, RMS>, dim3(static_cast<uint32_t>(blocks)),
+        return launch(layernorm_fw_vec<T, p.G, p.IT, p.WG, MODE>, dim3(static_cast<uint32_t>(blocks)),
                       dim3(p.WG), st, static_cast<T *>(a.y), a.mean, a.rstd,
                       static_cast<const T *>(a.x), static_cast<const T *>(a.gamma),
-                      static_cast<const T *>(a.beta), a.N, a.C, a.eps, RPB);
+                      static_cast<const T *>(a.beta), a.N, a.C, a.eps, RPB,
+                      static_cast<T *>(a.s_out), static_cast<const T *>(a.residual),
+                      static_cast<const T *>(a.bias), a.mask, a.keep_scale);
     }
     if constexpr (I + 1 < static_cast<int>(sizeof(LnFwTable<T>::plans) / sizeof(LnPlan)))
-        return dispatch_ln_fw<T, RMS, I + 1>(a, st);
+        return dispatch_ln_fw<T, MODE, I + 1>(a, st);
     return hipErrorInvalidValue;
 }
 
-// dgamma (and, for LayerNorm, dbeta) from the P partial rows; `slots` = 2 for LayerNorm,
-// 1 for RMSNorm (only the dgamma slot of each partial row is written).
+// Column sums of the P partial rows into dgamma, dbeta, dbias: `slots` outputs (1 RMSNorm,
+// 2 LayerNorm, 3 bias-dropout-residual LayerNorm), `stride` slots per partial row.
 template <typename T>
-static hipError_t launch_colsum(void *dgamma, void *dbeta, const void *part, int64_t P, int32_t C,
-                                int slots, hipStream_t st) {
+static hipError_t launch_colsum(void *dgamma, void *dbeta, void *dbias, const void *part, int64_t P,
+                                int32_t C, int slots, int stride, hipStream_t st) {
     using A = typename Accum<T>::type;
     if (C <= 1024) {
         const dim3 grid(static_cast<uint32_t>((C + 15) / 16), static_cast<uint32_t>(slots));
         return launch(layernorm_bw_colsum<T, 16, 16, 1>, grid, dim3(16 * 16), st,
-                      static_cast<T *>(dgamma), static_cast<T *>(dbeta),
-                      static_cast<const A *>(part), static_cast<int32_t>(P), C);
+                      static_cast<T *>(dgamma), static_cast<T *>(dbeta), static_cast<T *>(dbias),
+                      static_cast<const A *>(part), static_cast<int32_t>(P), C, stride);
     }
     const dim3 grid(static_cast<uint32_t>((C + 31) / 32), static_cast<uint32_t>(slots));
     return launch(layernorm_bw_colsum<T, 32, 32, 8>, grid, dim3(32 * 32), st,
-                  static_cast<T *>(dgamma), static_cast<T *>(dbeta), static_cast<const A *>(part),
-                  static_cast<int32_t>(P), C);
+                  static_cast<T *>(dgamma), static_cast<T *>(dbeta), static_cast<T *>(dbias),
+                  static_cast<const A *>(part), static_cast<int32_t>(P), C, stride);
 }
 
-template <typename T, bool RMS, int I>
+constexpr int slots_of(int mode) { return mode == kRmsNorm ? 1 : (mode == kBdrLayerNorm ? 3 : 2); }
+constexpr int stride_of(int mode) { return mode == kBdrLayerNorm ? 3 : 2; }
+
+template <typename T, int MODE, int I>
 static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
-    constexpr LnPlan p = LnBwTable<T>::plans[I];
+    using Table = std::conditional_t<MODE == kBdrLayerNorm, BdrBwTable<T>, LnBwTable<T>>;
+    constexpr LnPlan p = Table::plans[I];
     if (a.C <= p.bucket) {
         static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && (p.R == 1 || p.R == 2), "bad backward plan");
         static_assert(2 * (p.WG / 64) >= 2, "reduction slots");
         const hipError_t e = launch(
-            layernorm_bw_vec<T, p.G, p.IT, p.WG, p.R, RMS>, dim3(static_cast<uint32_t>(a.blocks)),
+            layernorm_bw_vec<T, p.G, p.IT, p.WG, p.R, MODE>, dim3(static_cast<uint32_t>(a.blocks)),
             dim3(p.WG), st, static_cast<T *>(a.dx), static_cast<typename Accum<T>::type *>(a.part),
             static_cast<const T *>(a.dy), static_cast<const T *>(a.x),
-            static_cast<const T *>(a.gamma), a.mean, a.rstd, a.N, a.C, a.rows_per_block);
+            static_cast<const T *>(a.gamma), a.mean, a.rstd, a.N, a.C, a.rows_per_block,
+            static_cast<T *>(a.dx2), static_cast<const T *>(a.ds_extra), a.mask, a.keep_scale);
         if (e != hipSuccess) return e;
-        return launch_colsum<T>(a.dgamma, a.dbeta, a.part, a.blocks, a.C, RMS ? 1 : 2, st);
+        return launch_colsum<T>(a.dgamma, a.dbeta, a.dbias, a.part, a.blocks, a.C, slots_of(MODE),
+                                stride_of(MODE), st);
     }
-    if constexpr (I + 1 < static_cast<int>(sizeof(LnBwTable<T>::plans) / sizeof(LnPlan)))
-        return dispatch_ln_bw<T, RMS, I + 1>(a, st);
+    if constexpr (I + 1 < static_cast<int>(sizeof(Table::plans) / sizeof(LnPlan)))
+        return dispatch_ln_bw<T, MODE, I + 1>(a, st);
     return hipErrorInvalidValue;
 }
 
@@ -696,7 +840,8 @@ static int norm_fw(void *y, float *mean, float *rstd, const void *x, const void 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (vec) {
-        e = dtype == LNR_F16 ? dispatch_ln_fw<f16, RMS, 0>(a, s) : dispatch_ln_fw<float, RMS, 0>(a, s);
+        constexpr int MODE = RMS ? kRmsNorm : kLayerNorm;
+        e = dtype == LNR_F16 ? dispatch_ln_fw<f16, MODE, 0>(a, s) : dispatch_ln_fw<float, MODE, 0>(a, s);
     } else if (dtype == LNR_F16) {
         e = launch(layernorm_fw_generic<f16, RMS>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), s,
                    static_cast<f16 *>(y), mean, rstd, static_cast<const f16 *>(x),
@@ -752,15 +897,16 @@ static int norm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const vo
     hipError_t e = hipSuccess;
     if (N == 0) {
         // No rows: the column sums are empty, and the column-sum kernel writes zeros.
-        e = dtype == LNR_F16 ? launch_colsum<f16>(dgamma, dbeta, workspace, 0, C32, slots, s)
-                             : launch_colsum<float>(dgamma, dbeta, workspace, 0, C32, slots, s);
+        e = dtype == LNR_F16 ? launch_colsum<f16>(dgamma, dbeta, nullptr, workspace, 0, C32, slots, 2, s)
+                             : launch_colsum<float>(dgamma, dbeta, nullptr, workspace, 0, C32, slots, 2, s);
         return status_of(e);
     }
     const bool vec = (static_cast<size_t>(C) * es) % 16 == 0 && aligned_to(dx, 16) &&
                      aligned_to(dy, 16) && aligned_to(x, 16) && aligned_to(gamma, 16);
     if (vec) {
         LnBwArgs a{dx, dgamma, dbeta, workspace, dy, x, gamma, mean, rstd, N, C32, rv, pv};
-        e = dtype == LNR_F16 ? dispatch_ln_bw<f16, RMS, 0>(a, s) : dispatch_ln_bw<float, RMS, 0>(a, s);
+        constexpr int MODE = RMS ? kRmsNorm : kLayerNorm;
+        e = dtype == LNR_F16 ? dispatch_ln_bw<f16, MODE, 0>(a, s) : dispatch_ln_bw<float, MODE, 0>(a, s);
     } else if (dtype == LNR_F16) {
         e = launch(layernorm_bw_dx_generic<f16, RMS>, dim3(static_cast<uint32_t>(N)),
                    dim3(kLnGenericWG), s, static_cast<f16 *>(dx), static_cast<const f16 *>(dy),
@@ -771,7 +917,7 @@ static int norm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const vo
                             static_cast<uint32_t>(pg)),
                        dim3(kLnGenericWG), s, static_cast<float *>(workspace),
                        static_cast<const f16 *>(dy), static_cast<const f16 *>(x), mean, rstd, N, C32, rg);
-        if (e == hipSuccess) e = launch_colsum<f16>(dgamma, dbeta, workspace, pg, C32, slots, s);
+        if (e == hipSuccess) e = launch_colsum<f16>(dgamma, dbeta, nullptr, workspace, pg, C32, slots, 2, s);
     } else {
         e = launch(layernorm_bw_dx_generic<float, RMS>, dim3(static_cast<uint32_t>(N)),
                    dim3(kLnGenericWG), s, static_cast<float *>(dx), static_cast<const float *>(dy),
@@ -782,14 +928,159 @@ static int norm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const vo
                             static_cast<uint32_t>(pg)),
                        dim3(kLnGenericWG), s, static_cast<double *>(workspace),
                        static_cast<const float *>(dy), static_cast<const float *>(x), mean, rstd, N, C32, rg);
-        if (e == hipSuccess) e = launch_colsum<float>(dgamma, dbeta, workspace, pg, C32, slots, s);
+        if (e == hipSuccess) e = launch_colsum<float>(dgamma, dbeta, nullptr, workspace, pg, C32, slots, 2, s);
     }
+    return status_of(e);
+}
+
+static size_t bdr_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype) {
+    if (!valid_dtype(dtype) || N < 0 || C < 1 || C > LNR_LAYERNORM_MAX_C) return 0;
+    int64_t pv, pg, rv, rg;
+    bw_partials(N, C, dtype, pv, pg, rv, rg, true);
+    return static_cast<size_t>(pv) * 3 * static_cast<size_t>(C) * accum_size(dtype);
+}
+
+// The fused op runs on the vector path only: every [N, C] and [C] buffer 16-byte aligned and
+// C * element size a multiple of 16 (C a multiple of 8 for fp16, of 4 for fp32).
+static bool bdr_vec_ok(int64_t C, size_t es, std::initializer_list<const void *> bufs) {
+    if ((static_cast<size_t>(C) * es) % 16 != 0) return false;
+    for (const void *b : bufs)
+        if (b != nullptr && !aligned_to(b, 16)) return false;
+    return true;
+}
+
+static int bdr_fw(void *s_out, void *y, float *mean, float *rstd, const void *x,
+                  const void *residual, const void *bias, const uint8_t *mask, float p,
+                  const void *gamma, const void *beta, int64_t N, int64_t C, float eps,
+                  lnr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (N < 0 || C < 1) return LNR_ERR_SHAPE;
+    if (C > LNR_LAYERNORM_MAX_C || N > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || !isfinite(eps) || !(p >= 0.f) || !(p < 1.f)) return LNR_ERR_SHAPE;
+    if ((mean == nullptr) != (rstd == nullptr)) return LNR_ERR_NULL;
+    if (N == 0) return LNR_OK;
+    if (s_out == nullptr || y == nullptr || x == nullptr || residual == nullptr ||
+        bias == nullptr || mask == nullptr || gamma == nullptr || beta == nullptr)
+        return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if ((static_cast<size_t>(C) * es) % 16 != 0) return LNR_ERR_UNSUPPORTED;
+    if (!bdr_vec_ok(C, es, {s_out, y, x, residual, bias, gamma, beta}) || !aligned_to(mean, 4) ||
+        !aligned_to(rstd, 4))
+        return LNR_ERR_ALIGN;
+    const size_t nb = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
+    const size_t cb = static_cast<size_t>(C) * es;
+    const size_t mbytes = static_cast<size_t>(N) * static_cast<size_t>((C + 7) / 8);
+    // s may replace residual in place (elementwise); no other overlap.
+    if (bad_alias(s_out, residual, nb) || overlap(s_out, nb, x, nb) || overlap(y, nb, s_out, nb) ||
+        overlap(y, nb, x, nb) || overlap(y, nb, residual, nb) || overlap(x, nb, residual, nb))
+        return LNR_ERR_ALIAS;
+    for (const void *out : {s_out, y})
+        if (overlap(out, nb, bias, cb) || overlap(out, nb, gamma, cb) || overlap(out, nb, beta, cb) ||
+            overlap(out, nb, mask, mbytes) || overlap(out, nb, mean, N * 4) ||
+            overlap(out, nb, rstd, N * 4))
+            return LNR_ERR_ALIAS;
+    if (overlap(mean, N * 4, rstd, N * 4)) return LNR_ERR_ALIAS;
+
+    LnFwArgs a{y, mean, rstd, x, gamma, beta, N, static_cast<int32_t>(C), eps};
+    a.s_out = s_out;
+    a.residual = residual;
+    a.bias = bias;
+    a.mask = mask;
+    a.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == LNR_F16 ? dispatch_ln_fw<f16, kBdrLayerNorm, 0>(a, st)
+                                          : dispatch_ln_fw<float, kBdrLayerNorm, 0>(a, st);
+    return status_of(e);
+}
+
+static int bdr_bw(void *dres, void *dx, void *dgamma, void *dbeta, void *dbias, const void *dy,
+                  const void *ds_extra, const void *s_in, const uint8_t *mask, float p,
+                  const void *gamma, const float *mean, const float *rstd, int64_t N, int64_t C,
+                  lnr_dtype dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (N < 0 || C < 1) return LNR_ERR_SHAPE;
+    if (C > LNR_LAYERNORM_MAX_C || N > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    if (!(p >= 0.f) || !(p < 1.f)) return LNR_ERR_SHAPE;
+    if (dgamma == nullptr || dbeta == nullptr || dbias == nullptr) return LNR_ERR_NULL;
+    if (N > 0 && (dres == nullptr || dx == nullptr || dy == nullptr || s_in == nullptr ||
+                  mask == nullptr || gamma == nullptr || mean == nullptr || rstd == nullptr))
+        return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if ((static_cast<size_t>(C) * es) % 16 != 0) return LNR_ERR_UNSUPPORTED;
+    if (!bdr_vec_ok(C, es, {dres, dx, dy, ds_extra, s_in, gamma}) || !aligned_to(dgamma, es) ||
+        !aligned_to(dbeta, es) || !aligned_to(dbias, es) || !aligned_to(mean, 4) ||
+        !aligned_to(rstd, 4))
+        return LNR_ERR_ALIGN;
+    const size_t need = bdr_workspace_bytes(N, C, dtype);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LNR_ERR_WORKSPACE;
+    if (need > 0 && !aligned_to(workspace, 8)) return LNR_ERR_ALIGN;
+    const size_t nb = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
+    const size_t cb = static_cast<size_t>(C) * es;
+    const size_t mbytes = static_cast<size_t>(N) * static_cast<size_t>((C + 7) / 8);
+    // dresidual may replace dy or ds_extra in place; dx overlaps nothing.
+    if (bad_alias(dres, dy, nb) || bad_alias(dres, ds_extra, nb) || overlap(dres, nb, s_in, nb) ||
+        overlap(dx, nb, dres, nb) || overlap(dx, nb, dy, nb) || overlap(dx, nb, ds_extra, nb) ||
+        overlap(dx, nb, s_in, nb))
+        return LNR_ERR_ALIAS;
+    for (const void *out : {dres, dx})
+        if (overlap(out, nb, gamma, cb) || overlap(out, nb, mask, mbytes) ||
+            overlap(out, nb, mean, N * 4) || overlap(out, nb, rstd, N * 4) ||
+            overlap(out, nb, workspace, need))
+            return LNR_ERR_ALIAS;
+    for (const void *out : {dgamma, dbeta, dbias}) {
+        if (overlap(out, cb, dres, nb) || overlap(out, cb, dx, nb) || overlap(out, cb, dy, nb) ||
+            overlap(out, cb, s_in, nb) || overlap(out, cb, gamma, cb) || overlap(out, cb, workspace, need))
+            return LNR_ERR_ALIAS;
+    }
+    if (overlap(dgamma, cb, dbeta, cb) || overlap(dgamma, cb, dbias, cb) || overlap(dbeta, cb, dbias, cb))
+        return LNR_ERR_ALIAS;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int32_t C32 = static_cast<int32_t>(C);
+    if (N == 0) {
+        const hipError_t e =
+            dtype == LNR_F16 ? launch_colsum<f16>(dgamma, dbeta, dbias, workspace, 0, C32, 3, 3, st)
+                             : launch_colsum<float>(dgamma, dbeta, dbias, workspace, 0, C32, 3, 3, st);
+        return status_of(e);
+    }
+    int64_t pv, pg, rv, rg;
+    bw_partials(N, C, dtype, pv, pg, rv, rg, true);
+    LnBwArgs a{dres, dgamma, dbeta, workspace, dy, s_in, gamma, mean, rstd, N, C32, rv, pv};
+    a.dx2 = dx;
+    a.dbias = dbias;
+    a.ds_extra = ds_extra;
+    a.mask = mask;
+    a.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p)));
+    const hipError_t e = dtype == LNR_F16 ? dispatch_ln_bw<f16, kBdrLayerNorm, 0>(a, st)
+                                          : dispatch_ln_bw<float, kBdrLayerNorm, 0>(a, st);
     return status_of(e);
 }
 
 }  // namespace lnr
 
 using namespace lnr;
+
+extern "C" int bdr_layernorm_fw(void *s, void *y, float *mean, float *rstd, const void *x,
+                                const void *residual, const void *bias, const uint8_t *keep_mask,
+                                float p, const void *gamma, const void *beta, int64_t N, int64_t C,
+                                float eps, lnr_dtype dtype, void *stream) {
+    return bdr_fw(s, y, mean, rstd, x, residual, bias, keep_mask, p, gamma, beta, N, C, eps, dtype,
+                  stream);
+}
+
+extern "C" size_t bdr_layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype) {
+    return bdr_workspace_bytes(N, C, dtype);
+}
+
+extern "C" int bdr_layernorm_bw(void *dresidual, void *dx, void *dgamma, void *dbeta, void *dbias,
+                                const void *dy, const void *ds_extra, const void *s,
+                                const uint8_t *keep_mask, float p, const void *gamma,
+                                const float *mean, const float *rstd, int64_t N, int64_t C,
+                                lnr_dtype dtype, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+    return bdr_bw(dresidual, dx, dgamma, dbeta, dbias, dy, ds_extra, s, keep_mask, p, gamma, mean,
+                  rstd, N, C, dtype, workspace, workspace_bytes, stream);
+}
 
 extern "C" int layernorm_fw(void *y, float *mean, float *rstd, const void *x, const void *gamma,
                             const void *beta, int64_t N, int64_t C, float eps, lnr_dtype dtype,

@@ -209,6 +209,67 @@ def rmsnorm_sweep_case(N: int, C: int, dtype=torch.float16) -> LayerNormCase:
 
 
 # ------------------------------------------------------------------------------------------
+# Bias + dropout + residual feeding LayerNorm (the L10 page's elementwise kernel before the
+# LayerNorm reduce kernel). The page gives no dropout rate; p = 0.1 is the workload rate,
+# with 0 and 0.5 as edge cases. The keep mask is drawn here (keep iff a uniform draw >= p)
+# and packed one bit per element, least significant bit first (numpy's packbits, bitorder
+# "little"): the kernels and the oracle both read the same bits.
+# ------------------------------------------------------------------------------------------
+BDR_P = 0.1
+
+
+@dataclass
+class BdrCase:
+    name: str
+    N: int
+    C: int
+    dtype: torch.dtype
+    p: float
+    x: torch.Tensor
+    residual: torch.Tensor
+    bias: torch.Tensor
+    gamma: torch.Tensor
+    beta: torch.Tensor
+    keep: torch.Tensor       # bool [N, C]
+    mask: torch.Tensor       # uint8 [N, ceil(C/8)]
+    dy: torch.Tensor
+    ds_extra: torch.Tensor
+    eps: float = LN_EPS
+
+
+def pack_keep_bits(keep: torch.Tensor) -> torch.Tensor:
+    import numpy as np
+    return torch.from_numpy(np.packbits(keep.numpy(), axis=1, bitorder="little"))
+
+
+def bdr_case(name, N, C, *, dtype, seed_base, p=BDR_P) -> BdrCase:
+    """x ~ N(0,1) (the GEMM output before its bias), residual ~ N(0,1) plus a per-row N(0,1)
+    offset, bias ~ N(0, 0.1), gamma ~ U(0.5,1.5), beta ~ N(0,0.1), dy and ds_extra ~ N(0,1)."""
+    x = normal((N, C), seed_base + K_X)
+    residual = normal((N, C), seed_base + K_SCORES).add_(normal((N, 1), seed_base + K_OFFSET))
+    bias = normal((C,), seed_base + K_LENGTHS, var=0.1)
+    gamma = uniform((C,), seed_base + K_GAMMA, 0.5, 1.5)
+    beta = normal((C,), seed_base + K_BETA, var=0.1)
+    keep = torch.rand((N, C), generator=_gen(seed_base + K_SDY)) >= p
+    dy = normal((N, C), seed_base + K_LNDY)
+    ds_extra = normal((N, C), seed_base + K_LNDY + 100)
+    return BdrCase(name, N, C, dtype, p, x.to(dtype), residual.to(dtype), bias.to(dtype),
+                   gamma.to(dtype), beta.to(dtype), keep, pack_keep_bits(keep), dy.to(dtype),
+                   ds_extra.to(dtype))
+
+
+def bdr_fw_bytes(N, C, s) -> int:
+    """Read x, residual, mask bits; write s, y, fp32 mean and rstd; read bias, gamma, beta."""
+    return 4 * N * C * s + N * ((C + 7) // 8) + 8 * N + 3 * C * s
+
+
+def bdr_bw_bytes(N, C, s, extra=False) -> int:
+    """Read dy, s, mask bits (and ds_extra), fp32 mean and rstd, gamma; write dresidual, dx,
+    dgamma, dbeta, dbias."""
+    return (5 if extra else 4) * N * C * s + N * ((C + 7) // 8) + 8 * N + 4 * C * s
+
+
+# ------------------------------------------------------------------------------------------
 # Softmax cross-entropy over a vocabulary (the L10 page's third reduce kernel). The pages give
 # no shapes; these stand in for a language-model head: the GPT-2 batch of [FT] section 1
 # (B = 32, T = 256: 8192 tokens) over vocabularies of 10^4 - 10^5 entries, one a multiple of

@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -227,6 +227,53 @@ def test_cross_entropy_bw_validation(lib):
     assert xbw(lib, z=A + 64) == ALIAS                       # partial overlap of dlogits, logits
     assert xbw(lib, lse=A + 128) == ALIAS                    # lse inside dlogits
     assert xbw(lib, N=0) == OK
+
+
+def bfw(lib, s=A, y=A + 2 ** 28, mean=A + 2 ** 29, rstd=A + 2 ** 29 + 2 ** 20, x=A + 2 ** 30,
+        r=A + 2 ** 31, b=A + 2 ** 32, m=A + 2 ** 32 + 2 ** 20, p=0.1, g=A + 2 ** 33,
+        be=A + 2 ** 33 + 2 ** 20, N=64, C=64, eps=1e-8, dtype=F16):
+    return lib.bdr_layernorm_fw(s, y, mean, rstd, x, r, b, m, p, g, be, N, C, eps, dtype, None)
+
+
+def test_bdr_layernorm_fw_validation(lib):
+    assert bfw(lib, dtype=4) == DTYPE
+    assert bfw(lib, C=0) == SHAPE
+    assert bfw(lib, p=1.0) == SHAPE
+    assert bfw(lib, p=-0.1) == SHAPE
+    assert bfw(lib, C=100) == UNSUP                          # fp16 rows must be whole vectors
+    assert bfw(lib, C=9000) == UNSUP
+    assert bfw(lib, m=None) == NULL
+    assert bfw(lib, mean=None) == NULL                       # mean and rstd: both or neither
+    assert bfw(lib, x=A + 2 ** 30 + 2) == ALIGN              # vector path needs 16 bytes
+    assert bfw(lib, s=A + 2 ** 31 + 64) == ALIAS             # s partially over residual
+    assert bfw(lib, y=A + 64) == ALIAS                       # y over s
+    assert bfw(lib, N=0) == OK
+
+
+def bbw(lib, dr=A, dx=A + 2 ** 28, dg=A + 2 ** 29, db=A + 2 ** 29 + 2 ** 16,
+        dbias=A + 2 ** 29 + 2 ** 17, dy=A + 2 ** 30, de=None, s=A + 2 ** 31, m=A + 2 ** 32,
+        p=0.1, g=A + 2 ** 32 + 2 ** 20, mean=A + 2 ** 33, rstd=A + 2 ** 33 + 2 ** 20, N=64, C=64,
+        dtype=F16, ws=A + 2 ** 34, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.bdr_layernorm_bw_workspace_bytes(N, C, dtype)
+    return lib.bdr_layernorm_bw(dr, dx, dg, db, dbias, dy, de, s, m, p, g, mean, rstd, N, C, dtype,
+                                ws, ws_bytes, None)
+
+
+def test_bdr_layernorm_bw_validation(lib):
+    assert bbw(lib, dtype=9) == DTYPE
+    assert bbw(lib, p=1.5) == SHAPE
+    assert bbw(lib, C=36) == UNSUP
+    assert bbw(lib, dbias=None) == NULL
+    assert bbw(lib, m=None) == NULL
+    assert bbw(lib, s=A + 2 ** 31 + 8) == ALIGN
+    need = lib.bdr_layernorm_bw_workspace_bytes(64, 64, F16)
+    assert need > 0                                          # vector path only: 3 slots per partial row
+    assert bbw(lib, ws_bytes=need - 1) == WS
+    assert bbw(lib, dx=A + 64) == ALIAS                      # dx over dresidual
+    assert bbw(lib, dr=A + 2 ** 30 + 128) == ALIAS           # dresidual partially over dy
+    assert bbw(lib, dbias=A + 2 ** 29 + 2) == ALIAS          # dbias over dgamma
+    # (N = 0 launches the zero-fill of the parameter gradients: covered by the GPU tests)
 
 
 def test_workspace_bytes(lib):

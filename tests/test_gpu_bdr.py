@@ -1,0 +1,206 @@
+"""GPU parity of bdr_layernorm_fw / bdr_layernorm_bw (bias + dropout + residual feeding
+LayerNorm) through the C ABI against the fp64 oracle.
+
+  * forward: s, y, mean and rstd on seeded inputs, every element (s is formed and normalised
+    in fp32; the stored s is rounded to the storage type);
+  * backward on identical inputs: both sides receive the oracle's s rounded to the storage
+    type, that s's statistics rounded to fp32, the same mask, dy and ds_extra; compared
+    element by element (dresidual and dx with the LayerNorm dx bound's rounding term);
+  * chained: GPU forward outputs feeding the GPU backward, at twice the tolerance, against
+    the oracle's gradient of the pipeline as stored: the oracle's s rounded to the storage
+    type with the statistics of the exact s (what the forward saves). Against fully exact
+    fp64 math the column sums cannot agree at fp16: each stored s carries ~2^-11 relative
+    rounding, and dgamma = sum over 8192 rows of dy * shat accumulates it to a few percent.
+    dgamma is compared norm-wise (max |err| <= atol + rtol * max |ref|): the kernel forms s
+    in fp32 and rounds that to fp16, so where the exact s lies within fp32 roundoff of an
+    fp16 rounding midpoint (about 1 element in 2000) the stored s is the neighbouring fp16
+    value; at |s| ~ 4-8 one such step moves dgamma_j by dy * 2^-8 * rstd ~ 4e-3. dbeta and
+    dbias do not depend on s and stay element-wise; the element-wise dgamma check is the
+    identical-input one above.
+"""
+import numpy as np
+import pytest
+import torch
+
+import layernorm_reduction_amd as lnr
+import oracle
+from layernorm_reduction_amd import workloads as W
+from parity_utils import TOL, assert_close, say, to_host64, violations
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U32 = 2.0 ** -24
+
+
+def assert_ds_close(got_t, ref, dtype, what, dy64, g64, rstd, scale=1.0, factor=1.0):
+    """The LayerNorm input-gradient bound (see the LayerNorm tests), times `factor` for dx =
+    keep * ds / (1 - p)."""
+    atol, rtol = TOL[dtype]
+    got = to_host64(got_t)
+    cond = factor * 16.0 * U32 * np.asarray(rstd, np.float64).reshape(-1, 1) * \
+        np.max(np.abs(dy64 * g64.reshape(1, -1)), axis=1, keepdims=True)
+    err = np.abs(got - ref)
+    lim = scale * (atol + rtol * np.abs(ref)) + cond
+    bad = ~(err <= lim)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err - lim, -np.inf)), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside the bound; worst at {i}: "
+                             f"gpu={got[i]!r} oracle={ref[i]!r} bound={lim[i]:.3e}")
+
+
+def run_bdr(case, extra=True, chain=True):
+    dt = case.dtype
+    atol, rtol = TOL[dt]
+    m = case.mask.numpy()
+    say(case.name, "oracle forward")
+    x64, r64, b64 = (t.double().numpy() for t in (case.x, case.residual, case.bias))
+    g64, be64 = case.gamma.double().numpy(), case.beta.double().numpy()
+    s_ref, y_ref, mean_ref, rstd_ref = oracle.bdr_ln_fw(x64, r64, b64, m, case.p, g64, be64, case.eps)
+
+    say(case.name, "GPU forward")
+    xd, rd, bd = case.x.to(DEV), case.residual.to(DEV), case.bias.to(DEV)
+    gd, bed, md = case.gamma.to(DEV), case.beta.to(DEV), case.mask.to(DEV)
+    s, y, mean, rstd = lnr.bdr_layernorm_fw(xd, rd, bd, md, case.p, gd, bed, case.eps)
+    torch.cuda.synchronize()
+    assert_close(s, s_ref, dt, f"{case.name} s")
+    assert_close(y, y_ref, dt, f"{case.name} y")
+    assert_close(mean, mean_ref, dt, f"{case.name} mean")
+    assert_close(rstd, rstd_ref, dt, f"{case.name} rstd")
+
+    say(case.name, "oracle backward (identical inputs)")
+    s_in = torch.from_numpy(s_ref).to(dt)                  # the stored s
+    s_in64 = s_in.double().numpy()
+    _, mu_in, rs_in = oracle.layernorm_fw(s_in64, g64, be64, case.eps)
+    mu32 = torch.from_numpy(mu_in).float()
+    rs32 = torch.from_numpy(rs_in).float()
+    dy64 = case.dy.double().numpy()
+    de64 = case.ds_extra.double().numpy() if extra else None
+    refs = oracle.bdr_ln_bw(s_in64, dy64, de64, m, case.p, g64, mu32.numpy(), rs32.numpy())
+    say(case.name, "GPU backward")
+    dyd = case.dy.to(DEV)
+    ded = case.ds_extra.to(DEV) if extra else None
+    got = lnr.bdr_layernorm_bw(dyd, s_in.to(DEV), md, case.p, gd, mu32.to(DEV), rs32.to(DEV), ded)
+    torch.cuda.synchronize()
+    inv_keep = 1.0 / (1.0 - case.p)
+    r32 = rs32.double().numpy()
+    assert_ds_close(got[0], refs[0], dt, f"{case.name} dresidual", dy64, g64, r32)
+    assert_ds_close(got[1], refs[1], dt, f"{case.name} dx", dy64, g64, r32, factor=inv_keep)
+    assert_close(got[2], refs[2], dt, f"{case.name} dgamma")
+    assert_close(got[3], refs[3], dt, f"{case.name} dbeta")
+    assert_close(got[4], refs[4], dt, f"{case.name} dbias")
+
+    if chain:
+        say(case.name, "chained fw -> bw against the stored-s gradient")
+        ex = oracle.bdr_ln_bw(s_in64, dy64, de64, m, case.p, g64, mean_ref, rstd_ref)
+        ch = lnr.bdr_layernorm_bw(dyd, s, md, case.p, gd, mean, rstd, ded)
+        torch.cuda.synchronize()
+        sc = 2.0
+        assert_ds_close(ch[0], ex[0], dt, f"{case.name} chain dresidual", dy64, g64, rstd_ref, scale=sc)
+        assert_ds_close(ch[1], ex[1], dt, f"{case.name} chain dx", dy64, g64, rstd_ref, scale=sc,
+                        factor=inv_keep)
+        got = to_host64(ch[2])
+        bad, _ = violations(got, ex[2], atol * sc, rtol * sc)
+        print(f"[info] {case.name} chained dgamma element-wise: {case.C - bad}/{case.C} within "
+              f"atol=rtol={atol * sc}", flush=True)
+        err = float(np.max(np.abs(got - ex[2])))
+        assert err <= atol * sc + rtol * sc * float(np.max(np.abs(ex[2]))), err
+        for k, nm in ((3, "dbeta"), (4, "dbias")):
+            assert_close(ch[k], ex[k], dt, f"{case.name} chain {nm}", atol=atol * sc, rtol=rtol * sc)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("extra", [False, True])
+def test_gpt2_shape(extra):
+    run_bdr(W.bdr_case("bdr-8192x256-f16", 8192, 256, dtype=torch.float16, seed_base=9000), extra)
+
+
+@pytest.mark.parametrize("C", [768, 1024, 4096])
+def test_hidden_sizes_fp16(C):
+    run_bdr(W.bdr_case(f"bdr-16384x{C}-f16", 16384, C, dtype=torch.float16, seed_base=9100 + C))
+
+
+@pytest.mark.parametrize("C", [1024, 8192])
+def test_fp32(C):
+    # C = 8192 fp32 is the plan whose backward spills part of its fp64 partials to scratch
+    N = 8192 if C == 1024 else 2048
+    run_bdr(W.bdr_case(f"bdr-{N}x{C}-f32", N, C, dtype=torch.float32, seed_base=9200 + C),
+            chain=False)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.5])
+@pytest.mark.parametrize("dtype,C", [(torch.float16, 8), (torch.float16, 24), (torch.float16, 264),
+                                     (torch.float16, 1000), (torch.float16, 2056), (torch.float16, 8192),
+                                     (torch.float32, 4), (torch.float32, 12), (torch.float32, 100),
+                                     (torch.float32, 4092)])
+def test_edges(dtype, C, p):
+    for N in (1, 7, 1031):
+        run_bdr(W.bdr_case(f"bdr-edge-{N}x{C}-{dtype}-p{p}", N, C, dtype=dtype,
+                           seed_base=9300 + C, p=p), extra=(N != 7), chain=False)
+
+
+def test_p_zero_equals_layernorm_of_the_sum():
+    case = W.bdr_case("bdr-p0", 1000, 1024, dtype=torch.float32, seed_base=9400, p=0.0)
+    xd, rd, bd = case.x.to(DEV), case.residual.to(DEV), case.bias.to(DEV)
+    gd, bed = case.gamma.to(DEV), case.beta.to(DEV)
+    say(case.name)
+    s, y, _, _ = lnr.bdr_layernorm_fw(xd, rd, bd, case.mask.to(DEV), 0.0, gd, bed, case.eps)
+    y2, _, _ = lnr.layernorm_fw(s, gd, bed, case.eps)
+    torch.cuda.synchronize()
+    assert torch.all(case.keep)
+    assert_close(y, to_host64(y2), torch.float32, "bdr(p=0) vs layernorm(s)")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+def test_in_place_and_determinism(dtype):
+    case = W.bdr_case("bdr-inplace", 3000, 1024, dtype=dtype, seed_base=9500)
+    xd, rd, bd = case.x.to(DEV), case.residual.to(DEV), case.bias.to(DEV)
+    gd, bed, md = case.gamma.to(DEV), case.beta.to(DEV), case.mask.to(DEV)
+    say(case.name, dtype)
+    s1, y1, m1, r1 = lnr.bdr_layernorm_fw(xd, rd, bd, md, case.p, gd, bed)
+    ri = rd.clone()
+    si, yi, _, _ = lnr.bdr_layernorm_fw(xd, ri, bd, md, case.p, gd, bed, s=ri)   # s over residual
+    dyd, ded = case.dy.to(DEV), case.ds_extra.to(DEV)
+    a = lnr.bdr_layernorm_bw(dyd, s1, md, case.p, gd, m1, r1, ded)
+    b = lnr.bdr_layernorm_bw(dyd, s1, md, case.p, gd, m1, r1, ded)
+    dyi = dyd.clone()
+    c = lnr.bdr_layernorm_bw(dyi, s1, md, case.p, gd, m1, r1, ded, dresidual=dyi)  # over dy
+    torch.cuda.synchronize()
+    assert torch.equal(s1, ri) and torch.equal(y1, yi)
+    for u, v, w in zip(a, b, c):
+        assert torch.equal(u, v) and torch.equal(u, w)
+
+
+def test_unsupported_shapes_and_alignment_are_rejected():
+    N, C = 16, 100  # fp16: 100 is not a multiple of 8
+    z = torch.zeros(N, C, dtype=torch.float16, device=DEV)
+    c = torch.zeros(C, dtype=torch.float16, device=DEV)
+    mk = torch.zeros(N, (C + 7) // 8, dtype=torch.uint8, device=DEV)
+    with pytest.raises(lnr.LnrError) as e:
+        lnr.bdr_layernorm_fw(z, z, c, mk, 0.1, c, c)
+    assert e.value.status == 3
+    C = 64
+    buf = torch.zeros(N * C + 8, dtype=torch.float16, device=DEV)
+    xs = buf[1:1 + N * C].view(N, C)               # 2-byte aligned, not 16
+    z = torch.zeros(N, C, dtype=torch.float16, device=DEV)
+    c = torch.zeros(C, dtype=torch.float16, device=DEV)
+    mk = torch.zeros(N, C // 8, dtype=torch.uint8, device=DEV)
+    with pytest.raises(lnr.LnrError) as e:
+        lnr.bdr_layernorm_fw(xs, z, c, mk, 0.1, c, c)
+    assert e.value.status == 5
+    with pytest.raises(lnr.LnrError) as e:
+        lnr.bdr_layernorm_fw(z, z.clone(), c, mk, 1.0, c, c)   # p must be < 1
+    assert e.value.status == 2
+
+
+def test_zero_rows_give_zero_parameter_gradients():
+    C = 512
+    s = torch.empty(0, C, dtype=torch.float16, device=DEV)
+    g = torch.ones(C, dtype=torch.float16, device=DEV)
+    st = torch.empty(0, dtype=torch.float32, device=DEV)
+    mk = torch.empty(0, C // 8, dtype=torch.uint8, device=DEV)
+    outs = [torch.full((C,), 7.0, dtype=torch.float16, device=DEV) for _ in range(3)]
+    say("N=0 bdr backward")
+    lnr.bdr_layernorm_bw(s, s, mk, 0.1, g, st, st, None, dgamma=outs[0], dbeta=outs[1], dbias=outs[2])
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.all(o == 0)
