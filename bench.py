@@ -241,6 +241,16 @@ def table_cases():
         cases.append((f"xent [8192,{V}] fp16", "xent", (8192, V), torch.float16, {}))
     cases.append(("xent [8192,32000] fp32", "xent", (8192, 32000), torch.float32, {}))
     cases.append(("xent [64,32000] fp16 (split rows)", "xent", (64, 32000), torch.float16, {}))
+    # Bias + dropout + residual feeding LayerNorm: post-LN (s has one consumer) and pre-LN (s
+    # is the residual stream, so a second gradient reaches it) at the model shape, then wider.
+    for extra in (False, True):
+        cases.append((f"bdr-ln [8192,256] fp16 {'pre-LN' if extra else 'post-LN'}", "bdr", (8192, 256),
+                      torch.float16, {"extra": extra}))
+    for C in (1024, 4096):
+        cases.append((f"bdr-ln [16384,{C}] fp16 post-LN", "bdr", (16384, C), torch.float16,
+                      {"extra": False}))
+    cases.append(("bdr-ln [32768,1024] fp32 post-LN", "bdr", (32768, 1024), torch.float32,
+                  {"extra": False}))
     return cases
 
 
@@ -399,6 +409,36 @@ def run_table(match: str = ""):
             bf = W.rmsnorm_fw_bytes(N, C, s)
             bb = W.rmsnorm_bw_bytes(N, C, s)
             rows, tensor = N, per
+        elif kind == "bdr":
+            N, C = shape
+            per = N * C * s
+            n = max(2, math.ceil(MIN_FOOTPRINT / (8 * per)))
+            fw, bw = [], []
+            keep = []
+            wsb = lnr.bdr_layernorm_bw_workspace_bytes(N, C, lnr.LNR_F16 if dt == torch.float16 else lnr.LNR_F32)
+            for _ in range(n):
+                x = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                r = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                dy = torch.randn(shape, device=dev, dtype=dt, generator=g)
+                de = torch.randn(shape, device=dev, dtype=dt, generator=g) if extra["extra"] else None
+                mk = torch.randint(0, 256, (N, (C + 7) // 8), device=dev, generator=g,
+                                   dtype=torch.int32).to(torch.uint8)
+                bi = torch.randn(C, device=dev, dtype=dt, generator=g)
+                gm = torch.rand(C, device=dev, dtype=dt, generator=g) + 0.5
+                bt = torch.randn(C, device=dev, dtype=dt, generator=g)
+                so, y, dr, dx = (torch.empty_like(x) for _ in range(4))
+                mean = torch.empty(N, device=dev, dtype=torch.float32)
+                rstd = torch.empty(N, device=dev, dtype=torch.float32)
+                dg, db, dbi = (torch.empty(C, device=dev, dtype=dt) for _ in range(3))
+                ws = torch.empty(max(wsb, 1), device=dev, dtype=torch.uint8)
+                fw.append(lnr.bind_bdr_layernorm_fw(x, r, bi, mk, W.BDR_P, gm, bt, W.LN_EPS, so, y,
+                                                    mean, rstd))
+                bw.append(lnr.bind_bdr_layernorm_bw(dy, so, mk, W.BDR_P, gm, mean, rstd, de, dr, dx,
+                                                    dg, db, dbi, ws))
+                keep += [x, r, dy, de, mk, bi, gm, bt, so, y, dr, dx, mean, rstd, dg, db, dbi, ws]
+            bf = W.bdr_fw_bytes(N, C, s)
+            bb = W.bdr_bw_bytes(N, C, s, extra["extra"])
+            rows, tensor = N, per
         torch.cuda.synchronize()
         f_b2b, f_k = timed(fw)
         b_b2b, b_k = timed(bw)
@@ -410,6 +450,10 @@ def run_table(match: str = ""):
         # one tensor and writes one.
         if kind == "xent":
             c_fw, c_bw = None, c_copy
+        elif kind == "bdr":
+            # fw reads two tensors and writes two, bw reads two or three and writes two: the
+            # read-two-write-one time scaled by the tensor count (same size, same bandwidth)
+            c_fw, c_bw = c_x2 * 4 / 3, c_x2 * (5 if extra["extra"] else 4) / 3
         else:
             c_fw, c_bw = c_copy, c_x2
         rec = {"case": name, "fw_us": round(f_b2b, 2), "bw_us": round(b_b2b, 2),

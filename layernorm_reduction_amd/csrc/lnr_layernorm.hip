@@ -234,7 +234,7 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
 // Backward, vector path: dx plus per-workgroup dgamma/dbeta column partials.
 // part layout: [P][2][C] of Accum<T>; slot 0 = dgamma, slot 1 = dbeta (unused for RMSNorm).
 // ------------------------------------------------------------------------------------------
-template <typename T, int G, int IT, int WG, int DEPTH, int MODE>
+template <typename T, int G, int IT, int WG, int DEPTH, int MODE, bool EXTRA>
 __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>::type *part,
                                                        const T *dy, const T *x,
                                                        const T *__restrict__ gamma,
@@ -248,8 +248,9 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
 #pragma clang fp contract(off)
     static_assert(DEPTH == 1 || DEPTH == 2, "rows fetched ahead: 1 or 2");
     // kBdrLayerNorm: x is the saved s; dx receives ds = (LayerNorm input gradient) + ds_extra
-    // (the residual gradient), dx2 = keep * ds * keep_scale (the gradient of x), and a third
-    // column partial accumulates dbias = sum over rows of dx2.
+    // (the residual gradient; EXTRA says it is given, and it is then fetched with the row),
+    // dx2 = keep * ds * keep_scale (the gradient of x), and a third column partial accumulates
+    // dbias = sum over rows of dx2.
     constexpr bool RMS = MODE == kRmsNorm;
     constexpr bool BDR = MODE == kBdrLayerNorm;
     constexpr int SLOTS = BDR ? 3 : 2;
@@ -297,8 +298,9 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     // branch around the loads the compiler keeps them outstanding. Iterations past the last
     // row are idle rows of zeros, so every group runs the same trip count and multi-wave rows
     // can use barriers.
+    static_assert(!EXTRA || BDR, "ds_extra belongs to the bias-dropout-residual mode");
     struct RowBuf {
-        RV xv[IT], dv[IT];
+        RV xv[IT], dv[IT], ev[EXTRA ? IT : 1];
         uint32_t kb[BDR ? IT : 1];
         float mu, rs;
     };
@@ -320,6 +322,10 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
             if constexpr (BDR) {
                 const uint32_t kl = keep_bits<T>(mask + (live ? row : first_row) * mb, ok ? c : 0);
                 b.kb[k] = ok ? kl : 0u;
+            }
+            if constexpr (EXTRA) {
+                const RV el = load_stream_raw<T>(ds_extra + off);
+                b.ev[k] = ok ? el : zero;
             }
         }
         const int64_t srow = live ? row : first_row;
@@ -380,9 +386,9 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
                         o[e] = rs * __builtin_fmaf(-xh[k][e], bb, gv[k][e] - a);
                 }
                 if constexpr (BDR) {
-                    if (ds_extra != nullptr) {
+                    if constexpr (EXTRA) {
                         float ef[V];
-                        load_stream<T>(ds_extra + base + static_cast<int64_t>(c) * V, ef);
+                        widen<T>(b.ev[k], ef);
 #pragma unroll
                         for (int e = 0; e < V; ++e) o[e] += ef[e];
                     }
@@ -651,16 +657,19 @@ template <> struct LnBwTable<float> {
         {2048, 512, 1, 1024, 1}, {4096, 1024, 1, 1024, 1}, {8192, 1024, 2, 1024, 1}};
 };
 
-// Backward plans of the fused bias-dropout-residual LayerNorm: its third column partial
-// (dbias) does not fit two vectors per lane with two rows in flight at 4096-8192 fp16
-// columns, so those buckets take one vector per lane. fp32 at 8192 columns keeps two
-// vectors per lane at 1024 threads and spills part of its fp64 partials to scratch.
+// Backward plans of the fused bias-dropout-residual LayerNorm. Its third column partial
+// (dbias) and second output cost registers, and two rows fetched ahead no longer fit: with
+// 1024 threads they spill. Measured on MI355X (fp16, N = 16384): from 512 columns up the
+// best plan is two vectors per lane, 512 threads and one row ahead (about 180 VGPRs, two
+// waves per SIMD); at C = 4096 it takes 98 us against 128 us for one vector per lane, at
+// 1024-8192 columns 9-14% less. fp32 at 8192 columns keeps two vectors per lane at 1024
+// threads and spills part of its fp64 partials to scratch.
 template <typename T> struct BdrBwTable;
 template <> struct BdrBwTable<f16> {
     static constexpr LnPlan plans[] = {
         {64, 8, 1, 512, 1},      {128, 16, 1, 512, 1},    {256, 32, 1, 512, 1},
-        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 128, 1, 1024, 1},
-        {2048, 256, 1, 1024, 1}, {4096, 512, 1, 512, 1},  {8192, 1024, 1, 1024, 1}};
+        {512, 32, 2, 512, 1},    {768, 64, 2, 512, 1},    {1024, 64, 2, 512, 1},
+        {2048, 128, 2, 512, 1},  {4096, 256, 2, 512, 1},  {8192, 512, 2, 512, 1}};
 };
 template <> struct BdrBwTable<float> {
     static constexpr LnPlan plans[] = {
@@ -778,6 +787,15 @@ static hipError_t launch_colsum(void *dgamma, void *dbeta, void *dbias, const vo
 constexpr int slots_of(int mode) { return mode == kRmsNorm ? 1 : (mode == kBdrLayerNorm ? 3 : 2); }
 constexpr int stride_of(int mode) { return mode == kBdrLayerNorm ? 3 : 2; }
 
+template <typename T, int G, int IT, int WG, int R, int MODE, bool EXTRA>
+static hipError_t launch_bw_vec(const LnBwArgs &a, hipStream_t st) {
+    return launch(layernorm_bw_vec<T, G, IT, WG, R, MODE, EXTRA>, dim3(static_cast<uint32_t>(a.blocks)),
+                  dim3(WG), st, static_cast<T *>(a.dx), static_cast<typename Accum<T>::type *>(a.part),
+                  static_cast<const T *>(a.dy), static_cast<const T *>(a.x),
+                  static_cast<const T *>(a.gamma), a.mean, a.rstd, a.N, a.C, a.rows_per_block,
+                  static_cast<T *>(a.dx2), static_cast<const T *>(a.ds_extra), a.mask, a.keep_scale);
+}
+
 template <typename T, int MODE, int I>
 static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
     using Table = std::conditional_t<MODE == kBdrLayerNorm, BdrBwTable<T>, LnBwTable<T>>;
@@ -785,12 +803,12 @@ static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
     if (a.C <= p.bucket) {
         static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && (p.R == 1 || p.R == 2), "bad backward plan");
         static_assert(2 * (p.WG / 64) >= 2, "reduction slots");
-        const hipError_t e = launch(
-            layernorm_bw_vec<T, p.G, p.IT, p.WG, p.R, MODE>, dim3(static_cast<uint32_t>(a.blocks)),
-            dim3(p.WG), st, static_cast<T *>(a.dx), static_cast<typename Accum<T>::type *>(a.part),
-            static_cast<const T *>(a.dy), static_cast<const T *>(a.x),
-            static_cast<const T *>(a.gamma), a.mean, a.rstd, a.N, a.C, a.rows_per_block,
-            static_cast<T *>(a.dx2), static_cast<const T *>(a.ds_extra), a.mask, a.keep_scale);
+        hipError_t e;
+        if constexpr (MODE == kBdrLayerNorm)
+            e = a.ds_extra != nullptr ? launch_bw_vec<T, p.G, p.IT, p.WG, p.R, MODE, true>(a, st)
+                                      : launch_bw_vec<T, p.G, p.IT, p.WG, p.R, MODE, false>(a, st);
+        else
+            e = launch_bw_vec<T, p.G, p.IT, p.WG, p.R, MODE, false>(a, st);
         if (e != hipSuccess) return e;
         return launch_colsum<T>(a.dgamma, a.dbeta, a.dbias, a.part, a.blocks, a.C, slots_of(MODE),
                                 stride_of(MODE), st);
