@@ -251,6 +251,18 @@ def table_cases():
                       {"extra": False}))
     cases.append(("bdr-ln [32768,1024] fp32 post-LN", "bdr", (32768, 1024), torch.float32,
                   {"extra": False}))
+    # Mask-aware read skipping: the same softmax, reading only runs with an unmasked key.
+    cases.append(("skip w2 softmax [32,8,256,256] causal fp16", "softmax_skip", (32, 8, 256, 256),
+                  torch.float16, {"causal": True, "mask": False}))
+    for Tk in (256, 512, 1024, 2048):
+        B = W.workload3_batch(Tk)
+        for causal in (True, False):
+            cases.append((f"skip w3 softmax [{B},8,{Tk},{Tk}] {'causal' if causal else 'full'} padded fp16",
+                          "softmax_skip", (B, 8, Tk, Tk), torch.float16, {"causal": causal, "mask": True}))
+    for dt in (torch.float16, torch.float32):
+        tag = "fp16" if dt == torch.float16 else "fp32"
+        cases.append((f"skip w5 softmax [64,16,512,512] padded {tag}", "softmax_skip", (64, 16, 512, 512),
+                      dt, {"causal": False, "mask": True}))
     return cases
 
 
@@ -324,11 +336,12 @@ def run_table(match: str = ""):
         if match not in name:
             continue
         s = W.dtype_size(dt)
-        if kind == "softmax":
+        dense = None
+        if kind in ("softmax", "softmax_skip"):
             B, H, T, _ = shape
             per = B * H * T * T * s
             n = max(2, math.ceil(MIN_FOOTPRINT / (4 * per)))
-            fw, bw = [], []
+            fw, bw, dfw, dbw = [], [], [], []
             keep = []
             for _ in range(n):
                 x = torch.randn(shape, device=dev, dtype=dt, generator=g)
@@ -338,11 +351,22 @@ def run_table(match: str = ""):
                 if extra["mask"]:
                     m = torch.zeros(B, T, device=dev, dtype=dt)
                     m[:, T * 3 // 4:] = float("-inf")
-                fw.append(lnr.bind_attn_softmax_fw(x, m, extra["causal"], y))
-                bw.append(lnr.bind_attn_softmax_bw(dy, y, dx))
+                dfw.append(lnr.bind_attn_softmax_fw(x, m, extra["causal"], y))
+                dbw.append(lnr.bind_attn_softmax_bw(dy, y, dx))
+                if kind == "softmax_skip":
+                    fw.append(lnr.bind_attn_softmax_fw_skip(x, m, extra["causal"], y))
+                    bw.append(lnr.bind_attn_softmax_bw_skip(dy, y, m, extra["causal"], dx))
                 keep += [x, dy, y, dx, m]
             bf = W.softmax_fw_bytes(B, H, T, T, s, has_mask=extra["mask"])
             bb = W.softmax_bw_bytes(B, H, T, T, s)
+            if kind == "softmax":
+                fw, bw = dfw, dbw
+            else:
+                # HBM figures use the bytes the skipping kernels move; the dense figures are
+                # kept apart as dense-equivalent rates.
+                dense = (dfw, dbw, bf, bb)
+                bf, bb = W.softmax_skip_bytes(keep[4].cpu() if extra["mask"] else None,
+                                              extra["causal"], B, H, T, T, s)
             rows, tensor = B * H * T, per
         elif kind == "layernorm":
             N, C = shape
@@ -442,6 +466,16 @@ def run_table(match: str = ""):
         torch.cuda.synchronize()
         f_b2b, f_k = timed(fw)
         b_b2b, b_k = timed(bw)
+        skip_rec = None
+        if dense is not None:
+            dfw, dbw, dbf, dbb = dense
+            df_b2b, _ = timed(dfw)
+            db_b2b, _ = timed(dbw)
+            skip_rec = {"dense_fw_us": round(df_b2b, 2), "dense_bw_us": round(db_b2b, 2),
+                        "dense_equivalent_GBps": round((dbf + dbb) / (f_b2b + b_b2b) * 1e-3, 1),
+                        "dense_bytes_fw": dbf, "dense_bytes_bw": dbb,
+                        "speedup_fwbw_vs_dense": round((df_b2b + db_b2b) / (f_b2b + b_b2b), 3)}
+            del dfw, dbw, dense
         del keep, fw, bw
         torch.cuda.empty_cache()
         c_copy, c_x2 = ceiling(tensor)
@@ -450,6 +484,8 @@ def run_table(match: str = ""):
         # one tensor and writes one.
         if kind == "xent":
             c_fw, c_bw = None, c_copy
+        elif kind == "softmax_skip":
+            c_fw, c_bw = None, None       # a dense-size ceiling does not bound a skipping kernel
         elif kind == "bdr":
             # fw reads two tensors and writes two, bw reads two or three and writes two: the
             # read-two-write-one time scaled by the tensor count (same size, same bandwidth)
@@ -465,14 +501,21 @@ def run_table(match: str = ""):
                "ceiling_copy_us": round(c_copy, 2), "ceiling_read2write1_us": round(c_x2, 2),
                "fwbw_frac_of_ceiling": (round((c_fw + c_bw) / (f_b2b + b_b2b), 4)
                                         if c_fw is not None else None),
-               "bw_frac_of_ceiling": round(c_bw / b_b2b, 4),
+               "bw_frac_of_ceiling": round(c_bw / b_b2b, 4) if c_bw is not None else None,
                "bytes_fw": bf, "bytes_bw": bb, "input_sets": n}
+        if skip_rec is not None:
+            rec.update(skip_rec)
         print(json.dumps(rec), flush=True)
         log(f"{name:48s} fw {f_b2b:8.1f} us {rec['fw_GBps']:7.0f} GB/s | bw {b_b2b:8.1f} us "
             f"{rec['bw_GBps']:7.0f} GB/s | fw+bw {rec['fwbw_GBps']:7.0f} GB/s "
             f"({rec['fwbw_frac_of_peak']:.0%} of 8 TB/s; same-size ceiling: "
             + (f"fw+bw {rec['fwbw_frac_of_ceiling']:.0%}" if rec['fwbw_frac_of_ceiling'] is not None
-               else f"bw {rec['bw_frac_of_ceiling']:.0%}") + ")")
+               else (f"bw {rec['bw_frac_of_ceiling']:.0%}" if rec['bw_frac_of_ceiling'] is not None
+                     else "n/a")) + ")")
+        if skip_rec is not None:
+            log(f"{'':48s} dense fw {skip_rec['dense_fw_us']:8.1f} us | bw {skip_rec['dense_bw_us']:8.1f} us"
+                f" | skip fw+bw {skip_rec['speedup_fwbw_vs_dense']:.2f}x faster, dense-equivalent "
+                f"{skip_rec['dense_equivalent_GBps']:7.0f} GB/s")
 
 
 def cpu_model() -> str:

@@ -253,6 +253,33 @@ LNR_API int bdr_layernorm_bw(void *dresidual, void *dx, void *dgamma, void *dbet
                              void *stream);
 
 /*
+ * attn_softmax_fw_skip / attn_softmax_bw_skip -- attn_softmax_fw / attn_softmax_bw that do not
+ * read score vectors whose keys are all masked.
+ * [HW4 "Problem structure and scoring": future tokens and padded keys are -inf, so their
+ *  probabilities are exactly 0; FastTransformer section 3 "The Surprising Bottleneck": the
+ *  materialised probability tensor's HBM traffic is the attention cost.]
+ *
+ *   Same arguments, layout, limits, aliasing and errors as attn_softmax_fw, and for the
+ *   backward as attn_softmax_bw plus the forward's mask and causal flag. A 16-byte run of a
+ *   row (8 fp16 or 4 fp32 elements) whose keys all lie after the query (causal) or all carry a
+ *   -inf mask entry is not read: the forward takes its scores as -inf and writes its zeros;
+ *   the backward writes zeros there without reading y or dy. Every element of the outputs is
+ *   written.
+ *   Results equal attn_softmax_fw's (forward) when the skipped scores are finite, and
+ *   attn_softmax_bw's (backward, up to the sign of zero) when out_fw is 0 and dout is finite at
+ *   the skipped positions -- which holds when out_fw is the forward's output for the same mask
+ *   and causal flag. Rows whose byte length is not a multiple of 16, or buffers not 16-byte
+ *   aligned, run the dense entry points (no skipping, same results).
+ *   Only exact -inf mask entries are skipped; a large finite negative mask is read as usual.
+ */
+LNR_API int attn_softmax_fw_skip(void *out, const void *inp, const void *mask, int64_t B,
+                                 int64_t H, int64_t Tq, int64_t Tk, int causal, lnr_dtype dtype,
+                                 void *stream);
+LNR_API int attn_softmax_bw_skip(void *dinp, const void *dout, const void *out_fw,
+                                 const void *mask, int64_t B, int64_t H, int64_t Tq, int64_t Tk,
+                                 int causal, lnr_dtype dtype, void *stream);
+
+/*
  * cross_entropy_fw_workspace_bytes -- device workspace cross_entropy_fw needs for (N, V,
  * dtype): per-chunk partial (max, sum) pairs when there are too few rows to fill the GPU and
  * each row is split over several workgroups; 0 when rows are not split (the common case of

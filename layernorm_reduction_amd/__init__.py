@@ -81,6 +81,8 @@ def load():
     vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.attn_softmax_fw.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
     lib.attn_softmax_bw.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, vp]
+    lib.attn_softmax_fw_skip.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
+    lib.attn_softmax_bw_skip.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
     lib.layernorm_fw.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ctypes.c_float, ci, vp]
     lib.layernorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
     lib.layernorm_bw_workspace_bytes.restype = sz
@@ -221,6 +223,56 @@ def attn_softmax_bw(dout, out_fw, dinp=None):
     st = load().attn_softmax_bw(_ptr(dinp), _ptr(dout), _ptr(out_fw), B, H, Tq, Tk,
                                 _dtype_code(dout), _stream(dout))
     _check(st, "attn_softmax_bw")
+    return dinp
+
+
+def _softmax_mask(mask, like, B, Tk):
+    if mask is not None:
+        _dev(mask, "mask", like=like)
+        if tuple(mask.shape) != (B, Tk):
+            raise ValueError(f"mask must be [B, Tk] = [{B}, {Tk}], got {tuple(mask.shape)}")
+
+
+def attn_softmax_fw_skip(inp, mask=None, causal: bool = False, out=None):
+    """attn_softmax_fw that does not read 16-byte score runs whose keys are all masked
+    (after the query when causal, or under -inf mask entries); writes every element."""
+    torch = _torch()
+    _dev(inp, "inp")
+    if inp.dim() != 4:
+        raise ValueError("inp must be [B, H, Tq, Tk]")
+    B, H, Tq, Tk = inp.shape
+    _softmax_mask(mask, inp, B, Tk)
+    if out is None:
+        out = torch.empty_like(inp)
+    else:
+        _dev(out, "out", like=inp)
+        if out.shape != inp.shape:
+            raise ValueError("out must have the shape of inp")
+    st = load().attn_softmax_fw_skip(_ptr(out), _ptr(inp), _ptr(mask), B, H, Tq, Tk,
+                                     int(bool(causal)), _dtype_code(inp), _stream(inp))
+    _check(st, "attn_softmax_fw_skip")
+    return out
+
+
+def attn_softmax_bw_skip(dout, out_fw, mask=None, causal: bool = False, dinp=None):
+    """attn_softmax_bw that neither reads y nor dout on 16-byte runs whose keys the forward
+    masked (same mask and causal flag as the forward); writes zeros there."""
+    torch = _torch()
+    _dev(dout, "dout")
+    _dev(out_fw, "out_fw", like=dout)
+    if dout.dim() != 4 or out_fw.shape != dout.shape:
+        raise ValueError("dout and out_fw must both be [B, H, Tq, Tk]")
+    B, H, Tq, Tk = dout.shape
+    _softmax_mask(mask, dout, B, Tk)
+    if dinp is None:
+        dinp = torch.empty_like(dout)
+    else:
+        _dev(dinp, "dinp", like=dout)
+        if dinp.shape != dout.shape:
+            raise ValueError("dinp must have the shape of dout")
+    st = load().attn_softmax_bw_skip(_ptr(dinp), _ptr(dout), _ptr(out_fw), _ptr(mask), B, H, Tq,
+                                     Tk, int(bool(causal)), _dtype_code(dout), _stream(dout))
+    _check(st, "attn_softmax_bw_skip")
     return dinp
 
 
@@ -598,6 +650,23 @@ def bind_attn_softmax_bw(dout, out_fw, dinp):
     args = (dinp.data_ptr(), dout.data_ptr(), out_fw.data_ptr(), B, H, Tq, Tk, _dtype_code(dout),
             _stream(dout))
     return BoundCall("attn_softmax_bw", load().attn_softmax_bw, args, (dout, out_fw, dinp))
+
+
+def bind_attn_softmax_fw_skip(inp, mask, causal, out):
+    attn_softmax_fw_skip(inp, mask, causal, out)
+    B, H, Tq, Tk = inp.shape
+    args = (out.data_ptr(), inp.data_ptr(), _ptr(mask), B, H, Tq, Tk, int(bool(causal)),
+            _dtype_code(inp), _stream(inp))
+    return BoundCall("attn_softmax_fw_skip", load().attn_softmax_fw_skip, args, (inp, mask, out))
+
+
+def bind_attn_softmax_bw_skip(dout, out_fw, mask, causal, dinp):
+    attn_softmax_bw_skip(dout, out_fw, mask, causal, dinp)
+    B, H, Tq, Tk = dout.shape
+    args = (dinp.data_ptr(), dout.data_ptr(), out_fw.data_ptr(), _ptr(mask), B, H, Tq, Tk,
+            int(bool(causal)), _dtype_code(dout), _stream(dout))
+    return BoundCall("attn_softmax_bw_skip", load().attn_softmax_bw_skip, args,
+                     (dout, out_fw, mask, dinp))
 
 
 def bind_layernorm_fw(x, gamma, beta, eps, y, mean, rstd):

@@ -1,0 +1,360 @@
+// lnr_softmax_skip.hip -- attention softmax forward and backward that read only the score
+// vectors holding at least one key the row may attend to.
+//
+// Method: "CMU 11-868 HW4: Softmax and LayerNorm as fused CUDA kernels", section "Problem
+// structure and scoring" (future tokens set to -inf, the attention mask added, then the row max
+// and the sum of exponentials), and "FastTransformer: Breaking the Compiler Ceiling via
+// Architectural Co-Design", section 3 "The Surprising Bottleneck" (the materialised
+// probability tensor's HBM traffic is the attention cost). A key after the query (causal) or
+// under a -inf mask entry contributes exp(-inf) = 0 to the row sum and has probability
+// exactly 0. So a 16-byte vector whose keys are all such keys need not be read:
+//   * forward: its scores are taken as -inf without a load, and its zeros are written;
+//   * backward: y is 0 there, so dx = y * (dy - t) = 0 and neither y nor dy is read.
+// Everything else is the dense kernels' arithmetic in the same order, so for finite scores
+// (forward) and for y = 0 with finite dy at the skipped keys (backward) the results equal the
+// dense entry points' (up to the sign of zero). Rows keep the dense layout: G lanes of one
+// wave hold a row, vector k of lane l covers elements [(k*G + l)*V, +V). Skipping is per
+// lane, and a row's skipped vectors form whole tails of 16-byte runs (causal) or the padded
+// tail (key-padding masks), so whole cache lines are never fetched.
+//
+// The causal limit is an index test. The mask test needs the mask vector first: it is read
+// through the caches (one [B, Tk] row serves all H*Tq rows of a batch), and the score load
+// waits for it. Each conditional load fills a raw 16-byte register vector that already holds
+// the skipped value, and nothing is converted until every load of the row is issued: a
+// conversion inside the branch would make the compiler wait for each load in turn.
+#include <math.h>
+
+#include <type_traits>
+
+#include "lnr_common.h"
+#include "lnr_fastdiv.h"
+#include "lnr_prims.h"
+
+namespace lnr {
+
+constexpr int64_t kSkipMaxRows = int64_t{UINT32_MAX} - 4096;
+
+// True when some element of the mask vector is not -inf (the vector has a key to read).
+template <typename T>
+__device__ __forceinline__ bool any_open(const RawVec<T> &m) {
+    bool open = false;
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::N; ++e) open |= static_cast<float>(m[e]) != -INFINITY;
+    return open;
+}
+
+template <typename T>
+__device__ __forceinline__ RawVec<T> splat(float v) {
+    RawVec<T> r;
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::N; ++e) r[e] = static_cast<T>(v);
+    return r;
+}
+
+// need[k] &= the mask vector k of the row has an open key; the mask vectors come back in m.
+// Mask reads hit the caches, so they are issued for every k (a lane with nothing to read
+// loads the row's first vector, which always exists) and the result is selected afterwards.
+template <typename T, int G, int IT>
+__device__ __forceinline__ void mask_runs(const T *mrow, int lane, bool (&need)[IT],
+                                          RawVec<T> (&m)[IT]) {
+    constexpr int V = Vec16<T>::N;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const RawVec<T> l = load_keep_raw<T>(mrow + (need[k] ? static_cast<int64_t>(k * G + lane) * V : 0));
+        m[k] = need[k] ? l : splat<T>(-INFINITY);
+    }
+#pragma unroll
+    for (int k = 0; k < IT; ++k) need[k] = need[k] && any_open<T>(m[k]);
+}
+
+template <typename T, int G, int IT, int WG>
+__global__ __launch_bounds__(WG) void softmax_fw_skip(T *out, const T *inp,
+                                                      const T *__restrict__ mask, uint32_t rows,
+                                                      int32_t Tk, DivU32 per_batch,
+                                                      DivU32 per_query, int32_t causal) {
+    constexpr int V = Vec16<T>::N;
+    constexpr int RPB = WG / G;
+    const int lane = threadIdx.x % G;
+    const uint32_t row = blockIdx.x * static_cast<uint32_t>(RPB) + threadIdx.x / G;
+    const bool live = row < rows;
+    const uint32_t r = live ? row : 0u;
+    const int nvec = Tk / V;
+    const int64_t base = static_cast<int64_t>(r) * Tk;
+    // Keys [0, kend) may be attended to: all of them, or 0..query index when causal (Tq = Tk).
+    const int qi = static_cast<int>(r - divu32(r, per_query) * per_query.d);
+    const int kend = causal ? qi + 1 : Tk;
+
+    bool need[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        need[k] = live && c < nvec && c * V < kend;
+    }
+    RawVec<T> m[IT];
+    if (mask != nullptr)
+        mask_runs<T, G, IT>(mask + static_cast<int64_t>(divu32(r, per_batch)) * Tk, lane, need, m);
+    RawVec<T> xr[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        xr[k] = splat<T>(-INFINITY);
+        if (need[k]) xr[k] = load_stream_raw<T>(inp + base + static_cast<int64_t>(k * G + lane) * V);
+    }
+    float z[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        widen<T>(xr[k], z[k]);
+        if (mask != nullptr && need[k]) {
+            float mf[V];
+            widen<T>(m[k], mf);
+#pragma unroll
+            for (int e = 0; e < V; ++e) z[k][e] += mf[e];
+        }
+    }
+    if (causal) {
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if ((k * G + lane) * V + e > qi) z[k][e] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) mx = fmaxf(mx, z[k][e]);
+    mx = group_allreduce<G>(mx, OpMax());
+    if (mx == -INFINITY) mx = 0.f;  // fully masked (or idle) row: every exponential is 0
+
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            z[k][e] = exp_nonpos(z[k][e] - mx);
+            s += z[k][e];
+        }
+    s = group_allreduce<G>(s, OpSum());
+    const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
+
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (live && c < nvec) {
+            float y[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) y[e] = z[k][e] * inv;
+            store_stream<T>(out + base + static_cast<int64_t>(c) * V, y);
+        }
+    }
+}
+
+template <typename T, int G, int IT, int WG>
+__global__ __launch_bounds__(WG) void softmax_bw_skip(T *dinp, const T *dout,
+                                                      const T *__restrict__ y,
+                                                      const T *__restrict__ mask, uint32_t rows,
+                                                      int32_t Tk, DivU32 per_batch,
+                                                      DivU32 per_query, int32_t causal) {
+    constexpr int V = Vec16<T>::N;
+    constexpr int RPB = WG / G;
+    const int lane = threadIdx.x % G;
+    const uint32_t row = blockIdx.x * static_cast<uint32_t>(RPB) + threadIdx.x / G;
+    const bool live = row < rows;
+    const uint32_t r = live ? row : 0u;
+    const int nvec = Tk / V;
+    const int64_t base = static_cast<int64_t>(r) * Tk;
+    const int kend = causal ? static_cast<int>(r - divu32(r, per_query) * per_query.d) + 1 : Tk;
+
+    bool need[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        need[k] = live && c < nvec && c * V < kend;
+    }
+    if (mask != nullptr) {
+        RawVec<T> m[IT];
+        mask_runs<T, G, IT>(mask + static_cast<int64_t>(divu32(r, per_batch)) * Tk, lane, need, m);
+    }
+    RawVec<T> yr[IT], gr[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        yr[k] = gr[k] = splat<T>(0.f);
+        if (need[k]) {
+            const int64_t off = base + static_cast<int64_t>(k * G + lane) * V;
+            yr[k] = load_stream_raw<T>(y + off);
+            gr[k] = load_stream_raw<T>(dout + off);
+        }
+    }
+    float yv[IT][V], gv[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        widen<T>(yr[k], yv[k]);
+        widen<T>(gr[k], gv[k]);
+    }
+    // The dense kernel's product sum is a chain of fused multiply-adds. With the fp16 widening
+    // next to the multiply, the compiler would pair two products of widened fp16 values into
+    // a dot2 instruction, which rounds differently (measured: results then differ from the
+    // dense kernel's in the last bit). An empty register constraint hides the widened values
+    // from that combine; it emits no instruction.
+    if constexpr (V == 8) {
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+#pragma unroll
+            for (int e = 0; e < V; ++e) asm("" : "+v"(yv[k][e]), "+v"(gv[k][e]));
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) t += yv[k][e] * gv[k][e];
+    t = group_allreduce<G>(t, OpSum());
+
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int c = k * G + lane;
+        if (live && c < nvec) {
+            float d[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) d[e] = yv[k][e] * (gv[k][e] - t);
+            store_stream<T>(dinp + base + static_cast<int64_t>(c) * V, d);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Row-length buckets (G lanes per row, IT vectors per lane), the HW4 page's template list.
+// ------------------------------------------------------------------------------------------
+struct SkipPlan {
+    int bucket;
+    int G;
+    int IT;
+    int WG;
+};
+
+template <typename T> struct SkipFwTable;
+template <> struct SkipFwTable<f16> {
+    static constexpr SkipPlan plans[] = {{32, 4, 1, 512},   {64, 8, 1, 512},   {128, 8, 2, 256},
+                                         {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 32, 2, 256},
+                                         {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
+};
+template <> struct SkipFwTable<float> {
+    static constexpr SkipPlan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 8, 4, 256},
+                                         {256, 16, 4, 256}, {384, 32, 3, 256}, {512, 32, 4, 256},
+                                         {768, 64, 3, 256}, {1024, 64, 4, 256}, {2048, 64, 8, 256}};
+};
+template <typename T> struct SkipBwTable;
+template <> struct SkipBwTable<f16> {
+    static constexpr SkipPlan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 256},
+                                         {256, 32, 1, 256}, {384, 16, 3, 256}, {512, 64, 1, 128},
+                                         {768, 32, 3, 256}, {1024, 64, 2, 128}, {2048, 64, 4, 128}};
+};
+template <> struct SkipBwTable<float> {
+    static constexpr SkipPlan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 256},
+                                         {256, 64, 1, 128}, {384, 32, 3, 256}, {512, 64, 2, 128},
+                                         {768, 64, 3, 128}, {1024, 64, 4, 128}, {2048, 64, 8, 128}};
+};
+
+struct SkipArgs {
+    void *out;         // fw: y;    bw: dinp
+    const void *a;     // fw: inp;  bw: dout
+    const void *b;     // fw: -;    bw: y
+    const void *mask;  // [B, Tk] or null
+    int64_t rows;
+    int32_t Tq, Tk;
+    int64_t rows_per_batch;
+    int32_t causal;
+};
+
+template <typename T, int I, bool BW>
+static hipError_t dispatch_skip(const SkipArgs &a, hipStream_t st) {
+    using Table = std::conditional_t<BW, SkipBwTable<T>, SkipFwTable<T>>;
+    constexpr SkipPlan p = Table::plans[I];
+    if (a.Tk <= p.bucket) {
+        constexpr int RPB = p.WG / p.G;
+        const dim3 grid(static_cast<uint32_t>((a.rows + RPB - 1) / RPB));
+        const DivU32 pb = make_divu32(static_cast<uint32_t>(a.rows_per_batch));
+        const DivU32 pq = make_divu32(static_cast<uint32_t>(a.Tq));
+        if constexpr (BW)
+            return launch(softmax_bw_skip<T, p.G, p.IT, p.WG>, grid, dim3(p.WG), st,
+                          static_cast<T *>(a.out), static_cast<const T *>(a.a),
+                          static_cast<const T *>(a.b), static_cast<const T *>(a.mask),
+                          static_cast<uint32_t>(a.rows), a.Tk, pb, pq, a.causal);
+        else
+            return launch(softmax_fw_skip<T, p.G, p.IT, p.WG>, grid, dim3(p.WG), st,
+                          static_cast<T *>(a.out), static_cast<const T *>(a.a),
+                          static_cast<const T *>(a.mask), static_cast<uint32_t>(a.rows), a.Tk, pb,
+                          pq, a.causal);
+    }
+    if constexpr (I + 1 < static_cast<int>(sizeof(Table::plans) / sizeof(SkipPlan)))
+        return dispatch_skip<T, I + 1, BW>(a, st);
+    return hipErrorInvalidValue;
+}
+
+// Shape, dtype, null, alignment and alias checks shared by both entry points (the same rules
+// as attn_softmax_fw / attn_softmax_bw, plus the mask against the output). The forward passes
+// b = a (its one input, which out may equal); the backward's out must not overlap b (y).
+static int check_skip(void *out, const void *a, const void *b, const void *mask, int64_t B,
+                      int64_t H, int64_t Tq, int64_t Tk, int causal, lnr_dtype dtype, bool bw) {
+    if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
+    if (B < 0 || H < 0 || Tq < 0 || Tk < 1) return LNR_ERR_SHAPE;
+    if (Tk > LNR_SOFTMAX_MAX_TK || Tq > INT32_MAX) return LNR_ERR_UNSUPPORTED;
+    if (H > 0 && Tq > 0 && B > INT64_MAX / H / Tq) return LNR_ERR_UNSUPPORTED;
+    if (causal && Tq != Tk) return LNR_ERR_SHAPE;
+    const int64_t rows = B * H * Tq;
+    if (rows == 0) return LNR_OK;
+    if (out == nullptr || a == nullptr || b == nullptr) return LNR_ERR_NULL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned_to(out, es) || !aligned_to(a, es) || !aligned_to(b, es) ||
+        (mask != nullptr && !aligned_to(mask, es)))
+        return LNR_ERR_ALIGN;
+    const size_t nbytes = static_cast<size_t>(rows) * static_cast<size_t>(Tk) * es;
+    if (bad_alias(out, a, nbytes)) return LNR_ERR_ALIAS;
+    if (bw && overlap(out, nbytes, b, nbytes)) return LNR_ERR_ALIAS;
+    if (mask != nullptr && overlap(out, nbytes, mask, static_cast<size_t>(B * Tk) * es))
+        return LNR_ERR_ALIAS;
+    return LNR_OK;
+}
+
+static bool skip_vec_ok(const void *out, const void *a, const void *b, const void *mask,
+                        int64_t rows, int64_t Tk, lnr_dtype dtype) {
+    return (static_cast<size_t>(Tk) * dtype_size(dtype)) % 16 == 0 && aligned_to(out, 16) &&
+           aligned_to(a, 16) && aligned_to(b, 16) && (mask == nullptr || aligned_to(mask, 16)) &&
+           rows <= kSkipMaxRows;
+}
+
+}  // namespace lnr
+
+using namespace lnr;
+
+extern "C" int attn_softmax_fw_skip(void *out, const void *inp, const void *mask, int64_t B,
+                                    int64_t H, int64_t Tq, int64_t Tk, int causal,
+                                    lnr_dtype dtype, void *stream) {
+    const int st = check_skip(out, inp, inp, mask, B, H, Tq, Tk, causal, dtype, false);
+    if (st != LNR_OK) return st;
+    const int64_t rows = B * H * Tq;
+    if (rows == 0) return LNR_OK;
+    if (!skip_vec_ok(out, inp, inp, mask, rows, Tk, dtype))
+        return attn_softmax_fw(out, inp, mask, B, H, Tq, Tk, causal, dtype, stream);
+    const SkipArgs a{out, inp, nullptr, mask, rows, static_cast<int32_t>(Tq), static_cast<int32_t>(Tk),
+                     H * Tq, causal ? 1 : 0};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return status_of(dtype == LNR_F16 ? dispatch_skip<f16, 0, false>(a, s)
+                                      : dispatch_skip<float, 0, false>(a, s));
+}
+
+extern "C" int attn_softmax_bw_skip(void *dinp, const void *dout, const void *out_fw,
+                                    const void *mask, int64_t B, int64_t H, int64_t Tq,
+                                    int64_t Tk, int causal, lnr_dtype dtype, void *stream) {
+    const int st = check_skip(dinp, dout, out_fw, mask, B, H, Tq, Tk, causal, dtype, true);
+    if (st != LNR_OK) return st;
+    const int64_t rows = B * H * Tq;
+    if (rows == 0) return LNR_OK;
+    if (!skip_vec_ok(dinp, dout, out_fw, mask, rows, Tk, dtype))
+        return attn_softmax_bw(dinp, dout, out_fw, B, H, Tq, Tk, dtype, stream);
+    const SkipArgs a{dinp, dout, out_fw, mask, rows, static_cast<int32_t>(Tq),
+                     static_cast<int32_t>(Tk), H * Tq, causal ? 1 : 0};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return status_of(dtype == LNR_F16 ? dispatch_skip<f16, 0, true>(a, s)
+                                      : dispatch_skip<float, 0, true>(a, s));
+}

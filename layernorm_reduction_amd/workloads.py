@@ -337,6 +337,33 @@ def softmax_bw_bytes(B, H, Tq, Tk, s) -> int:
     return 3 * B * H * Tq * Tk * s
 
 
+def softmax_open_runs(mask, causal, B, H, Tq, Tk, V) -> int:
+    """Number of 16-byte runs (V elements) of a [B, H, Tq, Tk] score tensor that hold at least
+    one key the row may attend to: not after the query when causal, not under a -inf entry of
+    the [B, Tk] mask (a CPU tensor or None). The skipping kernels read exactly these runs."""
+    import numpy as np
+    nr = Tk // V
+    if mask is None:
+        per_q = np.minimum(np.arange(Tq) // V + 1, nr) if causal else np.full(Tq, nr)
+        return int(per_q.sum()) * H * B
+    openk = (mask.float().numpy() != -np.inf)[:, : nr * V].reshape(B, nr, V).any(axis=2)
+    if not causal:
+        return int(openk.sum()) * Tq * H
+    # runs 0 .. q // V lie before or at query q
+    cum = np.concatenate([np.zeros((B, 1), np.int64), np.cumsum(openk, axis=1)], axis=1)
+    lim = np.minimum(np.arange(Tq) // V + 1, nr)
+    return int(cum[:, lim].sum()) * H
+
+
+def softmax_skip_bytes(mask, causal, B, H, Tq, Tk, s) -> tuple[int, int]:
+    """(fw, bw) bytes the skipping kernels move: the open runs read (once forward, y and dy
+    backward), every output element written, and the mask once when given."""
+    runs = softmax_open_runs(mask, causal, B, H, Tq, Tk, 16 // s)
+    E = B * H * Tq * Tk
+    mb = B * Tk * s if mask is not None else 0
+    return runs * 16 + E * s + mb, 2 * runs * 16 + E * s + mb
+
+
 def layernorm_fw_bytes(N, C, s) -> int:
     """Read x, write y, write fp32 mean and rstd, read gamma and beta."""
     return 2 * N * C * s + 8 * N + 2 * C * s

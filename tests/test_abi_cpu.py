@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -66,6 +66,35 @@ def sfw(lib, out=A, inp=A + 2 ** 30, mask=None, B=2, H=2, Tq=16, Tk=16, causal=0
 
 def sbw(lib, dinp=A, dout=A + 2 ** 30, y=A + 2 ** 31, B=2, H=2, Tq=16, Tk=16, dtype=F16):
     return lib.attn_softmax_bw(dinp, dout, y, B, H, Tq, Tk, dtype, None)
+
+
+def test_softmax_skip_validation(lib):
+    """The skipping entry points apply the dense ones' rules, and the backward's mask and
+    causal flag are checked like the forward's."""
+    def fw(out=A, inp=A + 2 ** 30, mask=None, B=2, H=2, Tq=16, Tk=16, causal=0, dtype=F16):
+        return lib.attn_softmax_fw_skip(out, inp, mask, B, H, Tq, Tk, causal, dtype, None)
+
+    def bw(dinp=A, dout=A + 2 ** 30, y=A + 2 ** 31, mask=None, B=2, H=2, Tq=16, Tk=16, causal=0,
+           dtype=F16):
+        return lib.attn_softmax_bw_skip(dinp, dout, y, mask, B, H, Tq, Tk, causal, dtype, None)
+
+    for f in (fw, bw):
+        assert f(dtype=7) == DTYPE
+        assert f(Tk=0) == SHAPE
+        assert f(B=-1) == SHAPE
+        assert f(Tk=2049) == UNSUP
+        assert f(Tq=8, causal=1) == SHAPE
+        assert f(out=None) == NULL if f is fw else f(dinp=None) == NULL
+        assert f(mask=A + 2 ** 32 + 1) == ALIGN                 # odd mask address for fp16
+        assert f(B=0) == OK and f(Tq=0) == OK                     # empty: nothing launched
+    assert fw(inp=None) == NULL
+    assert fw(inp=A + 1) == ALIGN
+    assert fw(out=A + 2, inp=A) == ALIAS                          # partial overlap
+    assert fw(mask=A + 64) == ALIAS                               # mask inside the output
+    assert bw(y=None) == NULL
+    assert bw(dout=A + 2) == ALIAS                                # dinp partly over dout
+    assert bw(y=A) == ALIAS                                       # dinp over y
+    assert bw(mask=A + 64) == ALIAS
 
 
 def test_softmax_fw_validation(lib):

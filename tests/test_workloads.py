@@ -45,3 +45,31 @@ def test_byte_formulas():
     assert W.layernorm_bw_bytes(8192, 256, s) == 3 * 8192 * 256 * s + 8 * 8192 + 3 * 256 * s
     assert W.softmax_fw_bytes(64, 16, 512, 512, s) == 2 * 64 * 16 * 512 * 512 * s + 64 * 512 * s
     assert math.isclose(W.softmax_bw_bytes(32, 8, 256, 256, 2) / 1e6, 100.663296)
+
+
+def test_softmax_open_runs_counts_like_brute_force():
+    """The skipping kernels' byte count: runs of V keys with at least one key that is neither
+    after the query (causal) nor under a -inf mask entry, counted one by one on small cases."""
+    import numpy as np
+
+    def brute(mask, causal, B, H, Tq, Tk, V):
+        n = 0
+        for b in range(B):
+            for q in range(Tq):
+                for r in range(Tk // V):
+                    n += any((not causal or k <= q) and (mask is None or mask[b, k] != -np.inf)
+                             for k in range(r * V, r * V + V))
+        return n * H
+
+    for causal in (False, True):
+        for Tk, V in ((64, 8), (48, 4), (72, 8)):
+            B, H = 3, 2
+            m = torch.zeros(B, Tk)
+            m[0, 20:] = -float("inf")
+            m[2, :] = -float("inf")
+            m[1, 5] = -float("inf")
+            assert W.softmax_open_runs(m, causal, B, H, Tk, Tk, V) == brute(m.numpy(), causal, B, H, Tk, Tk, V)
+            assert W.softmax_open_runs(None, causal, B, H, Tk, Tk, V) == brute(None, causal, B, H, Tk, Tk, V)
+    fw, bw = W.softmax_skip_bytes(None, False, 2, 3, 16, 64, 2)
+    assert fw == W.softmax_fw_bytes(2, 3, 16, 64, 2, has_mask=False)     # nothing to skip
+    assert bw == W.softmax_bw_bytes(2, 3, 16, 64, 2)
