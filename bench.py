@@ -59,6 +59,14 @@ def parse():
     p.add_argument("--cpu-table", action="store_true",
                    help="CPU only: time the oracle's fw+bw on the tiny, GPT-2 and hidden-size-sweep "
                         "shapes with all host threads and with one thread; one JSON line per case")
+    p.add_argument("--skip-traffic", action="store_true",
+                   help="run the dense and the read-skipping softmax kernels on three masked "
+                        "workloads (plus the 1 GiB calibration copy) for counter collection; one "
+                        "JSON line per case with the analytic bytes of both")
+    p.add_argument("--summarize-skip-traffic", metavar="DIR",
+                   help="CPU only: read pmc_fetch_skip/ and pmc_write_skip/ under DIR and the "
+                        "--skip-traffic output DIR/skip_traffic.jsonl; write "
+                        "profiles/softmax_skip_traffic.md")
     p.add_argument("--summarize-profiles", metavar="DIR",
                    help="CPU only: read the rocprofv3 outputs under DIR (prof_<w>/, pmc_fetch_<w>/, "
                         "pmc_write_<w>/) and write the summaries under profiles/")
@@ -72,6 +80,104 @@ PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc
            "--steps 20 --warmup 5 --no-cpu-baseline")
 DOMINANT = "softmax_bw_vec"
 COPY = "copy16"
+SKIP_PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {ctr} -f csv "
+                "-d $REPO/gpurun_out/pmc_{kind}_skip -o skip -- python3 $REPO/bench.py --skip-traffic")
+
+
+def skip_traffic_cases():
+    """(name, B, H, T, dtype, causal, padded): the GPT-2 causal scores, a row-length-sweep shape
+    with causal and padding masks, and the padded encoder shape."""
+    import torch
+    return [("w2 [32,8,256,256] causal", 32, 8, 256, torch.float16, True, False),
+            ("w3 [16,8,1024,1024] causal padded", 16, 8, 1024, torch.float16, True, True),
+            ("w5 [64,16,512,512] padded", 64, 16, 512, torch.float16, False, True)]
+
+
+def run_skip_traffic():
+    """Dense and skipping softmax kernels, 3 launches each per case, after the 1 GiB streaming
+    copy that calibrates the counters. Padded masks keep the first 3/4 of the keys."""
+    import torch
+    import layernorm_reduction_amd as lnr
+    from layernorm_reduction_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        lnr.copy_bytes(b, a)
+    torch.cuda.synchronize()
+    del a, b
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    for name, B, H, T, dt, causal, padded in skip_traffic_cases():
+        x = torch.randn(B, H, T, T, device=dev, dtype=dt, generator=g)
+        dy = torch.randn_like(x)
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        m = None
+        if padded:
+            m = torch.zeros(B, T, device=dev, dtype=dt)
+            m[:, T * 3 // 4:] = float("-inf")
+        for _ in range(3):
+            lnr.attn_softmax_fw(x, m, causal, out=y)
+            lnr.attn_softmax_bw(dy, y, dinp=dx)
+            lnr.attn_softmax_fw_skip(x, m, causal, out=y)
+            lnr.attn_softmax_bw_skip(dy, y, m, causal, dinp=dx)
+        torch.cuda.synchronize()
+        s = W.dtype_size(dt)
+        sf, sb = W.softmax_skip_bytes(m.cpu() if m is not None else None, causal, B, H, T, T, s)
+        print(json.dumps({"case": name, "grid_rows": B * H * T,
+                          "dense_fw_bytes": W.softmax_fw_bytes(B, H, T, T, s, has_mask=padded),
+                          "dense_bw_bytes": W.softmax_bw_bytes(B, H, T, T, s),
+                          "skip_fw_bytes": sf, "skip_bw_bytes": sb}), flush=True)
+        log(f"skip traffic: {name} done")
+        del x, dy, y, dx, m
+        torch.cuda.empty_cache()
+
+
+def summarize_skip_traffic(root_dir: str):
+    """profiles/softmax_skip_traffic.md: FETCH_SIZE / WRITE_SIZE per dispatch of the dense and
+    skipping softmax kernels (scaled by the 1 GiB copy), beside the analytic bytes."""
+    import csv
+    import collections
+
+    calib_grid = str((1 << 30) // 64)
+
+    def per_kernel(kind):
+        path = os.path.join(root_dir, f"pmc_{kind}_skip", "skip_counter_collection.csv")
+        by = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if COPY in r["Kernel_Name"] and r["Grid_Size"] != calib_grid:
+                continue
+            by[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
+        return {k: statistics.mean(v) for k, v in by.items()}
+
+    fetch, write = per_kernel("fetch"), per_kernel("write")
+    pick = lambda d, key: next(v for k, v in d.items() if key in k)
+    f_scale = float(1 << 30) / pick(fetch, COPY)
+    w_scale = float(1 << 30) / pick(write, COPY)
+    cases = [json.loads(l) for l in open(os.path.join(root_dir, "skip_traffic.jsonl")) if l.startswith("{")]
+    rows = ["# HBM traffic of the read-skipping softmax kernels\n",
+            "Commands (each counter in a run of its own; the analytic bytes come from the same "
+            "program's output):\n", "```",
+            SKIP_PMC_CMD.format(ctr="FETCH_SIZE", kind="fetch"),
+            SKIP_PMC_CMD.format(ctr="WRITE_SIZE", kind="write"), "```\n",
+            f"Scale: the 1 GiB streaming copy reads {pick(fetch, COPY) / 2**20:.1f} MiB by FETCH_SIZE "
+            f"and writes {pick(write, COPY) / 2**20:.1f} MiB by WRITE_SIZE; fetch counts are multiplied "
+            f"by {f_scale:.4f}, write counts by {w_scale:.4f}. Padded masks keep the first 3/4 of the "
+            f"keys. Each case runs its own (G, IT) instantiation, so each kernel name is one case.\n",
+            "| kernel | fetch MB (scaled) | write MB (scaled) | total MB |", "|---|---|---|---|"]
+    for k in fetch:
+        if "softmax" in k and k in write:
+            fb, wb = fetch[k] * f_scale, write[k] * w_scale
+            rows.append(f"| `{k[:90]}` | {fb / 1e6:.3f} | {wb / 1e6:.3f} | {(fb + wb) / 1e6:.3f} |")
+    rows += ["", "Analytic bytes per launch (dense: every element read and written once; skipping: "
+             "the runs holding an open key read, every element written, the mask once):\n",
+             "| case | dense fw MB | skip fw MB | dense bw MB | skip bw MB |", "|---|---|---|---|---|"]
+    for c in cases:
+        rows.append(f"| {c['case']} | {c['dense_fw_bytes'] / 1e6:.3f} | {c['skip_fw_bytes'] / 1e6:.3f} | "
+                    f"{c['dense_bw_bytes'] / 1e6:.3f} | {c['skip_bw_bytes'] / 1e6:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "softmax_skip_traffic.md"), "w") as fh:
+        fh.write("\n".join(rows) + "\n")
 
 
 def summarize_profiles(root_dir: str, workload: str):
@@ -589,6 +695,12 @@ def main():
         return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload)
+        return
+    if args.skip_traffic:
+        run_skip_traffic()
+        return
+    if args.summarize_skip_traffic:
+        summarize_skip_traffic(args.summarize_skip_traffic)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only; multi-GPU runs (--gpus N > 1) are not "
