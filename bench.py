@@ -74,14 +74,14 @@ def parse():
 
 
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
-             "-d $REPO/gpurun_out/prof_{w} -o {w} -- python3 $REPO/bench.py{args}")
+             "-d $OUT/prof_{w} -o {w} -- python3 $REPO/bench.py{args}")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {ctr} -f csv "
-           "-d $REPO/gpurun_out/pmc_{kind}_{w} -o {w} -- python3 $REPO/bench.py{args} "
+           "-d $OUT/pmc_{kind}_{w} -o {w} -- python3 $REPO/bench.py{args} "
            "--steps 20 --warmup 5 --no-cpu-baseline")
 DOMINANT = "softmax_bw_vec"
 COPY = "copy16"
 SKIP_PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {ctr} -f csv "
-                "-d $REPO/gpurun_out/pmc_{kind}_skip -o skip -- python3 $REPO/bench.py --skip-traffic")
+                "-d $OUT/pmc_{kind}_skip -o skip -- python3 $REPO/bench.py --skip-traffic")
 
 
 def skip_traffic_cases():
@@ -158,7 +158,8 @@ def summarize_skip_traffic(root_dir: str):
     cases = [json.loads(l) for l in open(os.path.join(root_dir, "skip_traffic.jsonl")) if l.startswith("{")]
     rows = ["# HBM traffic of the read-skipping softmax kernels\n",
             "Commands (each counter in a run of its own; the analytic bytes come from the same "
-            "program's output):\n", "```",
+            "program's output; $REPO = the repository root, $OUT = the directory the profiler "
+            "writes to):\n", "```",
             SKIP_PMC_CMD.format(ctr="FETCH_SIZE", kind="fetch"),
             SKIP_PMC_CMD.format(ctr="WRITE_SIZE", kind="write"), "```\n",
             f"Scale: the 1 GiB streaming copy reads {pick(fetch, COPY) / 2**20:.1f} MiB by FETCH_SIZE "
@@ -193,7 +194,7 @@ def summarize_profiles(root_dir: str, workload: str):
     os.makedirs(out_dir, exist_ok=True)
     stats = os.path.join(root_dir, f"prof_{workload}", f"{workload}_kernel_stats.csv")
     lines = [f"# Kernel trace: {workload} benchmark\n",
-             "Command ($REPO = the repository root on the GPU host):\n",
+             "Command ($REPO = the repository root, $OUT = the directory the profiler writes to):\n",
              "```", TRACE_CMD.format(w=workload, args=args), "```\n"]
     def roofline_of(path):
         if os.path.exists(path):
@@ -244,7 +245,8 @@ def summarize_profiles(root_dir: str, workload: str):
     f_scale = copy_bytes / pick(fetch, COPY)
     w_scale = copy_bytes / pick(write, COPY)
     rows = ["# HBM traffic per dispatch: {w} benchmark\n".format(w=workload),
-            "Commands (each counter in a run of its own):\n", "```",
+            "Commands (each counter in a run of its own; $REPO = the repository root, $OUT = the "
+            "directory the profiler writes to):\n", "```",
             PMC_CMD.format(ctr="FETCH_SIZE", kind="fetch", w=workload, args=args),
             PMC_CMD.format(ctr="WRITE_SIZE", kind="write", w=workload, args=args), "```\n",
             f"Scale: the 16-byte streaming copy of 1 GiB (`copy16`) reads {pick(fetch, COPY) / 2**20:.1f} MiB "
@@ -703,7 +705,7 @@ def main():
         summarize_skip_traffic(args.summarize_skip_traffic)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; multi-GPU runs (--gpus N > 1) are not "
+        print("bench.py measures one GPU only; multi-GPU runs (--gpus N > 1) are not "
               "supported. Rows shard across GPUs with no communication except one 2*C-float "
               "all-reduce of the LayerNorm parameter gradients.", file=sys.stderr)
         sys.exit(2)
