@@ -234,6 +234,10 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
 // Backward, vector path: dx plus per-workgroup dgamma/dbeta column partials.
 // part layout: [P][2][C] of Accum<T>; slot 0 = dgamma, slot 1 = dbeta (unused for RMSNorm).
 // ------------------------------------------------------------------------------------------
+// LDS budget of the backward's final column-tile reduction (gfx950 gives a workgroup up to
+// 160 KiB; the backward grids run one workgroup per CU).
+constexpr size_t kTileBytes = 96 * 1024;
+
 template <typename T, int G, int IT, int WG, int DEPTH, int MODE, bool EXTRA>
 __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>::type *part,
                                                        const T *dy, const T *x,
@@ -258,8 +262,13 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     using RV = RawVec<T>;
     constexpr int V = Vec16<T>::N;
     constexpr int NG = WG / G;  // row groups per workgroup
+    // Column partials staged per round of the final LDS reduction: (vector slot, partial)
+    // pairs of G*V columns, as many as fit kTileBytes (all of them for 512-thread plans).
+    constexpr int PAIRS = IT * (RMS ? 1 : SLOTS);
+    constexpr int PER_FIT = static_cast<int>(kTileBytes / (static_cast<size_t>(WG) * V * sizeof(A)));
+    constexpr int PER = PER_FIT < 1 ? 1 : (PER_FIT < PAIRS ? PER_FIT : PAIRS);
     __shared__ float red[2 * (WG / 64)];
-    __shared__ A tile[NG > 1 ? NG : 1][NG > 1 ? G * V : 1];
+    __shared__ A tile[NG > 1 ? NG : 1][NG > 1 ? PER * G * V : 1];
 
     const int lane = threadIdx.x % G;
     const int grp = threadIdx.x / G;
@@ -444,30 +453,35 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
             }
         }
     } else {
-        // LDS column tile: for vector slot k and for dgamma then dbeta, every group stages its
-        // G*V columns, then the workgroup sums the NG groups of each column in group order.
+        // LDS column tile: each round, every group stages PER (vector slot k, partial) pairs of
+        // its G*V columns; then the workgroup sums the NG groups of each column in group order.
+        constexpr int NSL = RMS ? 1 : SLOTS;
+        auto value = [&](int k, int which, int e) -> A {
+            if constexpr (RMS) return adg[k][e];
+            else if constexpr (BDR) return which == 0 ? adg[k][e] : (which == 1 ? adb[k][e] : adx[k][e]);
+            else return which == 0 ? adg[k][e] : adb[k][e];
+        };
 #pragma unroll
-        for (int k = 0; k < IT; ++k) {
+        for (int p0 = 0; p0 < PAIRS; p0 += PER) {
+            if (p0 > 0) __syncthreads();  // the previous round's sums have read the tile
 #pragma unroll
-            for (int which = 0; which < (RMS ? 1 : SLOTS); ++which) {
+            for (int q = 0; q < PER; ++q) {
+                const int pr = p0 + q;
+                if (pr < PAIRS) {
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    if constexpr (RMS)
-                        tile[grp][lane * V + e] = adg[k][e];
-                    else if constexpr (BDR)
-                        tile[grp][lane * V + e] = which == 0 ? adg[k][e] : (which == 1 ? adb[k][e] : adx[k][e]);
-                    else
-                        tile[grp][lane * V + e] = which == 0 ? adg[k][e] : adb[k][e];
+                    for (int e = 0; e < V; ++e) tile[grp][q * G * V + lane * V + e] = value(pr / NSL, pr % NSL, e);
                 }
-                __syncthreads();
-                for (int cc = threadIdx.x; cc < G * V; cc += WG) {
-                    A s = tile[0][cc];
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < PER * G * V; idx += WG) {
+                const int pr = p0 + idx / (G * V);
+                if (pr >= PAIRS) break;
+                A sum = tile[0][idx];
 #pragma unroll
-                    for (int g = 1; g < NG; ++g) s += tile[g][cc];
-                    const int col = k * G * V + cc;
-                    if (col < C) (which == 0 ? pg : (which == 1 ? pb : px))[col] = s;
-                }
-                __syncthreads();
+                for (int g = 1; g < NG; ++g) sum += tile[g][idx];
+                const int which = pr % NSL;
+                const int col = (pr / NSL) * G * V + idx % (G * V);
+                if (col < C) (which == 0 ? pg : (which == 1 ? pb : px))[col] = sum;
             }
         }
     }
