@@ -68,6 +68,31 @@ __device__ __forceinline__ void ms_fold(float &m, float &s, float vm, float acc)
 // Forward statistics of row blockIdx.x, chunk blockIdx.y of S: (m, s) with s = sum exp(z - m).
 // S == 1: writes lse and loss. S > 1: writes the chunk's (m, s) to part[(row*S + chunk)*2].
 // ------------------------------------------------------------------------------------------
+// 16 bytes of -inf in each storage type: what idle lanes of the forward's row loop read
+// (global memory like the logits, so one global load serves both; never written).
+__device__ uint32_t kIdleF16[4] __attribute__((aligned(16))) = {0xFC00FC00u, 0xFC00FC00u,
+                                                                         0xFC00FC00u, 0xFC00FC00u};
+__device__ uint32_t kIdleF32[4] __attribute__((aligned(16))) = {0xFF800000u, 0xFF800000u,
+                                                                         0xFF800000u, 0xFF800000u};
+template <typename T>
+__device__ __forceinline__ const RawVec<T> *idle_vec() {
+    return reinterpret_cast<const RawVec<T> *>(Vec16<T>::N == 8 ? kIdleF16 : kIdleF32);
+}
+
+// Largest element of a 16-byte vector, compared in the storage type (exact), as fp32.
+template <typename T>
+__device__ __forceinline__ float vec_max(const RawVec<T> &v) {
+    if constexpr (Vec16<T>::N == 8) {
+        const auto h4 = __builtin_elementwise_max(__builtin_shufflevector(v, v, 0, 1, 2, 3),
+                                                  __builtin_shufflevector(v, v, 4, 5, 6, 7));
+        const auto h2 = __builtin_elementwise_max(__builtin_shufflevector(h4, h4, 0, 1),
+                                                  __builtin_shufflevector(h4, h4, 2, 3));
+        return static_cast<float>(h2[0] > h2[1] ? h2[0] : h2[1]);
+    } else {
+        return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    }
+}
+
 template <typename T, int WG, int U>
 __global__ __launch_bounds__(WG) void xent_fw_kernel(float *__restrict__ loss,
                                                      float *__restrict__ lse,
@@ -93,29 +118,48 @@ __global__ __launch_bounds__(WG) void xent_fw_kernel(float *__restrict__ loss,
     if (chunk == S - 1)
         for (int32_t j = sp.tail + threadIdx.x; j < V; j += WG) ms_fold(m, s, to_f32(zr[j]), 1.f);
 
-    for (int32_t base = v0; base < v1; base += WG * U) {
-        float x[U][VE];
+    // The loop is bound by VALU issue at fp16 (one exponential and a few operations per 2-byte
+    // element), so the per-element work is kept small: idle vectors are replaced as raw bits,
+    // the maximum is taken exactly in the storage type, and for fp16 the widening and the
+    // subtraction of the maximum are one mixed-precision fma (x * 1 - vm, rounded once like the
+    // plain subtraction; the 1 is hidden from the compiler, which would otherwise fold the fma
+    // back into a widening and a subtraction).
+    float one = 1.0f;
+    if constexpr (VE == 8) asm("" : "+v"(one));
+    // The next U vectors are fetched before the current ones are reduced, so a wave keeps
+    // loads in flight through its exponentials.
+    auto fetch = [&](RV (&dst)[U], int32_t base) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int32_t v = base + u * WG + threadIdx.x;
             const bool ok = v < v1;
-            const RV raw = load_stream_raw<T>(reinterpret_cast<const T *>(zv + (ok ? v : v0)));
-            widen<T>(raw, x[u]);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) x[u][e] = ok ? x[u][e] : -INFINITY;
+            // Idle lanes read a vector of -inf: every load is unconditional, so no branch makes
+            // the compiler wait for all loads in flight before the current vectors are reduced.
+            const RV *src = ok ? zv + v : idle_vec<T>();
+            dst[u] = load_stream_raw<T>(reinterpret_cast<const T *>(src));
         }
-        float vm = -INFINITY;
+    };
+    RV cur[U], nxt[U];
+    if (v0 < v1) fetch(cur, v0);
+    for (int32_t base = v0; base < v1; base += WG * U) {
+        const bool more = base + WG * U < v1;
+        if (more) fetch(nxt, base + WG * U);
+        RV mv = cur[0];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < VE; ++e) vm = fmaxf(vm, x[u][e]);
+        for (int u = 1; u < U; ++u) mv = __builtin_elementwise_max(mv, cur[u]);
+        const float vm = vec_max<T>(mv);
         if (vm != -INFINITY) {
             float acc = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int e = 0; e < VE; ++e) acc += __builtin_amdgcn_exp2f((x[u][e] - vm) * kLog2e);
+                for (int e = 0; e < VE; ++e)
+                    acc += __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(cur[u][e]), one, -vm) * kLog2e);
             ms_fold(m, s, vm, acc);
+        }
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
         }
     }
 
