@@ -440,6 +440,16 @@ def run_table(match: str = ""):
         torch.cuda.empty_cache()
         return out
 
+    # Warm-up: about 0.2 s of 1 GiB streaming copies, so the first cases do not run while the
+    # device is still ramping up (the same case measured 5-15% slower at the start of a run).
+    wa = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    wb = torch.empty_like(wa)
+    for _ in range(600):
+        lnr.copy_bytes(wb, wa)
+    torch.cuda.synchronize()
+    del wa, wb
+    torch.cuda.empty_cache()
+
     for name, kind, shape, dt, extra in table_cases():
         if match not in name:
             continue
