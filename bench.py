@@ -41,8 +41,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--workload", choices=("w2", "w5"), default="w2")
     p.add_argument("--sample-every", type=int, default=8, metavar="S",
                    help="time the dominant kernel's own duration on every S-th timed step (each "
