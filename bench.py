@@ -70,6 +70,10 @@ def parse():
                    help="CPU only: read pmc_fetch_skip/ and pmc_write_skip/ under DIR and the "
                         "--skip-traffic output DIR/skip_traffic.jsonl; write "
                         "profiles/softmax_skip_traffic.md")
+    p.add_argument("--summarize-table-trace", metavar="DIR",
+                   help="CPU only: read DIR/prof_table/table_kernel_trace.csv and the table's JSON lines "
+                        "DIR/table_prof.jsonl; write profiles/table_kernel_trace.md (rocprofv3 kernel "
+                        "durations and achieved GB/s per case)")
     p.add_argument("--summarize-profiles", metavar="DIR",
                    help="CPU only: read the rocprofv3 outputs under DIR (prof_<w>/, pmc_fetch_<w>/, "
                         "pmc_write_<w>/) and write the summaries under profiles/")
@@ -182,6 +186,79 @@ def summarize_skip_traffic(root_dir: str):
                     f"{c['dense_bw_bytes'] / 1e6:.3f} | {c['skip_bw_bytes'] / 1e6:.3f} |")
     with open(os.path.join(ROOT, "profiles", "softmax_skip_traffic.md"), "w") as fh:
         fh.write("\n".join(rows) + "\n")
+
+
+TABLE_TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace -f csv -d $OUT/prof_table "
+                   "-o table -- python3 $REPO/bench.py --table > $OUT/table_prof.jsonl")
+
+
+def summarize_table_trace(root_dir: str):
+    """profiles/table_kernel_trace.md: each table case's kernels as rocprofv3 timed them.
+
+    The dispatches are taken in order. The table's warm-up copies come first; after that every
+    case ends with its same-size ceiling launches (the copy and read-two-write-one helpers), so
+    the dispatches between two such blocks are one case, matched to the table's JSON lines in
+    order. Within a case each kernel's median duration over all its dispatches is taken (the
+    table also runs each operation once per input set while it prepares the calls); an
+    operation's time is its kernel's, plus its column-sum or finish kernel where it has one."""
+    import csv
+
+    trace = os.path.join(root_dir, "prof_table", "table_kernel_trace.csv")
+    rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
+    recs = [json.loads(l) for l in open(os.path.join(root_dir, "table_prof.jsonl")) if l.startswith("{")]
+    helper = lambda n: COPY in n or "xor16" in n
+    blocks, cur, i = [], [], 0
+    while i < len(rows) and helper(rows[i]["Kernel_Name"]):
+        i += 1                                    # warm-up copies
+    for r in rows[i:]:
+        n = r["Kernel_Name"]
+        if helper(n):
+            if cur:
+                blocks.append(cur)
+                cur = []
+            continue
+        if "lnr" not in n:
+            continue                              # not this library's (torch's input generation)
+        cur.append((n, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    if cur:
+        blocks.append(cur)
+    if len(blocks) != len(recs):
+        raise SystemExit(f"{len(blocks)} traced cases against {len(recs)} table records")
+    lines = ["# rocprofv3 kernel durations of every table case\n",
+             "Command ($REPO = the repository root, $OUT = the directory the profiler writes to):\n",
+             "```", TABLE_TRACE_CMD, "```\n",
+             "Median kernel durations under the tracer (no launch gaps), and the achieved GB/s of the "
+             "algorithmic bytes over them. For the read-skipping rows the bytes are those the kernels "
+             "move, and the dense kernels' durations on the same inputs are listed beside them.\n",
+             "| case | fw µs | bw µs | fw GB/s | bw GB/s | fw+bw GB/s | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for rec, blk in zip(recs, blocks):
+        durs, order = {}, []
+        for n, d in blk:
+            if n not in durs:
+                durs[n] = []
+                order.append(n)
+            durs[n].append(d)
+        med = {n: statistics.median(v) for n, v in durs.items()}
+        # second kernels of two-kernel operations belong with their first kernel
+        fin = sum(med[n] for n in order if "finish" in n)
+        col = sum(med[n] for n in order if "colsum" in n)
+        prim = [n for n in order if "finish" not in n and "colsum" not in n]
+        if any("skip" in n for n in prim):
+            pick = lambda key: next(n for n in prim if key in n)
+            tf, tb = med[pick("fw_skip")], med[pick("bw_skip")]
+            extra = f" (dense {med[pick('softmax_fw_vec')]:.1f} / {med[pick('softmax_bw_vec')]:.1f} µs)"
+        else:
+            fw_n = next(n for n in prim if "fw" in n)
+            bw_n = next(n for n in prim if "bw" in n)
+            tf, tb = med[fw_n] + fin, med[bw_n] + col
+            extra = ""
+        bf, bb = rec["bytes_fw"], rec["bytes_bw"]
+        gf, gb, gfb = bf / tf * 1e-3, bb / tb * 1e-3, (bf + bb) / (tf + tb) * 1e-3
+        lines.append(f"| {rec['case']}{extra} | {tf:.1f} | {tb:.1f} | {gf:.0f} | {gb:.0f} | {gfb:.0f} | "
+                     f"{gfb / PEAK_HBM_GBPS:.0%} |")
+    with open(os.path.join(ROOT, "profiles", "table_kernel_trace.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def summarize_profiles(root_dir: str, workload: str):
@@ -718,6 +795,9 @@ def main():
         return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload)
+        return
+    if args.summarize_table_trace:
+        summarize_table_trace(args.summarize_table_trace)
         return
     if args.skip_traffic:
         run_skip_traffic()
