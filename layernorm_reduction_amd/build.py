@@ -48,5 +48,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "native", "c_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "native", "c_client")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """The plain C99 client of the C ABI (tests/native/c_client.c), compiled by the host C
+    compiler against include/lnr.h, liblnr.so and the HIP runtime; no device code."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [os.environ.get("CC", "gcc"), "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           f"-I{INCLUDE}", f"-I{rocm}/include", C_CLIENT_SRC, "-o", C_CLIENT + ".tmp", f"-L{PKG}", "-llnr",
+           f"-L{rocm}/lib", "-lamdhip64", "-lm", f"-Wl,-rpath,{PKG}", f"-Wl,-rpath,{rocm}/lib",
+           "-Wl,-rpath,$ORIGIN/../../layernorm_reduction_amd"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(C_CLIENT + ".tmp", C_CLIENT)
+    return C_CLIENT
+
+
 if __name__ == "__main__":
     print(build(verbose="-q" not in sys.argv))
+    print(build_c_client(verbose="-q" not in sys.argv))
