@@ -29,12 +29,14 @@
  *     No C++ exception crosses this interface.
  *   - Results are bitwise reproducible: no floating-point atomics; every reduction has a
  *     fixed order that depends only on the shape.
- *   - Sizes of zero are legal and enqueue nothing (except layernorm_bw, which still writes
- *     zero gradients for gamma and beta when N == 0).
+ *   - Sizes of zero are legal and enqueue nothing, except the normalisation backwards
+ *     (layernorm_bw, rmsnorm_bw, bdr_layernorm_bw), which still write zero parameter
+ *     gradients when N == 0.
  *   - Any buffer may start at any address aligned to its element size. Rows whose byte
  *     length is a multiple of 16 and buffers aligned to 16 bytes take the 128-bit vector
  *     kernels; anything else takes a slower element-wise kernel with identical results
- *     up to rounding order.
+ *     up to rounding order. The bias-dropout-residual entry points have no element-wise
+ *     kernel and reject such shapes instead (see there).
  */
 #ifndef LNR_H
 #define LNR_H
@@ -234,6 +236,9 @@ LNR_API size_t bdr_layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype 
 
 /*
  * bdr_layernorm_bw -- backward of bdr_layernorm_fw from the saved s, mean and rstd.
+ * [Same passage as bdr_layernorm_fw; the gradients are the chain rule through the
+ *  composition, with the LayerNorm part as layernorm_bw (L10 "Technique 2").]
+ *
  *   ds        = LayerNorm input gradient of dy (as layernorm_bw) + ds_extra
  *   dresidual = ds,   dx = keep * ds / (1 - p),   dbias_j = sum_i dx_ij,
  *   dgamma_j = sum_i dy_ij * shat_ij,   dbeta_j = sum_i dy_ij,  shat = (s - mean) * rstd.
