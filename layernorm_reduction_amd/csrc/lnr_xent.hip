@@ -17,9 +17,11 @@
 //     cost is one exp per logit plus one per U*VE. Then the workgroup reduces (m, s): the
 //     block maximum first, then the sum of the rescaled s. Split rows write (m, s) partials
 //     and a small kernel combines them in chunk order.
-//   * Any V and any row alignment: a row is a scalar head up to the first 16-byte boundary,
-//     16-byte vectors, and a scalar tail, so a vocabulary of odd size (every row starting at
-//     a different phase) still streams at full width.
+//   * Any V and any row alignment: a row is a scalar head up to the first 128-byte line
+//     boundary, 16-byte vectors, and a scalar tail, so a vocabulary of odd size (every row
+//     starting at a different phase) still streams at full width, and every wave-wide vector
+//     access covers whole cache lines (a 1 KiB access that straddles lines touches 9 of them,
+//     and the backward's stores then write partial lines: 7-9% slower at V = 50001).
 //   * Backward, one pass: each logit is read once and its gradient written once.
 #include <math.h>
 
@@ -35,22 +37,30 @@ struct RowSplit {
     int32_t head, nvec, tail;
 };
 
+// Vector part of a row starting at the first `align`-byte boundary of `row` (align 16 or
+// 128; 0: no vector part, every element scalar). The head is shorter than align bytes.
 template <typename T>
-__device__ __forceinline__ RowSplit split_row(const T *row, int32_t V, bool vec_ok) {
+__device__ __forceinline__ RowSplit split_row(const T *row, int32_t V, uint32_t align) {
     constexpr int VE = Vec16<T>::N;
-    if (!vec_ok) return {V, 0, V};
-    const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
-    int32_t head = static_cast<int32_t>(((16u - phase) & 15u) / sizeof(T));
+    if (align == 0) return {V, 0, V};
+    const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & (align - 1));
+    int32_t head = static_cast<int32_t>(((align - phase) & (align - 1)) / sizeof(T));
     if (head > V) head = V;
     const int32_t nvec = (V - head) / VE;
     return {head, nvec, head + nvec * VE};
 }
 
-// Vectors [v0, v1) of chunk c out of S (contiguous, in order).
-__device__ __forceinline__ void chunk_range(int32_t nvec, int32_t c, int32_t S, int32_t &v0,
-                                            int32_t &v1) {
-    v0 = static_cast<int32_t>(static_cast<int64_t>(nvec) * c / S);
-    v1 = static_cast<int32_t>(static_cast<int64_t>(nvec) * (c + 1) / S);
+// Vectors [v0, v1) of chunk c out of S (contiguous, in order). Inner chunk boundaries are
+// rounded down to a multiple of align / 16 vectors, so every chunk starts on a line.
+__device__ __forceinline__ int32_t chunk_bound(int32_t nvec, int32_t c, int32_t S, uint32_t align) {
+    if (c >= S) return nvec;
+    const int32_t b = static_cast<int32_t>(static_cast<int64_t>(nvec) * c / S);
+    return align > 16 ? b & ~static_cast<int32_t>(align / 16 - 1) : b;
+}
+__device__ __forceinline__ void chunk_range(int32_t nvec, int32_t c, int32_t S, uint32_t align,
+                                            int32_t &v0, int32_t &v1) {
+    v0 = chunk_bound(nvec, c, S, align);
+    v1 = chunk_bound(nvec, c + 1, S, align);
 }
 
 // Fold logits whose maximum is vm and whose exp-sum relative to that maximum is acc into
@@ -99,16 +109,16 @@ __global__ __launch_bounds__(WG) void xent_fw_kernel(float *__restrict__ loss,
                                                      float *__restrict__ part, const T *z,
                                                      const int64_t *__restrict__ target,
                                                      int32_t V, int64_t ignore_index,
-                                                     int32_t S, int32_t vec_ok) {
+                                                     int32_t S, uint32_t align) {
     using RV = RawVec<T>;
     constexpr int VE = Vec16<T>::N;
     __shared__ float red[WG / 64];
     const int64_t row = blockIdx.x;
     const int32_t chunk = blockIdx.y;
     const T *zr = z + row * static_cast<int64_t>(V);
-    const RowSplit sp = split_row(zr, V, vec_ok != 0);
+    const RowSplit sp = split_row(zr, V, align);
     int32_t v0, v1;
-    chunk_range(sp.nvec, chunk, S, v0, v1);
+    chunk_range(sp.nvec, chunk, S, align, v0, v1);
     const RV *zv = reinterpret_cast<const RV *>(zr + sp.head);
 
     float m = -INFINITY, s = 0.f;
@@ -218,8 +228,8 @@ __global__ __launch_bounds__(256) void xent_fw_finish(float *__restrict__ loss,
 
 // ------------------------------------------------------------------------------------------
 // Backward: dz = g * (exp(z - lse) - onehot), g = dloss[row] * scale (dloss NULL: 1).
-// Row blockIdx.x, chunk blockIdx.y of S. vec_ok also requires z and dz rows to share their
-// 16-byte phase (checked by the host).
+// Row blockIdx.x, chunk blockIdx.y of S. The row split follows dz's phase; the host passes an
+// align for which z and dz rows share their phase (128, else 16, else 0).
 // ------------------------------------------------------------------------------------------
 template <typename T, int WG, int U>
 __global__ __launch_bounds__(WG) void xent_bw_kernel(T *dz, const T *z,
@@ -227,7 +237,7 @@ __global__ __launch_bounds__(WG) void xent_bw_kernel(T *dz, const T *z,
                                                      const float *__restrict__ lse,
                                                      const float *__restrict__ dloss, float scale,
                                                      int32_t V, int64_t ignore_index, int32_t S,
-                                                     int32_t vec_ok) {
+                                                     uint32_t align) {
     using RV = RawVec<T>;
     constexpr int VE = Vec16<T>::N;
     const int64_t row = blockIdx.x;
@@ -235,9 +245,9 @@ __global__ __launch_bounds__(WG) void xent_bw_kernel(T *dz, const T *z,
     const int64_t rbase = row * static_cast<int64_t>(V);
     const T *zr = z + rbase;
     T *dr = dz + rbase;
-    const RowSplit sp = split_row(zr, V, vec_ok != 0);
+    const RowSplit sp = split_row(static_cast<const T *>(dr), V, align);
     int32_t v0, v1;
-    chunk_range(sp.nvec, chunk, S, v0, v1);
+    chunk_range(sp.nvec, chunk, S, align, v0, v1);
 
     const int64_t t = target[row];
     const bool ignored = t == ignore_index;
@@ -285,11 +295,15 @@ __global__ __launch_bounds__(WG) void xent_bw_kernel(T *dz, const T *z,
 // ------------------------------------------------------------------------------------------
 // Workgroup size and vectors in flight per thread, measured on MI355X ([8192, 32000] and
 // [8192, 50001] fp16): the forward is within 2% from 256x4 to 512x4 (84 us, 6.2 TB/s of
-// reads); the backward gains 14-22% from 256x4 to 1024x2 (204 -> 179 us at V = 32000).
+// reads); the backward gains 14-22% from 256x4 to 1024x2 (204 -> 179 us at V = 32000) and
+// 1-2% more from 1024x2 to 1024x4 on whole rows (line-aligned; fp16 and fp32). Split rows
+// ([64, 50001]: chunks of about 1000 vectors) stay at 1024x2, 3-5% faster than 1024x4 there.
 constexpr int kXentFwWG = 512;
 constexpr int kXentFwU = 4;
 constexpr int kXentBwWG = 1024;
-constexpr int kXentBwU = 2;
+constexpr int kXentBwU = 4;       // whole rows (S == 1)
+constexpr int kXentBwSplitU = 2;  // split rows (S > 1)
+constexpr uint32_t kXentLine = 128;  // bytes: the row split's alignment
 constexpr int64_t kXentTargetBlocks = 1024;  // split rows until about this many workgroups
 
 // Chunks per row: 1 when there are enough rows, else enough to reach kXentTargetBlocks
@@ -352,10 +366,10 @@ extern "C" int cross_entropy_fw(float *loss, float *lse, const void *logits, con
     hipError_t e;
     if (dtype == LNR_F16)
         e = launch(xent_fw_kernel<f16, kXentFwWG, kXentFwU>, grid, dim3(kXentFwWG), s, loss, lse,
-                   part, static_cast<const f16 *>(logits), target, V32, ignore_index, S, 1);
+                   part, static_cast<const f16 *>(logits), target, V32, ignore_index, S, kXentLine);
     else
         e = launch(xent_fw_kernel<float, kXentFwWG, kXentFwU>, grid, dim3(kXentFwWG), s, loss, lse,
-                   part, static_cast<const float *>(logits), target, V32, ignore_index, S, 1);
+                   part, static_cast<const float *>(logits), target, V32, ignore_index, S, kXentLine);
     if (e == hipSuccess && S > 1) {
         const dim3 g2(static_cast<uint32_t>((N + 255) / 256));
         if (dtype == LNR_F16)
@@ -392,19 +406,26 @@ extern "C" int cross_entropy_bw(void *dlogits, const void *logits, const int64_t
 
     // Bandwidth needs enough workgroups: split rows as the forward does.
     const int32_t S = xent_chunks(N, V, es, kXentBwWG);
-    const int32_t vec_ok =
-        ((reinterpret_cast<uintptr_t>(dlogits) - reinterpret_cast<uintptr_t>(logits)) & 15u) == 0;
+    // Vector part aligned to dz's lines where z shares that phase, else to 16 bytes, else none.
+    const uintptr_t dphase = reinterpret_cast<uintptr_t>(dlogits) - reinterpret_cast<uintptr_t>(logits);
+    const uint32_t align = (dphase & (kXentLine - 1)) == 0 ? kXentLine : (dphase & 15u) == 0 ? 16u : 0u;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(static_cast<uint32_t>(N), static_cast<uint32_t>(S));
     const int32_t V32 = static_cast<int32_t>(V);
+    auto go = [&](auto kernel, auto *dz, const auto *z) {
+        return launch(kernel, grid, dim3(kXentBwWG), s, dz, z, target, lse, dloss, scale, V32,
+                      ignore_index, S, align);
+    };
+    f16 *dh = static_cast<f16 *>(dlogits);
+    const f16 *zh = static_cast<const f16 *>(logits);
+    float *df = static_cast<float *>(dlogits);
+    const float *zf = static_cast<const float *>(logits);
     hipError_t e;
     if (dtype == LNR_F16)
-        e = launch(xent_bw_kernel<f16, kXentBwWG, kXentBwU>, grid, dim3(kXentBwWG), s,
-                   static_cast<f16 *>(dlogits), static_cast<const f16 *>(logits), target, lse, dloss,
-                   scale, V32, ignore_index, S, vec_ok);
+        e = S == 1 ? go(xent_bw_kernel<f16, kXentBwWG, kXentBwU>, dh, zh)
+                   : go(xent_bw_kernel<f16, kXentBwWG, kXentBwSplitU>, dh, zh);
     else
-        e = launch(xent_bw_kernel<float, kXentBwWG, kXentBwU>, grid, dim3(kXentBwWG), s,
-                   static_cast<float *>(dlogits), static_cast<const float *>(logits), target, lse,
-                   dloss, scale, V32, ignore_index, S, vec_ok);
+        e = S == 1 ? go(xent_bw_kernel<float, kXentBwWG, kXentBwU>, df, zf)
+                   : go(xent_bw_kernel<float, kXentBwWG, kXentBwSplitU>, df, zf);
     return status_of(e);
 }

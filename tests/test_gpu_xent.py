@@ -125,18 +125,28 @@ def test_in_place_backward_and_determinism(dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
-def test_unaligned_and_phase_shifted_buffers(dtype):
-    """Logits one element past a 16-byte boundary (vector middle after a scalar head), and a
-    gradient buffer at a different 16-byte phase from the logits (scalar path)."""
-    case = W.xent_case("xent-unaligned", 50, 1001, dtype=dtype, seed_base=8200)
+@pytest.mark.parametrize("NV", [(50, 1001), (20, 20011)])
+@pytest.mark.parametrize("dz_phase", ["line", "16B", "scalar"])
+def test_unaligned_and_phase_shifted_buffers(dz_phase, NV, dtype):
+    """Logits one element past a 16-byte boundary (vector middle after a scalar head of up to
+    a 128-byte line), and the gradient buffer at the logits' 128-byte phase ("line"), at their
+    16-byte phase only ("16B": 16-byte vectors from dz's first 16-byte boundary), or at
+    another 16-byte phase ("scalar": every element on its own). 20 x 20011 also splits each
+    row over several workgroups, whose inner boundaries are rounded to lines."""
+    N, V = NV
+    case = W.xent_case(f"xent-unaligned-{N}x{V}", N, V, dtype=dtype, seed_base=8200 + N)
+    es = torch.empty((), dtype=dtype).element_size()
     buf = torch.empty(case.N * case.V + 8, dtype=dtype, device=DEV)
     zd = buf[1:1 + case.N * case.V].view(case.N, case.V)
     zd.copy_(case.logits.to(DEV))
     td = case.target.to(DEV)
-    say(case.name, dtype)
+    say(case.name, dtype, dz_phase)
     loss, lse = lnr.cross_entropy_fw(zd, td)
-    out = torch.empty(case.N * case.V + 8, dtype=dtype, device=DEV)
-    dz = out[2:2 + case.N * case.V].view(case.N, case.V)
+    k = {"line": 1, "16B": 1 + 16 // es, "scalar": 2}[dz_phase]
+    out = torch.empty(case.N * case.V + 80, dtype=dtype, device=DEV)
+    dz = out[k:k + case.N * case.V].view(case.N, case.V)
+    shift = (dz.data_ptr() - zd.data_ptr()) % 128
+    assert {"line": shift == 0, "16B": shift == 16, "scalar": shift % 16 != 0}[dz_phase]
     lnr.cross_entropy_bw(zd, td, lse, case.dloss.to(DEV), 1.0, dlogits=dz)
     torch.cuda.synchronize()
     z64, t = case.logits.double().numpy(), case.target.numpy()
@@ -145,7 +155,7 @@ def test_unaligned_and_phase_shifted_buffers(dtype):
     l64 = lse.cpu().double().numpy()
     dz_ref = oracle.xent_bw_given_lse(z64, t, l64, case.dloss.double().numpy())
     g_rows = np.where(t == case.ignore_index, 0.0, case.dloss.double().numpy())
-    check_dz(dz, dz_ref, dtype, "phase-shifted dlogits", z64, l64, g_rows)
+    check_dz(dz, dz_ref, dtype, f"{dz_phase} dlogits", z64, l64, g_rows)
 
 
 def test_large_logits_and_invalid_targets():
