@@ -44,12 +44,15 @@ template <> struct Accum<float> { using type = double; };
 // shift near the mean removes the cancellation that fp32 one-pass sums suffer when the
 // variance is small next to mean^2. xhat is then formed as (d - mu(d)) * rstd, so no
 // rounding of K + mu(d) enters it. No contraction here: a constant row (or C = 1) gives
-// s1 = s2 = 0 and therefore a variance of exactly 0.
-__device__ __forceinline__ float ln_stats(float s1, float s2, int C, float eps, float &m1) {
+// s1 = s2 = 0 and therefore a variance of exactly 0. invC = 1 / C (rounded once per kernel);
+// the means are products with it and rstd is the hardware reciprocal square root (both
+// within 1 ulp of the divisions they replace, at a fraction of their instructions: every
+// lane of a row evaluates this once per row).
+__device__ __forceinline__ float ln_stats(float s1, float s2, float invC, float eps, float &m1) {
 #pragma clang fp contract(off)
-    m1 = s1 / static_cast<float>(C);
-    const float var = fmaxf(s2 / static_cast<float>(C) - m1 * m1, 0.f);
-    return 1.0f / sqrtf(var + eps);
+    m1 = s1 * invC;
+    const float var = fmaxf(s2 * invC - m1 * m1, 0.f);
+    return __builtin_amdgcn_rsqf(var + eps);
 }
 
 // What the row kernels normalise.
@@ -72,24 +75,32 @@ __device__ __forceinline__ uint32_t keep_bits(const uint8_t *mrow, int c) {
     }
 }
 
-// RMSNorm statistic: rstd = 1 / sqrt(mean(x^2) + eps), from the one sum of squares.
-__device__ __forceinline__ float rms_stats(float s2, int C, float eps) {
+// RMSNorm statistic: rstd = 1 / sqrt(mean(x^2) + eps), from the one sum of squares (invC
+// and the reciprocal square root as in ln_stats).
+__device__ __forceinline__ float rms_stats(float s2, float invC, float eps) {
 #pragma clang fp contract(off)
-    return 1.0f / sqrtf(s2 / static_cast<float>(C) + eps);
+    return __builtin_amdgcn_rsqf(s2 * invC + eps);
 }
 
 // ------------------------------------------------------------------------------------------
-// Forward, vector path. Workgroup b normalises rows [b*R, (b+1)*R) with R = rows_per_block;
-// group g of the workgroup takes rows b*R + g, b*R + g + NG, ... gamma and beta are loaded
-// once per workgroup. The next row's vectors (and its shift K) are fetched before the
-// current row is reduced, so each wave keeps a row of loads in flight while it computes;
-// the fetch is issued unconditionally (an idle lane reads a vector that always exists) so
-// that no branch makes the compiler drain the loads early.
+// Forward, vector path. Workgroup b normalises rows [b*P, (b+1)*P) with P = rows_per_block =
+// NG * R; group g of the workgroup takes rows b*P + g, b*P + g + NG, ... (R of them). gamma
+// and beta are loaded once per workgroup. The next row's vectors (and its shift K) are
+// fetched before the current row is reduced, so each wave keeps a row of loads in flight
+// while it computes; the fetch is issued unconditionally (an idle lane reads a vector that
+// always exists) so that no branch makes the compiler drain the loads early.
+// At fp16 the kernel is bound by VALU issue as much as by HBM (a wave64 fp32 operation takes
+// a SIMD 4 cycles), so the per-element work is kept small: idle lanes (only in plans wider
+// than the row) take the value K, which makes d = x - K exactly 0 without a select per
+// element; the widening and the subtraction of K are one mixed-precision fma (x * 1 - K,
+// rounded once like the plain subtraction; the 1 is hidden from the compiler, which would
+// otherwise fold it back into a conversion and a subtraction); and y = (d * rstd - mu(d) *
+// rstd) * gamma + beta is two fmas.
 // kBdrLayerNorm: the row is s = residual + keep * (x + bias) * keep_scale, formed in fp32 from
 // x, residual and the row's mask bytes, written to s_out (the residual stream), and
 // normalised in fp32.
 // ------------------------------------------------------------------------------------------
-template <typename T, int G, int IT, int WG, int MODE>
+template <typename T, int G, int IT, int WG, int MODE, int R>
 __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__ mean,
                                                        float *__restrict__ rstd, const T *x,
                                                        const T *__restrict__ gamma,
@@ -127,10 +138,19 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
     float b0 = 0.f;
     if constexpr (BDR) b0 = to_f32(bias[0]);
 
-    const int64_t iters = (rows_per_block + NG - 1) / NG;
+    // The row loop has R iterations, a compile-time count, but stays rolled: unrolled, the
+    // compiler issues the loads of all R rows up front, and the extra registers cost more
+    // than the copy of the prefetched row at the end of each iteration (2-5% on MI355X).
+    // Variants measured against this structure and rejected (all on MI355X, fp16 and fp32):
+    // fetching the first row before gamma and beta, and clamping a dead first row to a live
+    // one so that no branch forms around its loads (both 3-6% slower at 4096-8192 columns);
+    // masking dead prefetch addresses through inline asm (6% slower: the asm splits the
+    // loop's scheduling region).
+    const float invC = 1.0f / static_cast<float>(C);
     RV xn[IT], rn[BDR ? IT : 1];
     uint32_t kn[BDR ? IT : 1];
     float Kn;
+    T Kraw = T(0);  // the shift as stored (not kBdrLayerNorm): what idle lanes hold
     auto fetch = [&](int64_t row, bool live) {
         const int64_t rbase = (live ? row : r0) * static_cast<int64_t>(C);
         const uint8_t *mrow = BDR ? mask + (live ? row : r0) * mb : nullptr;
@@ -140,7 +160,7 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
             const bool ok = live && c < nvec;
             const int64_t off = rbase + (ok ? static_cast<int64_t>(c) * V : 0);
             const RV l = load_stream_raw<T>(x + off);
-            xn[k] = ok ? l : zero;
+            xn[k] = BDR ? (ok ? l : zero) : l;
             if constexpr (BDR) {
                 const RV lr = load_stream_raw<T>(residual + off);
                 const uint32_t kb = keep_bits<T>(mrow, ok ? c : 0);
@@ -153,15 +173,18 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
             const float s0 = r0v + ((mrow[0] & 1u) ? (x0 + b0) * keep_scale : 0.f);
             Kn = live ? s0 : 0.f;
         } else if constexpr (!RMS) {
-            const float kl = to_f32(x[rbase]);  // the shift: one broadcast load per group
-            Kn = live ? kl : 0.f;
+            Kraw = x[rbase];  // the shift: one broadcast load per group
+            Kn = to_f32(Kraw);
         } else {
             Kn = 0.f;
         }
     };
+    float one = 1.0f;
+    if constexpr (V == 8) asm("" : "+v"(one));
     fetch(r0 + grp, r0 + grp < r1);
-    for (int64_t it = 0; it < iters; ++it) {
-        const int64_t row = r0 + it * NG + grp;
+#pragma unroll 1
+    for (int it = 0; it < R; ++it) {
+        const int64_t row = r0 + static_cast<int64_t>(it) * NG + grp;
         const bool live = row < r1;
         RV xc[IT], rc[BDR ? IT : 1];
         uint32_t kc[BDR ? IT : 1];
@@ -174,14 +197,30 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
             }
         }
         const float K = Kn;
-        fetch(row + NG, it + 1 < iters && row + NG < r1);
+        const T Kc = Kraw;
+        fetch(row + NG, it + 1 < R && row + NG < r1);
 
         float d[IT][V];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
-            widen<T>(xc[k], d[k]);
             const bool ok = k * G + lane < nvec;
+            if constexpr (!BDR) {
+                if ((k + 1) * G > nvec) {  // uniform: this vector slot has idle lanes
+                    RV kv;
+#pragma unroll
+                    for (int e = 0; e < V; ++e) kv[e] = Kc;
+                    xc[k] = ok ? xc[k] : kv;
+                }
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    d[k][e] = __builtin_fmaf(static_cast<float>(xc[k][e]), one, -K);
+                    if constexpr (!RMS) s1 += d[k][e];
+                    s2 += d[k][e] * d[k][e];
+                }
+                continue;
+            }
+            widen<T>(xc[k], d[k]);
             if constexpr (BDR) {
                 float rf[V];
                 widen<T>(rc[k], rf);
@@ -202,11 +241,12 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
         float m1 = 0.f, rs;
         if constexpr (RMS) {
             s2 = row_allreduce<G>(s2, OpSum(), red);
-            rs = rms_stats(s2, C, eps);
+            rs = rms_stats(s2, invC, eps);
         } else {
             row_allreduce_sum2<G>(s1, s2, red);
-            rs = ln_stats(s1, s2, C, eps, m1);
+            rs = ln_stats(s1, s2, invC, eps, m1);
         }
+        const float nmr = -(m1 * rs);
         const int64_t base = (live ? row : 0) * static_cast<int64_t>(C);
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
@@ -218,7 +258,7 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
                     if constexpr (RMS)
                         o[e] = d[k][e] * rs * gm[k][e];
                     else
-                        o[e] = (d[k][e] - m1) * rs * gm[k][e] + bt[k][e];
+                        o[e] = __builtin_fmaf(__builtin_fmaf(d[k][e], rs, nmr), gm[k][e], bt[k][e]);
                 }
                 store_stream<T>(y + base + static_cast<int64_t>(c) * V, o);
             }
@@ -556,12 +596,13 @@ __global__ __launch_bounds__(kLnGenericWG) void layernorm_fw_generic(
         s2 += d * d;
     }
     float m1 = 0.f, rs;
+    const float invC = 1.0f / static_cast<float>(C);
     if constexpr (RMS) {
         s2 = row_allreduce<kLnGenericWG>(s2, OpSum(), red);
-        rs = rms_stats(s2, C, eps);
+        rs = rms_stats(s2, invC, eps);
     } else {
         row_allreduce_sum2<kLnGenericWG>(s1, s2, red);
-        rs = ln_stats(s1, s2, C, eps, m1);
+        rs = ln_stats(s1, s2, invC, eps, m1);
     }
     T *yr = y + row * static_cast<int64_t>(C);
     for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
@@ -642,22 +683,24 @@ struct LnPlan {
 
 // Measured on MI355X (fp16, N = 8192..32768): both LayerNorm kernels run best with one or
 // two 16-byte vectors per lane and as many lanes per row as that gives (several waves per row
-// from 2048 columns up). The forward gains from a row loop (R rows per group) once rows reach
-// 1024 columns; the backward gains from fetching two rows ahead once rows reach 4096. At
-// 8192 fp16 columns the forward takes four vectors per lane over four waves (interleaved
-// A/B at [16384,8192]: 90-96 us against 93-108 us for two vectors over eight waves).
+// from 2048 columns up). The forward takes one row per group (R = 1) up to 2048 columns and
+// two rows per group above, where the prefetch of the second row pays (at 4096-8192 columns
+// 6-12% faster than one row; at 1024 fp16 columns one row is 3-8% faster than two). fp32 at
+// 1024 columns is a tie and keeps two. At 8192 fp16 columns the forward takes four vectors
+// per lane over four waves. The same plans serve RMSNorm and the bias-dropout-residual
+// LayerNorm.
 template <typename T> struct LnFwTable;
 template <> struct LnFwTable<f16> {  // V = 8
     static constexpr LnPlan plans[] = {
-        {64, 8, 1, 256, 1},     {128, 16, 1, 256, 1},   {256, 16, 2, 128, 1},
-        {512, 32, 2, 256, 2},   {768, 32, 3, 256, 2},   {1024, 64, 2, 128, 2},
-        {2048, 128, 2, 256, 2}, {4096, 256, 2, 256, 4}, {8192, 256, 4, 256, 2}};
+        {64, 8, 1, 256, 1},     {128, 16, 1, 256, 1},   {256, 16, 2, 256, 1},
+        {512, 32, 2, 256, 1},   {768, 32, 3, 64, 1},    {1024, 64, 2, 128, 1},
+        {2048, 128, 2, 128, 1}, {4096, 256, 2, 256, 2}, {8192, 256, 4, 256, 2}};
 };
 template <> struct LnFwTable<float> {  // V = 4
     static constexpr LnPlan plans[] = {
         {64, 16, 1, 256, 1},    {128, 16, 2, 256, 1},   {256, 32, 2, 128, 1},
         {512, 64, 2, 256, 2},   {768, 64, 3, 256, 2},   {1024, 128, 2, 256, 2},
-        {2048, 256, 2, 256, 2}, {4096, 512, 2, 512, 4}, {8192, 1024, 2, 1024, 4}};
+        {2048, 256, 2, 256, 2}, {4096, 512, 2, 512, 2}, {8192, 1024, 2, 1024, 2}};
 };
 template <typename T> struct LnBwTable;
 template <> struct LnBwTable<f16> {
@@ -770,7 +813,7 @@ static hipError_t dispatch_ln_fw(const LnFwArgs &a, hipStream_t st) {
         static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && p.R >= 1, "bad forward plan");
         constexpr int64_t RPB = static_cast<int64_t>(p.WG / p.G) * p.R;
         const int64_t blocks = (a.N + RPB - 1) / RPB;
-        return launch(layernorm_fw_vec<T, p.G, p.IT, p.WG, MODE>, dim3(static_cast<uint32_t>(blocks)),
+        return launch(layernorm_fw_vec<T, p.G, p.IT, p.WG, MODE, p.R>, dim3(static_cast<uint32_t>(blocks)),
                       dim3(p.WG), st, static_cast<T *>(a.y), a.mean, a.rstd,
                       static_cast<const T *>(a.x), static_cast<const T *>(a.gamma),
                       static_cast<const T *>(a.beta), a.N, a.C, a.eps, RPB,
