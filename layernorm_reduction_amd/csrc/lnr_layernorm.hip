@@ -278,6 +278,16 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
 // 160 KiB; the backward grids run one workgroup per CU).
 constexpr size_t kTileBytes = 96 * 1024;
 
+// Two 16-byte vectors of zeros in global memory (never written): what a row past the end
+// reads in the backward (x from the first, dy from the second), so that it adds nothing to
+// the column partials without a select per element. Two addresses, not one: loads the
+// compiler can prove equal for a dead row are merged and branched around.
+__device__ uint32_t kZero32[8] __attribute__((aligned(16))) = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+template <typename T>
+__device__ __forceinline__ const T *zero16(int which) {
+    return reinterpret_cast<const T *>(kZero32 + 4 * which);
+}
+
 template <typename T, int G, int IT, int WG, int DEPTH, int MODE, bool EXTRA>
 __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>::type *part,
                                                        const T *dy, const T *x,
@@ -322,6 +332,10 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     const int64_t first_row = blockIdx.x;
     const float invC = 1.0f / static_cast<float>(C);
     const RV zero = {};
+    // 1 and -0 hidden from the compiler, which would otherwise fold x * 1 + y and x * y + -0
+    // back into separate widenings and plain operations.
+    float one = 1.0f, nzero = -0.0f;
+    asm("" : "+v"(one), "+v"(nzero));
 
     RV gmr[IT];  // gamma, kept as stored (16 bytes per vector) to save registers
     A adg[IT][V], adb[IT][RMS ? 1 : V], adx[IT][BDR ? V : 1];
@@ -363,6 +377,15 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
         for (int k = 0; k < IT; ++k) {
             const int c = k * G + lane;
             const bool ok = live && c < nvec;
+            if constexpr (!BDR) {
+                // No select per element: an idle lane (c >= nvec) reads its row's first vector
+                // and adds nothing, since its gamma is zero and its column partials are never
+                // written; a row past the end reads zeros from the sentinel.
+                const int64_t off = rbase + (c < nvec ? static_cast<int64_t>(c) * V : 0);
+                b.xv[k] = load_stream_raw<T>(live ? x + off : zero16<T>(0));
+                b.dv[k] = load_stream_raw<T>(live ? dy + off : zero16<T>(1));
+                continue;
+            }
             const int64_t off = rbase + (ok ? static_cast<int64_t>(c) * V : 0);
             const RV xl = load_stream_raw<T>(x + off);
             const RV dl = load_stream_raw<T>(dy + off);
@@ -399,6 +422,27 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
         float sg = 0.f, sgx = 0.f;
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
+            if constexpr (!BDR && V == 8) {
+                // fp16 storage: every operation that takes a stored value is one mixed-precision
+                // fma, with no separate widening (the kernel is VALU-bound at fp16). x - mu and
+                // gamma * dy round exactly as the plain operations do (the product of two
+                // halves is exact in fp32); the dgamma partial rounds once (an fma).
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float xs = static_cast<float>(b.xv[k][e]);
+                    const float ds = static_cast<float>(b.dv[k][e]);
+                    if constexpr (RMS)
+                        xh[k][e] = __builtin_fmaf(xs, rs, nzero);
+                    else
+                        xh[k][e] = __builtin_fmaf(xs, one, -mu) * rs;
+                    gv[k][e] = __builtin_fmaf(static_cast<float>(gmr[k][e]), ds, nzero);
+                    if constexpr (!RMS) sg += gv[k][e];
+                    sgx = __builtin_fmaf(gv[k][e], xh[k][e], sgx);
+                    adg[k][e] = __builtin_fmaf(ds, xh[k][e], adg[k][e]);
+                    if constexpr (!RMS) adb[k][e] = __builtin_fmaf(ds, one, adb[k][e]);
+                }
+                continue;
+            }
             float xf[V], df[V], gmf[V];
             widen<T>(b.xv[k], xf);
             widen<T>(b.dv[k], df);
@@ -702,6 +746,9 @@ template <> struct LnFwTable<float> {  // V = 4
         {512, 64, 2, 256, 2},   {768, 64, 3, 256, 2},   {1024, 128, 2, 256, 2},
         {2048, 256, 2, 256, 2}, {4096, 512, 2, 512, 2}, {8192, 1024, 2, 1024, 2}};
 };
+// The backward row kernel runs within 2-11% of a read-two-write-one stream of the same size
+// (N = 16384..32768). Timed alone, two vectors per lane over 512 threads at 1024 columns was
+// 2% faster than the plan below, but 1-5% slower inside the whole backward; not taken.
 template <typename T> struct LnBwTable;
 template <> struct LnBwTable<f16> {
     static constexpr LnPlan plans[] = {
