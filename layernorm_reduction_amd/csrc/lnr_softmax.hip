@@ -49,30 +49,52 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
     const int nvec = Tk / V;
     const int64_t base = static_cast<int64_t>(live ? row : 0u) * Tk;
 
-    float z[IT][V];
+    // Scores and mask are loaded as stored, every load unconditional (an idle lane reads its
+    // row's first vector; a row past the end reads row 0), so no branch makes the compiler
+    // wait between loads. Idle lanes then take -inf scores (a select only in buckets wider
+    // than the row); their mask values come from the same row and change nothing. At fp16 the
+    // widening and the mask add are one mixed-precision fma (x * 1 + m: both exact in fp32,
+    // the sum rounded once, as the plain addition).
+    using RV = RawVec<T>;
+    RV xr[IT], mr[IT];
+    const T *mrow = mask != nullptr
+                        ? mask + static_cast<int64_t>(divu32(live ? row : 0u, per_batch)) * Tk
+                        : nullptr;
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
-        if (live && c < nvec) {
-            load_stream<T>(inp + base + static_cast<int64_t>(c) * V, z[k]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) z[k][e] = -INFINITY;
-        }
+        const int64_t off = c < nvec ? static_cast<int64_t>(c) * V : 0;
+        xr[k] = load_stream_raw<T>(inp + base + off);
     }
-    if (mask != nullptr) {
-        const T *mrow = mask + static_cast<int64_t>(divu32(live ? row : 0u, per_batch)) * Tk;
+    if (mrow != nullptr) {
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int c = k * G + lane;
-            if (live && c < nvec) {
-                float m[V];
-                load_keep<T>(mrow + static_cast<int64_t>(c) * V, m);
+            mr[k] = load_keep_raw<T>(mrow + (c < nvec ? static_cast<int64_t>(c) * V : 0));
+        }
+    } else {
 #pragma unroll
-                for (int e = 0; e < V; ++e) z[k][e] += m[e];
-            }
+        for (int k = 0; k < IT; ++k)
+#pragma unroll
+            for (int e = 0; e < V; ++e) mr[k][e] = T(0);
+    }
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        if ((k + 1) * G > nvec) {  // uniform: this vector slot has idle lanes
+            RV ninf;
+#pragma unroll
+            for (int e = 0; e < V; ++e) ninf[e] = static_cast<T>(-INFINITY);
+            xr[k] = k * G + lane < nvec ? xr[k] : ninf;
         }
     }
+    float one = 1.0f;
+    if constexpr (V == 8) asm("" : "+v"(one));
+    float z[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            z[k][e] = __builtin_fmaf(static_cast<float>(xr[k][e]), one, static_cast<float>(mr[k][e]));
     if (causal) {
         const int qi = static_cast<int>(row - divu32(row, per_query) * per_query.d);
 #pragma unroll
