@@ -150,17 +150,41 @@ __global__ __launch_bounds__(WG) void softmax_bw_vec(T *dinp, const T *dout,
     const int nvec = Tk / V;
     const int64_t base = (live ? row : 0) * static_cast<int64_t>(Tk);
 
-    float yv[IT][V], gv[IT][V];
+    // Every load unconditional (an idle lane reads its row's first vector, a row past the end
+    // row 0), so no branch makes the compiler wait between loads (with a branch per vector it
+    // waited after every pair of loads: 5-10% slower at 2-4 vectors per lane). Idle lanes then
+    // take y = 0 (a select only in buckets wider than the row), which removes them from the sum.
+    using RV = RawVec<T>;
+    RV yr[IT], gr[IT];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
-        if (live && c < nvec) {
-            load_stream<T>(y + base + static_cast<int64_t>(c) * V, yv[k]);
-            load_stream<T>(dout + base + static_cast<int64_t>(c) * V, gv[k]);
-        } else {
+        const int64_t off = base + (c < nvec ? static_cast<int64_t>(c) * V : 0);
+        yr[k] = load_stream_raw<T>(y + off);
+        gr[k] = load_stream_raw<T>(dout + off);
+    }
 #pragma unroll
-            for (int e = 0; e < V; ++e) yv[k][e] = gv[k][e] = 0.f;
+    for (int k = 0; k < IT; ++k) {
+        if ((k + 1) * G > nvec) {  // uniform: this vector slot has idle lanes
+            const RV zero = {};
+            yr[k] = k * G + lane < nvec ? yr[k] : zero;
         }
+    }
+    float yv[IT][V], gv[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        widen<T>(yr[k], yv[k]);
+        widen<T>(gr[k], gv[k]);
+    }
+    // The product sum is a chain of fused multiply-adds. With the fp16 widening next to the
+    // multiply, the compiler would pair two products into a dot2 instruction, which rounds
+    // differently; an empty register constraint hides the widened values from that combine
+    // (it emits no instruction), so this kernel and the read-skipping one agree bit for bit.
+    if constexpr (V == 8) {
+#pragma unroll
+        for (int k = 0; k < IT; ++k)
+#pragma unroll
+            for (int e = 0; e < V; ++e) asm("" : "+v"(yv[k][e]), "+v"(gv[k][e]));
     }
     float t = 0.f;
 #pragma unroll
@@ -180,6 +204,7 @@ __global__ __launch_bounds__(WG) void softmax_bw_vec(T *dinp, const T *dout,
         }
     }
 }
+
 
 // ------------------------------------------------------------------------------------------
 // Element-wise fallback kernels: one wave per row, any Tk, any element alignment.
