@@ -151,6 +151,11 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
     uint32_t kn[BDR ? IT : 1];
     float Kn;
     T Kraw = T(0);  // the shift as stored (not kBdrLayerNorm): what idle lanes hold
+    // kBdrLayerNorm: the raw inputs of the row's shift (x, residual and mask of its first
+    // element), loaded with the row and combined when it is reduced. Combined in the fetch,
+    // the compiler sinks the x load under the mask bit and the fetch waits for that load.
+    T x0n = T(0), r0n = T(0);
+    uint32_t m0n = 0u;
     auto fetch = [&](int64_t row, bool live) {
         const int64_t rbase = (live ? row : r0) * static_cast<int64_t>(C);
         const uint8_t *mrow = BDR ? mask + (live ? row : r0) * mb : nullptr;
@@ -169,9 +174,10 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
             }
         }
         if constexpr (BDR) {
-            const float x0 = to_f32(x[rbase]), r0v = to_f32(residual[rbase]);
-            const float s0 = r0v + ((mrow[0] & 1u) ? (x0 + b0) * keep_scale : 0.f);
-            Kn = live ? s0 : 0.f;
+            x0n = x[rbase];
+            r0n = residual[rbase];
+            m0n = mrow[0];
+            Kn = 0.f;
         } else if constexpr (!RMS) {
             Kraw = x[rbase];  // the shift: one broadcast load per group
             Kn = to_f32(Kraw);
@@ -196,8 +202,10 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
                 kc[k] = kn[k];
             }
         }
-        const float K = Kn;
+        float K = Kn;
         const T Kc = Kraw;
+        if constexpr (BDR)
+            K = to_f32(r0n) + ((m0n & 1u) ? (to_f32(x0n) + b0) * keep_scale : 0.f);
         fetch(row + NG, it + 1 < R && row + NG < r1);
 
         float d[IT][V];
