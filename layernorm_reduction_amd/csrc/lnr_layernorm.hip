@@ -379,11 +379,11 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     // DEFER: a row's dx is stored after the next row's fetch has been issued. Memory
     // operations retire in issue order, so a store issued before a fetch holds up the wait for
     // that fetch's data by its own round trip. It pays off where a row sits inside one wave
-    // with one vector per lane (measured on MI355X, fp16, 256 columns: -4% backward time).
-    // Rows spread over several waves (a barrier per row) ran 4-5% slower with it and three
-    // vectors per lane ran out of registers (-14%): those plans store each row as soon as it is
-    // formed.
-    constexpr bool DEFER = DEPTH == 1 && G <= 64 && IT == 1 && !BDR;
+    // with one or two vectors per lane (measured on MI355X: fp16 256 columns -4% backward time,
+    // fp32 512 columns -9%). Rows spread over several waves (a barrier per row) ran 4-5% slower
+    // with it and three vectors per lane ran out of registers (-14%): those plans store each
+    // row as soon as it is formed.
+    constexpr bool DEFER = DEPTH == 1 && G <= 64 && IT <= 2 && !BDR;
     const int64_t iters = (rows_per_block + NG - 1) / NG;
     auto row_of = [&](int64_t it) { return (it * NG + grp) * P + first_row; };
     auto fetch = [&](RowBuf &b, int64_t it) {
@@ -810,19 +810,21 @@ template <> struct LnFwTable<float> {  // V = 4
         {2048, 256, 2, 256, 2}, {4096, 512, 2, 512, 2}, {8192, 1024, 2, 1024, 2}};
 };
 // The backward row kernel runs within 2-11% of a read-two-write-one stream of the same size
-// (N = 16384..32768). Timed alone, two vectors per lane over 512 threads at 1024 columns was
-// 2% faster than the plan below, but 1-5% slower inside the whole backward; not taken.
+// (N = 16384..32768). Up to 1024 columns (fp16) and 512 (fp32) a row sits inside one wave and
+// its dx stores are deferred (DEFER in the kernel): with that, two vectors per lane over 512
+// threads beat a row over two waves at fp16 1024 columns (-0.5 to -2.4%) and at fp32 512
+// columns (-9%). Four fp32 vectors per lane at 1024 columns spill and lose (+3%).
 template <typename T> struct LnBwTable;
 template <> struct LnBwTable<f16> {
     static constexpr LnPlan plans[] = {
         {64, 8, 1, 512, 1},      {128, 16, 1, 512, 1},    {256, 32, 1, 512, 1},
-        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 128, 1, 1024, 1},
+        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 64, 2, 512, 1},
         {2048, 256, 1, 1024, 1}, {4096, 256, 2, 512, 2},  {8192, 512, 2, 512, 2}};
 };
 template <> struct LnBwTable<float> {
     static constexpr LnPlan plans[] = {
         {64, 16, 1, 512, 1},     {128, 32, 1, 512, 1},    {256, 64, 1, 512, 1},
-        {512, 128, 1, 512, 1},   {768, 64, 3, 512, 1},    {1024, 256, 1, 1024, 1},
+        {512, 64, 2, 512, 1},    {768, 64, 3, 512, 1},    {1024, 256, 1, 1024, 1},
         {2048, 512, 1, 1024, 1}, {4096, 1024, 1, 1024, 1}, {8192, 1024, 2, 1024, 1}};
 };
 
