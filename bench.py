@@ -350,13 +350,20 @@ def summarize_profiles(root_dir: str, workload: str):
 
 class HipEvents:
     """Timing events created through the HIP runtime (hipEvent_t handles as plain ints), so
-    the library's lnr_time_next_launch hook can record them at a kernel's own start/end."""
+    the library's lnr_time_next_launch hook can record them at a kernel's own start/end.
+
+    They are created with hipEventDisableSystemFence: recording one then skips the
+    system-scope cache writeback and invalidation that a default event performs, which would
+    slow the kernel it brackets. The events only give timestamps, read after a device-wide
+    synchronize."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
 
     def __init__(self):
         import ctypes
         self.ct = ctypes
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -365,8 +372,8 @@ class HipEvents:
         out = []
         for _ in range(n):
             h = self.ct.c_void_p()
-            if self.hip.hipEventCreate(self.ct.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(self.ct.byref(h), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(h.value)
         return out
 
