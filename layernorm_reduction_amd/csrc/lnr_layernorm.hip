@@ -794,13 +794,14 @@ struct LnPlan {
 // two rows per group above, where the prefetch of the second row pays (at 4096-8192 columns
 // 6-12% faster than one row; at 1024 fp16 columns one row is 3-8% faster than two). fp32 at
 // 1024 columns is a tie and keeps two. At 8192 fp16 columns the forward takes four vectors
-// per lane over four waves. The same plans serve RMSNorm and the bias-dropout-residual
-// LayerNorm.
+// per lane over four waves. At 1024 fp16 columns four rows per 256-thread workgroup beat two
+// per 128 threads by 1-2% (64, 512 and 1024 threads: tie, tie, 8% slower). The same plans
+// serve RMSNorm and the bias-dropout-residual LayerNorm.
 template <typename T> struct LnFwTable;
 template <> struct LnFwTable<f16> {  // V = 8
     static constexpr LnPlan plans[] = {
         {64, 8, 1, 256, 1},     {128, 16, 1, 256, 1},   {256, 16, 2, 256, 1},
-        {512, 32, 2, 256, 1},   {768, 32, 3, 64, 1},    {1024, 64, 2, 128, 1},
+        {512, 32, 2, 256, 1},   {768, 32, 3, 64, 1},    {1024, 64, 2, 256, 1},
         {2048, 128, 2, 128, 1}, {4096, 256, 2, 256, 2}, {8192, 256, 4, 256, 2}};
 };
 template <> struct LnFwTable<float> {  // V = 4
