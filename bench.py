@@ -364,6 +364,7 @@ class HipEvents:
         self.ct = ctypes
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -376,6 +377,11 @@ class HipEvents:
                 raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(h.value)
         return out
+
+    def record(self, ev, stream):
+        """Record `ev` on `stream` (a hipStream_t as an int; 0 is the default stream)."""
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = self.ct.c_float()
@@ -919,24 +925,28 @@ def main():
     # ---------------------------------------------------------------- diagnostics (untimed)
     ops = {}
     if not args.no_ops:
-        # Per operation: the whole call bracketed by events (includes the launch latency of
-        # each of its kernels), and the first kernel's own duration through the hook.
+        # Per operation, in two passes so that neither set of events perturbs the other: the
+        # first kernel's own duration through the hook, then the whole call bracketed by
+        # events on its stream (includes the launch latency of each of its kernels).
         names = ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw")
         nbytes = (b_sfw, b_sbw, b_lfw, b_lbw)
         reps = max(20, min(K, 200))
+        stream = torch.cuda.current_stream().cuda_stream
         for k, (name, nb) in enumerate(zip(names, nbytes)):
-            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
             ka, kb = hev.create(reps), hev.create(reps)
             for i in range(reps):
-                c = sets[i % n_sets]["calls"][k]
-                pairs[i][0].record()
                 hook(ka[i], kb[i])
-                c()
-                pairs[i][1].record()
+                sets[i % n_sets]["calls"][k]()
             torch.cuda.synchronize()
-            us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
             kus = sorted(hev.elapsed_ms(a, b) * 1e3 for a, b in zip(ka, kb))
-            hev.destroy(ka + kb)
+            ca, cb = hev.create(reps), hev.create(reps)
+            for i in range(reps):
+                hev.record(ca[i], stream)
+                sets[i % n_sets]["calls"][k]()
+                hev.record(cb[i], stream)
+            torch.cuda.synchronize()
+            us = sorted(hev.elapsed_ms(a, b) * 1e3 for a, b in zip(ca, cb))
+            hev.destroy(ka + kb + ca + cb)
             med, kmed = us[len(us) // 2], kus[len(kus) // 2]
             ops[name] = {"bytes": nb, "call_median_us": round(med, 2),
                          "kernel_median_us": round(kmed, 2),
