@@ -7,7 +7,11 @@ entries). Checked here:
     seeded inputs, the backward on identical stored inputs (y = the oracle's output rounded to
     the storage type), and the chained pass;
   * equality with the dense entry points on the same inputs (a property of the design: the
-    skipped runs contribute exactly 0 either way; equality is numeric, so -0 equals +0);
+    skipped runs contribute exactly 0 either way; equality is numeric, so -0 equals +0). The
+    backward is equal where both use the same launch plan; where they do not (256 fp16 keys:
+    the dense backward takes four vectors per lane, the skipping one a single vector), the row
+    sum adds the same products in another order, and the two agree to one unit in the last
+    place of the storage type;
   * that skipped runs are really not read: NaN planted in them leaves the outputs finite and
     equal to the oracle's on clean inputs, where a read would poison the row (NaN + -inf and
     0 * NaN are NaN);
@@ -29,6 +33,18 @@ DEV = "cuda:0"
 
 def _dev(t):
     return None if t is None else t.to(DEV)
+
+
+def assert_equal_or_one_ulp(a, b, what):
+    """a == b element by element, or within one unit in the last place of b's storage type."""
+    if torch.equal(a, b):
+        return
+    an = a.detach().cpu().numpy()
+    bn = b.detach().cpu().numpy()
+    ulp = np.spacing(np.abs(bn)).astype(np.float64)
+    diff = np.abs(an.astype(np.float64) - bn.astype(np.float64))
+    bad = ~(diff <= ulp)
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements differ by more than one ulp"
 
 
 def run_skip(case, check_chain=True):
@@ -57,7 +73,7 @@ def run_skip(case, check_chain=True):
     dx_dense = lnr.attn_softmax_bw(dyd, ytd)
     torch.cuda.synchronize()
     assert_close(dx, dx_ref, case.dtype, f"{case.name} bw_skip")
-    assert torch.equal(dx, dx_dense), f"{case.name}: bw_skip differs from the dense backward"
+    assert_equal_or_one_ulp(dx, dx_dense, f"{case.name}: bw_skip against the dense backward")
     del dx_ref, dx, dx_dense, ytd
 
     if check_chain:
