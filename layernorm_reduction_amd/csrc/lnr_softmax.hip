@@ -280,8 +280,11 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 // 128-byte lines; the backward (one product sum) mostly with one vector per lane and as many
 // lanes per row as the row allows. At 256 fp16 keys the backward takes four vectors per lane
 // over eight lanes, like the forward: 2-3% faster from 32 to 256 MiB tensors (interleaved
-// timing, median of 9). The read-skipping backward keeps one vector per lane there (7-12%
-// slower with four), so the two add a row's products in different orders at that width.
+// timing, median of 9); at 1024 keys four vectors over 32 lanes (-4%) and at 2048 keys
+// 256-thread workgroups (-4%). Fewer lanes per row lose badly on short rows (32-128 keys:
+// 1.04-3.8x slower) and at 512 keys (+2-5%). The read-skipping backward keeps one vector per
+// lane at 256 keys (7-12% slower with four), so the two add a row's products in different
+// orders at that width.
 // ------------------------------------------------------------------------------------------
 struct Plan {
     int bucket;  // longest row this instantiation takes; 0 = element-wise fallback
@@ -305,7 +308,7 @@ template <typename T> struct SoftmaxBwTable;
 template <> struct SoftmaxBwTable<f16> {
     static constexpr Plan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 256},
                                      {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 64, 1, 128},
-                                     {768, 32, 3, 256}, {1024, 64, 2, 128}, {2048, 64, 4, 128}};
+                                     {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
 };
 template <> struct SoftmaxBwTable<float> {
     static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 256},
