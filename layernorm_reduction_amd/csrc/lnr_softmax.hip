@@ -278,13 +278,15 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 // sum, scale) runs best with 2-4 vectors per lane from 256 columns up, and with 1-2 vectors
 // per lane on short rows, where fewer, wider groups keep each load instruction on whole
 // 128-byte lines; the backward (one product sum) mostly with one vector per lane and as many
-// lanes per row as the row allows. At 256 fp16 keys the backward takes four vectors per lane
-// over eight lanes, like the forward: 2-3% faster from 32 to 256 MiB tensors (interleaved
-// timing, median of 9); at 1024 keys four vectors over 32 lanes (-4%) and at 2048 keys
-// 256-thread workgroups (-4%). Fewer lanes per row lose badly on short rows (32-128 keys:
-// 1.04-3.8x slower) and at 512 keys (+2-5%). The read-skipping backward keeps one vector per
-// lane at 256 keys (7-12% slower with four), so the two add a row's products in different
-// orders at that width.
+// lanes per row as the row allows. Exceptions, timed against the previous plan in one process
+// (median of 9): fp16 256 keys take four vectors over eight lanes like the forward (-2 to -3%
+// from 32 to 256 MiB), fp16 1024 keys four vectors over 32 lanes (-4%), fp16 2048 and fp32
+// 1024 keys 256-thread workgroups (-4%, -5%). Fewer lanes per row lose on 32-128 fp16 keys
+// (1.04-3.8x slower) and at 512 (+2-5%). The read-skipping backward keeps one vector per lane
+// at 256 fp16 keys (7-12% slower with four), so the two add a row's products in different
+// orders there and agree to an fp16 ulp; fp32 512 keys over 32 lanes with four vectors was
+// 1-4% faster but not taken, since at fp32 storage the cancellation in dy - sum makes two
+// summation orders differ by more than an ulp.
 // ------------------------------------------------------------------------------------------
 struct Plan {
     int bucket;  // longest row this instantiation takes; 0 = element-wise fallback
@@ -313,7 +315,7 @@ template <> struct SoftmaxBwTable<f16> {
 template <> struct SoftmaxBwTable<float> {
     static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 256},
                                      {256, 64, 1, 128}, {384, 32, 3, 256}, {512, 64, 2, 128},
-                                     {768, 64, 3, 128}, {1024, 64, 4, 128}, {2048, 64, 8, 128}};
+                                     {768, 64, 3, 128}, {1024, 64, 4, 256}, {2048, 64, 8, 128}};
 };
 
 struct SoftmaxFwArgs {
