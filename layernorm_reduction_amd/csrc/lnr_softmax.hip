@@ -277,11 +277,13 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 // are the HW4 page's template list. Measured on MI355X: the forward (mask add, max, exp,
 // sum, scale) runs best with 2-4 vectors per lane from 256 columns up, and with 1-2 vectors
 // per lane on short rows, where fewer, wider groups keep each load instruction on whole
-// 128-byte lines; the backward (one product sum) mostly with one vector per lane and as many
-// lanes per row as the row allows. Exceptions, timed against the previous plan in one process
-// (median of 9): fp16 256 keys take four vectors over eight lanes like the forward (-2 to -3%
-// from 32 to 256 MiB), fp16 1024 keys four vectors over 32 lanes (-4%), fp16 2048 and fp32
-// 1024 keys 256-thread workgroups (-4%, -5%). Fewer lanes per row lose on 32-128 fp16 keys
+// 128-byte lines; its fp16 32- and 64-key rows run in 128-thread workgroups (-2% against 512;
+// other sizes tie or lose up to 8% at the longer rows, which keep 256). The backward (one
+// product sum) runs best mostly with one vector per lane and as many lanes per row as the row
+// allows. Its exceptions, timed against the previous plan in one process (median of 9): fp16
+// 256 keys take four vectors over eight lanes like the forward (-2 to -3% from 32 to 256
+// MiB), fp16 1024 keys four vectors over 32 lanes (-4%), fp16 2048 and fp32 1024 keys
+// 256-thread workgroups (-4%, -5%). Fewer lanes per row lose on 32-128 fp16 keys
 // (1.04-3.8x slower) and at 512 (+2-5%). The read-skipping backward keeps one vector per lane
 // at 256 fp16 keys (7-12% slower with four), so the two add a row's products in different
 // orders there and agree to an fp16 ulp; fp32 512 keys over 32 lanes with four vectors was
@@ -297,7 +299,7 @@ struct Plan {
 
 template <typename T> struct SoftmaxFwTable;
 template <> struct SoftmaxFwTable<f16> {   // V = 8
-    static constexpr Plan plans[] = {{32, 4, 1, 512},   {64, 8, 1, 512},   {128, 8, 2, 256},
+    static constexpr Plan plans[] = {{32, 4, 1, 128},   {64, 8, 1, 128},   {128, 8, 2, 256},
                                      {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 32, 2, 256},
                                      {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
 };
