@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the fused softmax / LayerNorm row-reduction hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input:
-    attn_softmax_fw -> attn_softmax_bw -> layernorm_fw -> layernorm_bw
-on the GPT-2 training shapes (B=32, T=256, C=256, H=8, fp16 storage, fp32 compute):
-softmax over [32, 8, 256, 256] causal scores and LayerNorm over [8192, 256] activations.
-``--workload w5`` runs the large encoder-layer shapes instead (softmax [64,16,512,512] with
-key padding, LayerNorm [32768,1024]).
+One step = one pass of the whole path over one batch of synthetic input: the large
+encoder-layer training shapes (LightSeq's max_seq_len 512, fp16 storage, fp32 compute):
+    attn_softmax_fw -> attn_softmax_bw   on [64, 16, 512, 512] scores with key padding,
+    layernorm_fw -> layernorm_bw         on [32768, 1024] activations,
+    layernorm_fw -> layernorm_bw         on [32768, 4096] activations.
+The same shapes are repeated in fp32 storage (reported under "fp32_repeat", not part of the
+step). ``--workload w2`` runs the GPT-2 training shapes instead (B=32, T=256, C=256, H=8:
+causal softmax over [32, 8, 256, 256] and LayerNorm over [8192, 256]).
 
 The metric is achieved HBM bandwidth: the algorithmic bytes of one step (every tensor read
 or written once, dense) divided by the measured step time. Inputs are resident in HBM before
@@ -43,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=2000)
-    p.add_argument("--workload", choices=("w2", "w5"), default="w2")
+    p.add_argument("--workload", choices=("w2", "w5"), default="w5")
     p.add_argument("--sample-every", type=int, default=8, metavar="S",
                    help="time the dominant kernel's own duration on every S-th timed step (each "
                         "timed launch goes through hipExtLaunchKernel with two events, which "
@@ -83,8 +85,7 @@ def parse():
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
              "-d $OUT/prof_{w} -o {w} -- python3 $REPO/bench.py{args}")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {ctr} -f csv "
-           "-d $OUT/pmc_{kind}_{w} -o {w} -- python3 $REPO/bench.py{args} "
-           "--steps 20 --warmup 5 --no-cpu-baseline")
+           "-d $OUT/pmc_{kind}_{w} -o {w} -- python3 $REPO/bench.py{args}")
 DOMINANT = "softmax_bw_vec"
 COPY = "copy16"
 SKIP_PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {ctr} -f csv "
@@ -269,7 +270,7 @@ def summarize_profiles(root_dir: str, workload: str):
     import csv
     import collections
 
-    args = "" if workload == "w2" else " --workload w5 --steps 50 --warmup 5 --no-cpu-baseline"
+    args = (" --workload w2" if workload == "w2" else "") + " --steps 20 --warmup 5 --no-cpu-baseline"
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     stats = os.path.join(root_dir, f"prof_{workload}", f"{workload}_kernel_stats.csv")
@@ -337,7 +338,8 @@ def summarize_profiles(root_dir: str, workload: str):
         if k in write:
             fb, wb = fetch[k] * f_scale, write[k] * w_scale
             rows.append(f"| `{k[:90]}` | {fb / 1e6:.3f} | {wb / 1e6:.3f} | {(fb + wb) / 1e6:.3f} |")
-    dom_f, dom_w = pick(fetch, DOMINANT) * f_scale, pick(write, DOMINANT) * w_scale
+    # the step's softmax backward is the fp16 instantiation (the fp32 repeat has its own)
+    dom_f, dom_w = pick(fetch, DOMINANT + "IDF16_") * f_scale, pick(write, DOMINANT + "IDF16_") * w_scale
     with open(os.path.join(out_dir, f"{workload}_traffic.md"), "w") as fh:
         fh.write("\n".join(rows) + "\n")
     with open(os.path.join(out_dir, f"traffic_softmax_bw_{workload}.json"), "w") as fh:
@@ -837,48 +839,28 @@ def main():
     lnr.load()
 
     # ---------------------------------------------------------------- workload
-    if args.workload == "w2":
-        [sc], [lc] = W.workload2()
-        wl_name = "GPT-2 training shapes B=32 T=256 C=256 H=8: causal softmax [32,8,256,256] + LayerNorm [8192,256]"
-    else:
-        sc = W.workload5_softmax(torch.float16)
-        lc = W.workload5_layernorm(1024, torch.float16)
-        wl_name = "encoder layer: padded softmax [64,16,512,512] + LayerNorm [32768,1024]"
-    s = W.dtype_size(sc.dtype)
-    b_sfw = W.softmax_fw_bytes(sc.B, sc.H, sc.Tq, sc.Tk, s, has_mask=sc.mask is not None)
-    b_sbw = W.softmax_bw_bytes(sc.B, sc.H, sc.Tq, sc.Tk, s)
-    b_lfw = W.layernorm_fw_bytes(lc.N, lc.C, s)
-    b_lbw = W.layernorm_bw_bytes(lc.N, lc.C, s)
-    step_bytes = b_sfw + b_sbw + b_lfw + b_lbw
-
-    per_set = 4 * sc.x.numel() * s + 4 * lc.x.numel() * s
+    wl_name, parts = workload_parts(args.workload)
+    calls_meta = []       # (op label, algorithmic bytes) in step order
+    per_set = 0
+    for kind, c in parts:
+        s = W.dtype_size(c.dtype)
+        if kind == "softmax":
+            tag = f"[{c.B},{c.H},{c.Tq},{c.Tk}]"
+            calls_meta += [(f"attn_softmax_fw {tag}", W.softmax_fw_bytes(c.B, c.H, c.Tq, c.Tk, s, has_mask=c.mask is not None)),
+                           (f"attn_softmax_bw {tag}", W.softmax_bw_bytes(c.B, c.H, c.Tq, c.Tk, s))]
+        else:
+            tag = f"[{c.N},{c.C}]"
+            calls_meta += [(f"layernorm_fw {tag}", W.layernorm_fw_bytes(c.N, c.C, s)),
+                           (f"layernorm_bw {tag}", W.layernorm_bw_bytes(c.N, c.C, s))]
+        per_set += 4 * c.x.numel() * s
+    step_bytes = sum(nb for _, nb in calls_meta)
+    dom = 1                                   # the softmax backward: three passes over the scores
+    b_sbw = calls_meta[dom][1]
     n_sets = max(2, math.ceil(MIN_FOOTPRINT / per_set))
     log(f"workload {args.workload}: {wl_name}; {step_bytes / 1e6:.1f} MB/step; {n_sets} input sets "
         f"({n_sets * per_set / 2 ** 30:.2f} GiB)")
 
-    sets = []
-    ws_bytes = lnr.layernorm_bw_workspace_bytes(lc.N, lc.C, lnr.LNR_F16 if lc.dtype == torch.float16 else lnr.LNR_F32)
-    for i in range(n_sets):
-        t = {
-            "sx": sc.x.to(dev), "sdy": sc.dy.to(dev), "sy": torch.empty_like(sc.x, device=dev),
-            "sdx": torch.empty_like(sc.x, device=dev),
-            "smask": None if sc.mask is None else sc.mask.to(dev),
-            "lx": lc.x.to(dev), "ldy": lc.dy.to(dev), "lg": lc.gamma.to(dev), "lb": lc.beta.to(dev),
-            "ly": torch.empty_like(lc.x, device=dev), "ldx": torch.empty_like(lc.x, device=dev),
-            "mean": torch.empty(lc.N, dtype=torch.float32, device=dev),
-            "rstd": torch.empty(lc.N, dtype=torch.float32, device=dev),
-            "dg": torch.empty(lc.C, dtype=lc.dtype, device=dev),
-            "db": torch.empty(lc.C, dtype=lc.dtype, device=dev),
-            "ws": torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev),
-        }
-        t["calls"] = (
-            lnr.bind_attn_softmax_fw(t["sx"], t["smask"], sc.causal, t["sy"]),
-            lnr.bind_attn_softmax_bw(t["sdy"], t["sy"], t["sdx"]),
-            lnr.bind_layernorm_fw(t["lx"], t["lg"], t["lb"], lc.eps, t["ly"], t["mean"], t["rstd"]),
-            lnr.bind_layernorm_bw(t["ldy"], t["lx"], t["lg"], t["mean"], t["rstd"], t["ldx"], t["dg"],
-                                  t["db"], t["ws"]),
-        )
-        sets.append(t)
+    sets = [bind_parts(lnr, parts, dev) for _ in range(n_sets)]
     torch.cuda.synchronize()
 
     def step(i):
@@ -893,9 +875,10 @@ def main():
     # ---------------------------------------------------------------- timed region
     # The dominant kernel (softmax backward: three passes over the quadratic score tensor) is
     # timed inside the timed steps with HIP events that the kernel itself records at its start
-    # and end (lnr_time_next_launch), on the stream it runs on, on every S-th step.
+    # and end (lnr_time_next_launch), on the stream it runs on: on every step of a short run
+    # (fewer than 160 steps), else on every S-th step.
     K = args.steps
-    every = max(1, args.sample_every)
+    every = 1 if K < 160 else max(1, args.sample_every)
     n_samp = (K + every - 1) // every
     hev = HipEvents()
     ev_a, ev_b = hev.create(n_samp), hev.create(n_samp)
@@ -903,57 +886,29 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        sfw, sbw, lfw, lbw = sets[i % n_sets]["calls"]
-        sfw()
-        if i % every == 0:
-            hook(ev_a[i // every], ev_b[i // every])
-        sbw()
-        lfw()
-        lbw()
+        for j, c in enumerate(sets[i % n_sets]["calls"]):
+            if j == dom and i % every == 0:
+                hook(ev_a[i // every], ev_b[i // every])
+            c()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / K
     value = step_bytes * K / elapsed / 1e9
-    sbw_ms = [hev.elapsed_ms(a, b) for a, b in zip(ev_a, ev_b)]
+    sbw_us = sorted(hev.elapsed_ms(a, b) * 1e3 for a, b in zip(ev_a, ev_b))
     hev.destroy(ev_a + ev_b)
-    sbw_avg_us = statistics.mean(sbw_ms) * 1e3
+    sbw_avg_us = statistics.mean(sbw_us)
     sbw_gbps = b_sbw / (sbw_avg_us * 1e-6) / 1e9
     log(f"step {ms_per_step * 1e3:.1f} us -> {value:.0f} GB/s ({value / PEAK_HBM_GBPS:.1%} of 8 TB/s); "
-        f"softmax_bw kernel {sbw_avg_us:.1f} us -> {sbw_gbps:.0f} GB/s")
+        f"softmax_bw kernel {sbw_avg_us:.1f} us over {len(sbw_us)} launches -> {sbw_gbps:.0f} GB/s")
 
     # ---------------------------------------------------------------- diagnostics (untimed)
-    ops = {}
+    ops, parts_out, fp32 = {}, {}, None
     if not args.no_ops:
-        # Per operation, in two passes so that neither set of events perturbs the other: the
-        # first kernel's own duration through the hook, then the whole call bracketed by
-        # events on its stream (includes the launch latency of each of its kernels).
-        names = ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw")
-        nbytes = (b_sfw, b_sbw, b_lfw, b_lbw)
         reps = max(20, min(K, 200))
         stream = torch.cuda.current_stream().cuda_stream
-        for k, (name, nb) in enumerate(zip(names, nbytes)):
-            ka, kb = hev.create(reps), hev.create(reps)
-            for i in range(reps):
-                hook(ka[i], kb[i])
-                sets[i % n_sets]["calls"][k]()
-            torch.cuda.synchronize()
-            kus = sorted(hev.elapsed_ms(a, b) * 1e3 for a, b in zip(ka, kb))
-            ca, cb = hev.create(reps), hev.create(reps)
-            for i in range(reps):
-                hev.record(ca[i], stream)
-                sets[i % n_sets]["calls"][k]()
-                hev.record(cb[i], stream)
-            torch.cuda.synchronize()
-            us = sorted(hev.elapsed_ms(a, b) * 1e3 for a, b in zip(ca, cb))
-            hev.destroy(ka + kb + ca + cb)
-            med, kmed = us[len(us) // 2], kus[len(kus) // 2]
-            ops[name] = {"bytes": nb, "call_median_us": round(med, 2),
-                         "kernel_median_us": round(kmed, 2),
-                         "GBps": round(nb / (med * 1e-6) / 1e9, 1),
-                         "frac_of_peak": round(nb / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
-            if name != "layernorm_bw":   # one kernel: its own duration is the op's
-                ops[name]["kernel_GBps"] = round(nb / (kmed * 1e-6) / 1e9, 1)
+        for k, (name, nb) in enumerate(calls_meta):
+            ops[name] = time_op(hev, hook, stream, [st["calls"][k] for st in sets], nb, reps)
         # streaming copy ceiling: 16-byte loads/stores over 1 GiB
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -970,33 +925,26 @@ def main():
         ops["copy_1GiB"] = {"bytes": 2 * n, "call_median_us": round(cus, 1),
                             "GBps": round(2 * n / (cus * 1e-6) / 1e9, 1)}
         del src, dst
+        torch.cuda.empty_cache()
         # Same-size streaming ceilings, back to back over rotating buffers like the step: a
         # copy of one op tensor (the forward pattern) and read-two-write-one (the backward).
-        torch.cuda.empty_cache()
-        for op, nb, pattern in (("attn_softmax_fw", sc.x.numel() * s, "copy"),
-                                ("attn_softmax_bw", sc.x.numel() * s, "read2write1"),
-                                ("layernorm_fw", lc.x.numel() * s, "copy"),
-                                ("layernorm_bw", lc.x.numel() * s, "read2write1")):
-            nbuf = max(2, math.ceil(MIN_FOOTPRINT / (3 * nb)))
-            bufs = [[torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(3)] for _ in range(nbuf)]
-            go = ((lambda b: lnr.copy_bytes(b[2], b[0])) if pattern == "copy"
-                  else (lambda b: lnr.xor_bytes(b[2], b[0], b[1])))
-            for i in range(3):
-                go(bufs[i % nbuf])
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record()
-            for i in range(reps):
-                go(bufs[i % nbuf])
-            b.record()
-            torch.cuda.synchronize()
-            cu = a.elapsed_time(b) * 1e3 / reps
-            ops[op]["same_size_ceiling"] = {"pattern": pattern, "tensor_bytes": nb, "b2b_us": round(cu, 2)}
-            del bufs
-            torch.cuda.empty_cache()
+        for (kind, c), k in zip(parts, range(0, len(calls_meta), 2)):
+            nb = c.x.numel() * W.dtype_size(c.dtype)
+            for name, pattern in ((calls_meta[k][0], "copy"), (calls_meta[k + 1][0], "read2write1")):
+                ops[name]["same_size_ceiling"] = {"pattern": pattern, "tensor_bytes": nb,
+                                                  "b2b_us": round(same_size_ceiling(lnr, dev, nb, pattern, reps), 2)}
+        parts_out = fwbw_summary(parts, calls_meta, ops)
         for k, v in ops.items():
-            log(f"  {k:16s} call {v['call_median_us']:9.1f} us  {v['GBps']:8.1f} GB/s"
+            log(f"  {k:32s} call {v['call_median_us']:9.1f} us  {v['GBps']:8.1f} GB/s"
                 + (f"  | kernel {v['kernel_median_us']:8.1f} us" if "kernel_median_us" in v else ""))
+        for k, v in parts_out.items():
+            log(f"  fw+bw {k:40s} {v['GBps']:8.1f} GB/s ({v['frac_of_peak']:.1%} of 8 TB/s)")
+        if args.workload == "w5":
+            # The same encoder-layer shapes repeated in fp32 storage (both dtypes against the
+            # roofline); each op back to back over rotating input sets, not part of the step.
+            del sets
+            torch.cuda.empty_cache()
+            fp32 = run_fp32_repeat(lnr, W, dev, hev, hook, stream, reps)
 
     # ---------------------------------------------------------------- roofline
     traffic = None
@@ -1006,52 +954,20 @@ def main():
             tr = json.load(fh)
         if tr.get("source_sha256") == source_digest():
             traffic = tr.get("bytes_per_launch")
+    pct = lambda q: sbw_us[min(len(sbw_us) - 1, int(q * len(sbw_us)))]
     roofline = {"bound": "hbm", "kernel": "softmax_bw_vec (attn_softmax_bw)", "achieved": round(sbw_gbps, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(sbw_gbps / PEAK_HBM_GBPS, 4),
-                "traffic": traffic, "avg_us": round(sbw_avg_us, 3), "launches": n_samp,
-                "sampled": f"every {every}th of {K} timed steps", "bytes_per_launch": b_sbw}
+                "traffic": traffic, "avg_us": round(sbw_avg_us, 3), "median_us": round(pct(0.5), 3),
+                "min_us": round(sbw_us[0], 3), "p90_us": round(pct(0.9), 3), "launches": len(sbw_us),
+                "sampled": f"every {every} of {K} timed steps" if every > 1 else f"every one of {K} timed steps",
+                "bytes_per_launch": b_sbw}
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        log("timing the oracle on the host cores")
-        if args.workload == "w2":
-            xs, dys, ms = sc.x, sc.dy, sc.mask
-            xl, dyl = lc.x, lc.dy
-            frac = 1.0
-            sample = "one whole step: softmax fw+bw [32,8,256,256] and LayerNorm fw+bw [8192,256]"
-        else:
-            bsub = 8
-            xs, dys, ms = sc.x[:bsub], sc.dy[:bsub], None if sc.mask is None else sc.mask[:bsub]
-            xl, dyl = lc.x[: lc.N // 8], lc.dy[: lc.N // 8]
-            frac = bsub / sc.B
-            sample = "1/8 of a step: softmax fw+bw [8,16,512,512] and LayerNorm fw+bw [4096,1024]"
-        g64 = lc.gamma
-        b64 = lc.beta
-        times = []
-        t_start = time.perf_counter()
-        while True:
-            c0 = time.perf_counter()
-            y = oracle.softmax_fw(xs, ms, sc.causal)
-            oracle.softmax_bw(y, dys)
-            del y
-            oracle.layernorm_fw(xl, g64, b64, lc.eps)
-            oracle.layernorm_bw(xl, dyl, g64, lc.eps)
-            times.append(time.perf_counter() - c0)
-            # about 10 s of CPU work in all (at least 3 samples, never past 30 s)
-            spent = time.perf_counter() - t_start
-            if (len(times) >= 3 and spent >= 10.0) or spent >= 30.0:
-                break
-        tmed = statistics.median(times)
-        cpu = {"value": round(step_bytes * frac / tmed / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
-               "cpu_model": cpu_model(),
-               "kind": "oracle", "sample": f"{sample}, repeated {len(times)} times",
-               "seconds_per_sample": round(tmed, 3), "repeats": len(times),
-               "seconds_total": round(sum(times), 1),
-               "note": "fp64 correctness oracle, not a tuned CPU kernel; the median sample is reported"}
-        log(f"oracle: {tmed:.2f} s per sample on {cpu['cores']} threads -> {cpu['value']} GB/s")
+        cpu = cpu_baseline(args.workload, parts, step_bytes)
 
+    first = parts[0][1]
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -1067,15 +983,203 @@ def main():
         "data": "synthetic",
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "config": {"workload": wl_name, "storage": "fp16", "compute": "fp32",
-                   "softmax": [sc.B, sc.H, sc.Tq, sc.Tk], "causal": sc.causal,
-                   "key_padding": sc.mask is not None, "layernorm": [lc.N, lc.C],
+                   "softmax": [first.B, first.H, first.Tq, first.Tk], "causal": first.causal,
+                   "key_padding": first.mask is not None,
+                   "layernorm": [[c.N, c.C] for kind, c in parts if kind == "layernorm"],
                    "bytes_per_step": step_bytes, "input_sets": n_sets, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ops": ops,
+        "fwbw": parts_out,
+        "fp32_repeat": fp32,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out), flush=True)
+
+
+def workload_parts(name):
+    """(description, [(kind, case), ...]) of a bench workload: the ops of one step in order."""
+    import torch
+    from layernorm_reduction_amd import workloads as W
+    if name == "w5":
+        return ("encoder layer, max_seq_len 512: padded softmax [64,16,512,512] + LayerNorm "
+                "[32768,1024] + LayerNorm [32768,4096], fp16 storage",
+                [("softmax", W.workload5_softmax(torch.float16)),
+                 ("layernorm", W.workload5_layernorm(1024, torch.float16)),
+                 ("layernorm", W.workload5_layernorm(4096, torch.float16))])
+    [sc], [lc] = W.workload2()
+    return ("GPT-2 training shapes B=32 T=256 C=256 H=8: causal softmax [32,8,256,256] + "
+            "LayerNorm [8192,256], fp16 storage", [("softmax", sc), ("layernorm", lc)])
+
+
+def bind_parts(lnr, parts, dev):
+    """One input set on the device: every buffer of every op, and the bound calls (fw, bw per
+    op, in step order)."""
+    import torch
+    t = {"calls": [], "keep": []}
+    for kind, c in parts:
+        if kind == "softmax":
+            x, dy = c.x.to(dev), c.dy.to(dev)
+            y, dx = torch.empty_like(x), torch.empty_like(x)
+            m = None if c.mask is None else c.mask.to(dev)
+            t["calls"] += [lnr.bind_attn_softmax_fw(x, m, c.causal, y), lnr.bind_attn_softmax_bw(dy, y, dx)]
+            t["keep"] += [x, dy, y, dx, m]
+        else:
+            code = lnr.LNR_F16 if c.dtype == torch.float16 else lnr.LNR_F32
+            x, dy, g, b = c.x.to(dev), c.dy.to(dev), c.gamma.to(dev), c.beta.to(dev)
+            y, dx = torch.empty_like(x), torch.empty_like(x)
+            mean = torch.empty(c.N, dtype=torch.float32, device=dev)
+            rstd = torch.empty(c.N, dtype=torch.float32, device=dev)
+            dg, db = torch.empty(c.C, dtype=c.dtype, device=dev), torch.empty(c.C, dtype=c.dtype, device=dev)
+            ws = torch.empty(max(lnr.layernorm_bw_workspace_bytes(c.N, c.C, code), 1), dtype=torch.uint8,
+                             device=dev)
+            t["calls"] += [lnr.bind_layernorm_fw(x, g, b, c.eps, y, mean, rstd),
+                           lnr.bind_layernorm_bw(dy, x, g, mean, rstd, dx, dg, db, ws)]
+            t["keep"] += [x, dy, g, b, y, dx, mean, rstd, dg, db, ws]
+    return t
+
+
+def time_op(hev, hook, stream, calls, nb, reps):
+    """One op over rotating input sets, in two passes so that neither set of events perturbs
+    the other: the first kernel's own duration through the hook, then the whole call
+    bracketed by events on its stream (includes the launch latency of each of its kernels)."""
+    import torch
+    n = len(calls)
+    ka, kb = hev.create(reps), hev.create(reps)
+    for i in range(reps):
+        hook(ka[i], kb[i])
+        calls[i % n]()
+    torch.cuda.synchronize()
+    kus = sorted(hev.elapsed_ms(a, b) * 1e3 for a, b in zip(ka, kb))
+    ca, cb = hev.create(reps), hev.create(reps)
+    for i in range(reps):
+        hev.record(ca[i], stream)
+        calls[i % n]()
+        hev.record(cb[i], stream)
+    torch.cuda.synchronize()
+    us = sorted(hev.elapsed_ms(a, b) * 1e3 for a, b in zip(ca, cb))
+    hev.destroy(ka + kb + ca + cb)
+    med, kmed = us[len(us) // 2], kus[len(kus) // 2]
+    return {"bytes": nb, "call_median_us": round(med, 2), "call_min_us": round(us[0], 2),
+            "call_p90_us": round(us[int(0.9 * len(us))], 2), "kernel_median_us": round(kmed, 2),
+            "GBps": round(nb / (med * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nb / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "kernel_GBps": round(nb / (kmed * 1e-6) / 1e9, 1)}
+
+
+def same_size_ceiling(lnr, dev, nb, pattern, reps):
+    """Back-to-back time of the copy (forward pattern) or read-two-write-one (backward) helper
+    over tensors of nb bytes, rotating buffers like the step."""
+    import torch
+    nbuf = max(2, math.ceil(MIN_FOOTPRINT / (3 * nb)))
+    bufs = [[torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(3)] for _ in range(nbuf)]
+    go = ((lambda b: lnr.copy_bytes(b[2], b[0])) if pattern == "copy"
+          else (lambda b: lnr.xor_bytes(b[2], b[0], b[1])))
+    for i in range(3):
+        go(bufs[i % nbuf])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        go(bufs[i % nbuf])
+    b.record()
+    torch.cuda.synchronize()
+    cu = a.elapsed_time(b) * 1e3 / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return cu
+
+
+def fwbw_summary(parts, calls_meta, ops):
+    """fw+bw GB/s per op of the step from the call medians: (fw bytes + bw bytes) / (t_fw + t_bw)."""
+    out = {}
+    for (kind, c), k in zip(parts, range(0, len(calls_meta), 2)):
+        fw, bw = ops[calls_meta[k][0]], ops[calls_meta[k + 1][0]]
+        nb = fw["bytes"] + bw["bytes"]
+        us = fw["call_median_us"] + bw["call_median_us"]
+        label = calls_meta[k][0].split(" ", 1)[1]
+        name = f"{'softmax' if kind == 'softmax' else 'layernorm'} {label} {'fp16' if c.dtype.itemsize == 2 else 'fp32'}"
+        out[name] = {"bytes": nb, "us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+    return out
+
+
+def run_fp32_repeat(lnr, W, dev, hev, hook, stream, reps):
+    """The encoder-layer shapes in fp32 storage: each op's call and kernel medians over two
+    rotating input sets, and fw+bw GB/s per op."""
+    import torch
+    parts = [("softmax", W.workload5_softmax(torch.float32)),
+             ("layernorm", W.workload5_layernorm(1024, torch.float32)),
+             ("layernorm", W.workload5_layernorm(4096, torch.float32))]
+    ops, calls_meta = {}, []
+    for kind, c in parts:
+        s = W.dtype_size(c.dtype)
+        sets = [bind_parts(lnr, [(kind, c)], dev) for _ in range(2)]
+        torch.cuda.synchronize()
+        if kind == "softmax":
+            tag = f"[{c.B},{c.H},{c.Tq},{c.Tk}]"
+            meta = [(f"attn_softmax_fw {tag}", W.softmax_fw_bytes(c.B, c.H, c.Tq, c.Tk, s, has_mask=True)),
+                    (f"attn_softmax_bw {tag}", W.softmax_bw_bytes(c.B, c.H, c.Tq, c.Tk, s))]
+        else:
+            tag = f"[{c.N},{c.C}]"
+            meta = [(f"layernorm_fw {tag}", W.layernorm_fw_bytes(c.N, c.C, s)),
+                    (f"layernorm_bw {tag}", W.layernorm_bw_bytes(c.N, c.C, s))]
+        for k, (name, nb) in enumerate(meta):
+            for i in range(3):
+                sets[i % 2]["calls"][k]()
+            ops[name] = time_op(hev, hook, stream, [st["calls"][k] for st in sets], nb, reps)
+            log(f"  fp32 {name:32s} call {ops[name]['call_median_us']:9.1f} us  {ops[name]['GBps']:8.1f} GB/s")
+        calls_meta += meta
+        del sets
+        torch.cuda.empty_cache()
+    return {"ops": ops, "fwbw": fwbw_summary(parts, calls_meta, ops)}
+
+
+def cpu_baseline(workload, parts, step_bytes):
+    """The oracle timed on the host cores over a bounded sample of the step (about 10 s of CPU
+    work in all), scaled to the step's bytes."""
+    import oracle
+    log("timing the oracle on the host cores")
+    if workload == "w2":
+        frac, sample = 1.0, "one whole step: softmax fw+bw [32,8,256,256] and LayerNorm fw+bw [8192,256]"
+        cut = lambda n: n
+    else:
+        frac = 1.0 / 8
+        sample = ("1/8 of a step: softmax fw+bw [8,16,512,512], LayerNorm fw+bw [4096,1024] and "
+                  "[4096,4096]")
+        cut = lambda n: n // 8
+    work = []
+    for kind, c in parts:
+        if kind == "softmax":
+            b = cut(c.B)
+            work.append(("softmax", c.x[:b], c.dy[:b], None if c.mask is None else c.mask[:b], c.causal))
+        else:
+            n = cut(c.N)
+            work.append(("layernorm", c.x[:n], c.dy[:n], c.gamma, c.beta, c.eps))
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        c0 = time.perf_counter()
+        for w in work:
+            if w[0] == "softmax":
+                y = oracle.softmax_fw(w[1], w[3], w[4])
+                oracle.softmax_bw(y, w[2])
+                del y
+            else:
+                oracle.layernorm_fw(w[1], w[3], w[4], w[5])
+                oracle.layernorm_bw(w[1], w[2], w[3], w[5])
+        times.append(time.perf_counter() - c0)
+        spent = time.perf_counter() - t_start
+        if (len(times) >= 3 and spent >= 10.0) or spent >= 30.0:
+            break
+    tmed = statistics.median(times)
+    cpu = {"value": round(step_bytes * frac / tmed / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+           "cpu_model": cpu_model(), "kind": "oracle", "sample": f"{sample}, repeated {len(times)} times",
+           "seconds_per_sample": round(tmed, 3), "repeats": len(times),
+           "seconds_total": round(sum(times), 1),
+           "note": "fp64 correctness oracle, not a tuned CPU kernel; the median sample is reported"}
+    log(f"oracle: {tmed:.2f} s per sample on {cpu['cores']} threads -> {cpu['value']} GB/s")
+    return cpu
 
 
 if __name__ == "__main__":

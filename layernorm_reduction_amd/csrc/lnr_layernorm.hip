@@ -427,11 +427,16 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
             else
                 b.mu = 0.f;
         } else {
+            // mean is NULL in RMSNorm mode: it is never dereferenced there.
             const int64_t srow = live ? row : first_row;
             const float rl = rstd[srow];
-            const float ml = mean[srow];
-            b.mu = live ? ml : 0.f;
             b.rs = live ? rl : 0.f;
+            if constexpr (!RMS) {
+                const float ml = mean[srow];
+                b.mu = live ? ml : 0.f;
+            } else {
+                b.mu = 0.f;
+            }
         }
     };
     // A row's dx as stored, held until the next row's fetch has been issued (DEFER only).
@@ -494,7 +499,18 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
                 gv[k][e] = gmf[e] * df[e];
                 if constexpr (!RMS) sg += gv[k][e];
                 sgx = __builtin_fmaf(gv[k][e], xh[k][e], sgx);
-                adg[k][e] += static_cast<A>(df[e] * xh[k][e]);
+                if constexpr (std::is_same_v<A, double>) {
+                    // fp32 storage: the column term dy * xhat is formed in double from the
+                    // stored values and the fp32 statistics (x - mean and the product with rstd
+                    // are exact in double, the fma rounds once at 2^-53), so a column sum over
+                    // tens of thousands of rows carries no fp32 rounding of its terms.
+                    const double xhd = RMS ? static_cast<double>(xf[e]) * static_cast<double>(rs)
+                                           : (static_cast<double>(xf[e]) - static_cast<double>(mu)) *
+                                                 static_cast<double>(rs);
+                    adg[k][e] = __builtin_fma(static_cast<double>(df[e]), xhd, adg[k][e]);
+                } else {
+                    adg[k][e] += static_cast<A>(df[e] * xh[k][e]);
+                }
                 if constexpr (!RMS) adb[k][e] += static_cast<A>(df[e]);
             }
         }
@@ -768,8 +784,16 @@ __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_colpart_generic(
     for (int64_t r = r0; r < r1; ++r) {
         const float d = to_f32(dy[r * C + col]);
         const float xv = to_f32(x[r * C + col]);
-        const float xh = RMS ? xv * rstd[r] : (xv - mean[r]) * rstd[r];
-        sg += static_cast<A>(d * xh);
+        if constexpr (std::is_same_v<A, double>) {
+            // fp32 storage: the term formed in double, as in the vector kernel.
+            const double rs = static_cast<double>(rstd[r]);
+            const double xh = RMS ? static_cast<double>(xv) * rs
+                                  : (static_cast<double>(xv) - static_cast<double>(mean[r])) * rs;
+            sg = __builtin_fma(static_cast<double>(d), xh, sg);
+        } else {
+            const float xh = RMS ? xv * rstd[r] : (xv - mean[r]) * rstd[r];
+            sg += static_cast<A>(d * xh);
+        }
         sb += static_cast<A>(d);
     }
     part[(static_cast<int64_t>(blockIdx.y) * 2 + 0) * C + col] = sg;
@@ -1072,7 +1096,8 @@ static int norm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const vo
         overlap(dx, nbytes, rstd, N * 4) || overlap(dgamma, cbytes, dbeta, cbytes) ||
         overlap(workspace, need, dx, nbytes) || overlap(workspace, need, x, nbytes) ||
         overlap(workspace, need, dy, nbytes) || overlap(workspace, need, dgamma, cbytes) ||
-        overlap(workspace, need, dbeta, cbytes))
+        overlap(workspace, need, dbeta, cbytes) || overlap(workspace, need, gamma, cbytes) ||
+        overlap(workspace, need, mean, N * 4) || overlap(workspace, need, rstd, N * 4))
         return LNR_ERR_ALIAS;
     for (const void *out : {dgamma, dbeta})
         if (overlap(out, cbytes, x, nbytes) || overlap(out, cbytes, dy, nbytes) ||
@@ -1223,6 +1248,12 @@ static int bdr_bw(void *dres, void *dx, void *dgamma, void *dbeta, void *dbias, 
             return LNR_ERR_ALIAS;
     }
     if (overlap(dgamma, cb, dbeta, cb) || overlap(dgamma, cb, dbias, cb) || overlap(dbeta, cb, dbias, cb))
+        return LNR_ERR_ALIAS;
+    // Every workgroup writes its partial row while others still read the inputs.
+    if (overlap(workspace, need, dy, nb) || overlap(workspace, need, s_in, nb) ||
+        overlap(workspace, need, ds_extra, nb) || overlap(workspace, need, gamma, cb) ||
+        overlap(workspace, need, mean, N * 4) || overlap(workspace, need, rstd, N * 4) ||
+        overlap(workspace, need, mask, mbytes))
         return LNR_ERR_ALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -4,10 +4,16 @@ Tolerances (|gpu - oracle| <= atol + rtol * |oracle|, element by element, the al
 convention of the HW4 page's kernel tests):
   * fp16 storage: atol = rtol = 1e-3 (the HW4 page, "Faster than what?").
   * fp32 storage: atol = rtol = 1e-5.
-Column sums over N rows of products formed in fp32 (dgamma = sum_i dy * xhat) carry the fp32
-rounding of every term, random over rows: about 2^-24 * sqrt(sum_i (dy * xhat)^2) per column,
-which reaches 1e-5 on near-zero columns from a few thousand rows up. Their bound adds six
-times that (colsum_slack; see assert_close's `slack`).
+Every comparison prints the largest ratio of error to bound it saw, so the margin is on record.
+
+Input gradients of the normalisations (assert_grad_close): dx = rstd * (g - mean(g) - xhat *
+mean(g * xhat)) is formed in fp32 from terms as large as rstd * |g|, so its rounding error is a
+few units of fp32 roundoff times rstd * max_j |g_ij| for its row. Below rstd = 8 (a row
+variance above 1/64) that is under 1e-5 for the workloads' gradients and the plain bound holds.
+Only near-constant rows (a C = 2 row with nearly equal entries, a zero row) have an exact dx
+that is a tiny remainder of much larger terms; the edge-case tests, and only they, let those
+rows add the rounding term 16 * 2^-24 * rstd_i * max_j |g_ij| to the bound, and print how many
+elements needed it.
 """
 from __future__ import annotations
 
@@ -52,38 +58,30 @@ def violations(got: np.ndarray, ref: np.ndarray, atol: float, rtol: float, chunk
     return bad, worst
 
 
-def colsum_slack(dy64: np.ndarray, xhat64: np.ndarray, rows: int = 4096) -> np.ndarray:
-    """Per-column allowance for the fp32 rounding of the N terms of sum_i dy_ij * xhat_ij: xhat
-    (two fp32 operations) and the product (one) each round with relative error below 2^-24,
-    independently over rows, so the sum's error has a standard deviation of about
-    2^-24 * sqrt(sum_i (dy * xhat)^2); the allowance is six of those."""
-    sq = np.zeros(dy64.shape[1])
-    for s in range(0, dy64.shape[0], rows):
-        sq += np.sum((dy64[s:s + rows] * xhat64[s:s + rows]) ** 2, axis=0)
-    return 6.0 * 2.0 ** -24 * np.sqrt(sq)
+def worst_ratio(got: np.ndarray, ref: np.ndarray, atol: float, rtol: float, chunk: int = 1 << 24) -> float:
+    """Largest |got - ref| / (atol + rtol * |ref|) over all elements (inf if any is NaN)."""
+    g = got.reshape(-1)
+    r = ref.reshape(-1)
+    w = 0.0
+    for s in range(0, g.size, chunk):
+        with np.errstate(invalid="ignore"):
+            q = np.abs(g[s:s + chunk] - r[s:s + chunk]) / (atol + rtol * np.abs(r[s:s + chunk]))
+        if q.size:
+            m = float(np.max(q)) if not np.isnan(q).any() else float("inf")
+            w = max(w, m)
+    return w
 
 
-def assert_close(got, ref, dtype, what: str, atol=None, rtol=None, slack=None):
-    """Element-wise |got - ref| <= atol + rtol * |ref| (+ slack, a per-element array)."""
+def assert_close(got, ref, dtype, what: str, atol=None, rtol=None):
+    """Element-wise |got - ref| <= atol + rtol * |ref|; prints the worst error-to-bound ratio."""
     a0, r0 = TOL[dtype]
     atol = a0 if atol is None else atol
     rtol = r0 if rtol is None else rtol
     got = to_host64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
-    if slack is not None:
-        atol = atol + np.asarray(slack, np.float64).reshape(-1)
-        assert atol.size == got.size, (what, atol.size, got.size)
-        got, ref = got.reshape(-1), ref.reshape(-1)
-        bad = ~(np.abs(got - ref) <= atol + rtol * np.abs(ref))
-        if bad.any():
-            idx = int(np.argmax(np.where(bad, np.abs(got - ref) - atol - rtol * np.abs(ref), -np.inf)))
-            raise AssertionError(
-                f"{what}: {int(bad.sum())} of {got.size} elements outside atol={TOL[dtype][0]} + "
-                f"fp32 column-sum slack, rtol={rtol}; worst at index {idx}: gpu={got[idx]!r} "
-                f"oracle={ref[idx]!r} |diff|={abs(got[idx] - ref[idx]):.3e} slack="
-                f"{float(atol[idx]) - TOL[dtype][0]:.3e}")
-        return
+    print(f"[parity] {what}: worst err/bound {worst_ratio(got, ref, atol, rtol):.3f} "
+          f"(atol={atol:g} rtol={rtol:g})", flush=True)
     bad, (idx, ex) = violations(got, ref, atol, rtol)
     if bad:
         gi = got.reshape(-1)[idx]
@@ -96,3 +94,43 @@ def assert_close(got, ref, dtype, what: str, atol=None, rtol=None, slack=None):
 def max_abs_err(got, ref) -> float:
     got = to_host64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
     return float(np.max(np.abs(got - np.asarray(ref, np.float64)))) if got.size else 0.0
+
+
+U32 = 2.0 ** -24
+NEAR_CONSTANT_RSTD = 8.0
+
+
+def assert_grad_close(got_t, ref, dtype, what: str, rstd, gmax, allow_near_constant: bool = False,
+                      factor: float = 1.0):
+    """Element-wise plain bound atol + rtol * |ref| on a normalisation's input gradient.
+
+    rstd [N] and gmax [N] (max_j of the magnitudes the row's fp32 formula subtracts) give the
+    rounding term 16 * 2^-24 * rstd_i * gmax_i (times `factor` for a gradient scaled after it is
+    formed). That term is added only where allow_near_constant is set and only on rows with
+    rstd_i >= NEAR_CONSTANT_RSTD; the number of elements that needed it is printed."""
+    atol, rtol = TOL[dtype]
+    got = to_host64(got_t) if isinstance(got_t, torch.Tensor) else np.asarray(got_t, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    r = np.asarray(rstd, np.float64).reshape(-1, 1)
+    err = np.abs(got - ref)
+    lim0 = atol + rtol * np.abs(ref)
+    plain_bad = ~(err <= lim0)
+    ratio = float(np.max(err / lim0)) if err.size else 0.0
+    n_allow = 0
+    if allow_near_constant:
+        term = factor * 16.0 * U32 * r * np.asarray(gmax, np.float64).reshape(-1, 1)
+        term = np.where(r >= NEAR_CONSTANT_RSTD, term, 0.0)
+        lim = lim0 + term
+        bad = ~(err <= lim)
+        n_allow = int(np.sum(plain_bad & ~bad))
+    else:
+        lim = lim0
+        bad = plain_bad
+    print(f"[parity] {what}: worst err/plain bound {ratio:.3f}; {n_allow} of {err.size} elements "
+          f"(near-constant rows) needed the rounding term", flush=True)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err - lim, -np.inf)), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} elements outside the bound; "
+                             f"worst at {i}: gpu={got[i]!r} oracle={ref[i]!r} bound={lim[i]:.3e} "
+                             f"rstd={float(r[i[0], 0]):.3e}")

@@ -171,6 +171,9 @@ def test_layernorm_bw_validation(lib):
     assert lbw(lib, dx=A + 2 ** 30 + 64) == ALIAS            # dx over dy
     assert lbw(lib, db=A + 2 ** 33 + 2) == ALIAS             # dbeta over dgamma
     assert lbw(lib, ws=A + 2 ** 30) == ALIAS                 # workspace over dy
+    assert lbw(lib, ws=A + 2 ** 32) == ALIAS                 # workspace over gamma
+    assert lbw(lib, ws=A + 2 ** 32 + 2 ** 20) == ALIAS       # workspace over mean
+    assert lbw(lib, ws=A + 2 ** 32 + 2 ** 21) == ALIAS       # workspace over rstd
 
 
 def rfw(lib, y=A, rstd=A + 2 ** 32, x=A + 2 ** 30, g=A + 2 ** 31, N=64, C=64, eps=1e-6, dtype=F16):
@@ -212,6 +215,8 @@ def test_rmsnorm_bw_validation(lib):
     assert rbw(lib, dx=A + 2 ** 31) == ALIAS                 # dx over x
     assert rbw(lib, dg=A + 2 ** 30 + 2) == ALIAS             # dgamma over dy
     assert rbw(lib, ws=A + 2 ** 31) == ALIAS                 # workspace over x
+    assert rbw(lib, ws=A + 2 ** 32) == ALIAS                 # workspace over gamma
+    assert rbw(lib, ws=A + 2 ** 32 + 2 ** 21) == ALIAS       # workspace over rstd
     assert lib.rmsnorm_bw_workspace_bytes(0, 64, F16) == 0
 
 
@@ -302,6 +307,14 @@ def test_bdr_layernorm_bw_validation(lib):
     assert bbw(lib, dx=A + 64) == ALIAS                      # dx over dresidual
     assert bbw(lib, dr=A + 2 ** 30 + 128) == ALIAS           # dresidual partially over dy
     assert bbw(lib, dbias=A + 2 ** 29 + 2) == ALIAS          # dbias over dgamma
+    # the workspace (written while other workgroups still read) over any input
+    assert bbw(lib, ws=A + 2 ** 30) == ALIAS                 # over dy
+    assert bbw(lib, ws=A + 2 ** 31) == ALIAS                 # over s
+    assert bbw(lib, de=A + 2 ** 35, ws=A + 2 ** 35) == ALIAS  # over ds_extra
+    assert bbw(lib, ws=A + 2 ** 32) == ALIAS                 # over the keep mask
+    assert bbw(lib, ws=A + 2 ** 32 + 2 ** 20) == ALIAS       # over gamma
+    assert bbw(lib, ws=A + 2 ** 33) == ALIAS                 # over mean
+    assert bbw(lib, ws=A + 2 ** 33 + 2 ** 20) == ALIAS       # over rstd
     # (N = 0 launches the zero-fill of the parameter gradients: covered by the GPU tests)
 
 

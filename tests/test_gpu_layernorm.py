@@ -5,59 +5,39 @@
     fp32 (the ABI's statistics format) and is compared, element by element, with the oracle's
     backward evaluated on those same fp32 statistics (dx, dgamma, dbeta);
   * chained: GPU forward statistics feeding the GPU backward, against the true gradient (the
-    oracle recomputes the statistics from x in fp64), with twice the tolerance because the
-    chain also carries the fp32 rounding of the statistics.
+    oracle recomputes the statistics from x in fp64).
 Workloads 1, 2, 4 and 5 run at their full sizes, in the launch configuration the benchmark uses.
 
-dx tolerance: the fp32 formula dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) carries a
-rounding error of a few units of fp32 roundoff times rstd * max |g| of its row, because the
-terms it subtracts are that large. For rows of ordinary spread this is far below atol; for
-rows whose exact dx is a tiny remainder (C = 2 rows with nearly equal entries, where the
-projection removes all but eps/(var + eps) of g - mean(g)) it is the whole error. The dx
-bound is therefore atol + rtol * |ref| + 16 * 2^-24 * rstd_i * max_j |g_ij|.
-
-Identical-input dgamma: each term dy * xhat is formed in fp32, so the column sum carries the
-fp32 rounding of N terms; its bound adds six standard deviations of that rounding per column
-(parity_utils.colsum_slack), which matters only for near-zero columns at fp32 storage.
-
-Chained dgamma with fp32 storage over N = 32768 rows: the column sums of dy * xhat over 32768
-rows carry the fp32 rounding of every row's statistics (about 6e-8 relative per row, random
-over rows), about 1e-5 absolute, so near-zero columns can miss an element-wise 1e-5 bound
-however exactly the sum is taken. That one comparison uses the norm-wise bound
-max |err| <= atol + rtol * max |ref| and prints its element-wise pass rate.
+Every comparison uses the plain element-wise bound atol + rtol * |ref| (1e-3 fp16, 1e-5 fp32),
+with two exceptions, both printed when they apply:
+  * near-constant rows of the edge-case tests (parity_utils.assert_grad_close): dx of a row
+    with rstd >= 8 may add the fp32 formula's own rounding term;
+  * the chained dgamma at fp32 storage over 32768 rows is compared norm-wise, max |err| <=
+    atol + rtol * max |ref|, with its element-wise pass rate printed: every row's fp32
+    statistics carry about 1e-7 relative rounding, random over rows, and a column sum over
+    32768 rows accumulates that to about 1e-5 absolute, so near-zero columns can miss an
+    element-wise 1e-5 however exactly the sum itself is taken.
 """
 import numpy as np
 import pytest
 import torch
 
+import gpu_cases
 import layernorm_reduction_amd as lnr
 import oracle
 from layernorm_reduction_amd import workloads as W
-from parity_utils import TOL, assert_close, colsum_slack, say, to_host64, violations
+from parity_utils import TOL, assert_close, assert_grad_close, say, to_host64, violations
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-U32 = 2.0 ** -24
+def gmax_of(dy64, g64):
+    """Per row, max_j |gamma_j * dy_ij|: the largest term the dx formula subtracts from."""
+    return np.max(np.abs(dy64 * g64.reshape(1, -1)), axis=1)
 
 
-def assert_dx_close(dx, ref, dtype, what, dy64, g64, rstd, scale=1.0):
-    """Element-wise bound plus the fp32 formula's own rounding term (see the module note)."""
-    atol, rtol = TOL[dtype]
-    got = to_host64(dx)
-    cond = 16.0 * U32 * np.asarray(rstd, np.float64).reshape(-1, 1) * \
-        np.max(np.abs(dy64 * g64.reshape(1, -1)), axis=1, keepdims=True)
-    err = np.abs(got - ref)
-    lim = scale * (atol + rtol * np.abs(ref)) + cond
-    bad = ~(err <= lim)
-    if bad.any():
-        i = np.unravel_index(np.argmax(np.where(bad, err - lim, -np.inf)), err.shape)
-        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} elements outside the bound; "
-                             f"worst at {i}: gpu={got[i]!r} oracle={ref[i]!r} bound={lim[i]:.3e}")
-
-
-def run_ln(case, chain=True, chain_dgamma_normwise=False):
+def run_ln(case, chain=True, chain_dgamma_normwise=False, edge=False):
     atol, rtol = TOL[case.dtype]
     say(case.name, "oracle forward")
     x64 = case.x.double().numpy()
@@ -82,10 +62,10 @@ def run_ln(case, chain=True, chain_dgamma_normwise=False):
     dyd = case.dy.to(DEV)
     dx, dg, db = lnr.layernorm_bw(dyd, xd, gd, m32.to(DEV), r32.to(DEV))
     torch.cuda.synchronize()
-    assert_dx_close(dx, dx_ref, case.dtype, f"{case.name} dx", dy64, g64, r32.double().numpy())
-    xhat64 = (x64 - m32.double().numpy()[:, None]) * r32.double().numpy()[:, None]
-    assert_close(dg, dg_ref, case.dtype, f"{case.name} dgamma", slack=colsum_slack(dy64, xhat64))
-    del xhat64
+    gm = gmax_of(dy64, g64)
+    assert_grad_close(dx, dx_ref, case.dtype, f"{case.name} dx", r32.double().numpy(), gm,
+                      allow_near_constant=edge)
+    assert_close(dg, dg_ref, case.dtype, f"{case.name} dgamma")
     assert_close(db, db_ref, case.dtype, f"{case.name} dbeta")
     del dx_ref, dg_ref, db_ref, dx, dg, db
 
@@ -94,19 +74,18 @@ def run_ln(case, chain=True, chain_dgamma_normwise=False):
         tdx, tdg, tdb = oracle.layernorm_bw(x64, dy64, g64, case.eps)
         dx2, dg2, db2 = lnr.layernorm_bw(dyd, xd, gd, mean, rstd)
         torch.cuda.synchronize()
-        s = 2.0
-        assert_dx_close(dx2, tdx, case.dtype, f"{case.name} chain dx", dy64, g64, rstd_ref, scale=s)
-        assert_close(db2, tdb, case.dtype, f"{case.name} chain dbeta", atol=atol * s, rtol=rtol * s)
+        assert_grad_close(dx2, tdx, case.dtype, f"{case.name} chain dx", rstd_ref, gm,
+                          allow_near_constant=edge)
+        assert_close(db2, tdb, case.dtype, f"{case.name} chain dbeta")
         if chain_dgamma_normwise:
             got = to_host64(dg2)
-            bad, _ = violations(got, tdg, atol * s, rtol * s)
+            bad, _ = violations(got, tdg, atol, rtol)
             print(f"[info] {case.name} chained dgamma element-wise: {case.C - bad}/{case.C} within "
-                  f"atol=rtol={atol * s}", flush=True)
+                  f"atol=rtol={atol}", flush=True)
             err = np.max(np.abs(got - tdg))
-            assert err <= atol * s + rtol * s * np.max(np.abs(tdg)), err
+            assert err <= atol + rtol * np.max(np.abs(tdg)), err
         else:
-            assert_close(dg2, tdg, case.dtype, f"{case.name} chain dgamma", atol=atol * s,
-                         rtol=rtol * s)
+            assert_close(dg2, tdg, case.dtype, f"{case.name} chain dgamma")
     del xd, gd, bd, dyd
     torch.cuda.empty_cache()
 
@@ -134,7 +113,7 @@ def test_workload5_encoder_layer(C, dtype):
 
 # ------------------------------------------------------------------------- edge cases
 
-EDGE_C = [1, 2, 8, 24, 64, 100, 264, 1000, 1024, 2056, 4095, 4096, 8191, 8192]
+EDGE_C = gpu_cases.NORM_EDGE_C
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
@@ -143,7 +122,7 @@ def test_bucket_boundaries_and_ragged_rows(C, dtype):
     for N in (1, 7, 1031):
         case = W.layernorm_case(f"edge-N{N}-C{C}-{dtype}", N, C, dtype=dtype,
                                 seed_base=7000 + C, row_offset_var=1.0)
-        run_ln(case, chain=False)
+        run_ln(case, chain=False, edge=True)
 
 
 def odd_trip_count(N, C, dtype):
@@ -224,11 +203,10 @@ def test_unaligned_buffers_take_the_fallback(dtype):
     x64, g64 = case.x.double().numpy(), case.gamma.double().numpy()
     y_ref, _, _ = oracle.layernorm_fw(x64, g64, case.beta.double().numpy(), case.eps)
     dx_ref, dg_ref, db_ref = oracle.layernorm_bw(x64, case.dy.double().numpy(), g64, case.eps)
-    atol, rtol = TOL[dtype]
     assert_close(y, y_ref, dtype, "unaligned y")
-    assert_close(dx, dx_ref, dtype, "unaligned dx", atol=2 * atol, rtol=2 * rtol)
-    assert_close(dg, dg_ref, dtype, "unaligned dgamma", atol=2 * atol, rtol=2 * rtol)
-    assert_close(db, db_ref, dtype, "unaligned dbeta", atol=2 * atol, rtol=2 * rtol)
+    assert_close(dx, dx_ref, dtype, "unaligned dx")
+    assert_close(dg, dg_ref, dtype, "unaligned dgamma")
+    assert_close(db, db_ref, dtype, "unaligned dbeta")
 
 
 def test_zero_rows_give_zero_parameter_gradients():

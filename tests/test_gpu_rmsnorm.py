@@ -5,46 +5,36 @@ RMSNorm as the FastTransformer page defines it (section 5.4): y = x * rsqrt(mean
   * forward: y and rstd on seeded inputs, every element;
   * backward on identical stored inputs: the GPU receives the oracle's rstd rounded to fp32
     and is compared with the oracle's backward evaluated on that same rstd;
-  * chained: GPU forward rstd feeding the GPU backward, against the true gradient, with twice
-    the tolerance.
+  * chained: GPU forward rstd feeding the GPU backward, against the true gradient.
 
-dx tolerance: dx = rstd * (g - xhat * b) with b = mean(g * xhat) subtracts two terms that can
-both be much larger than their difference; fp32 evaluation carries a rounding error of a few
-units of fp32 roundoff times rstd * max_j (|g_ij| + |xhat_ij * b_i|). The dx bound is
-atol + rtol * |ref| + 16 * 2^-24 * rstd_i * max_j (|g_ij| + |xhat_ij b_i|).
+Plain element-wise bounds throughout (1e-3 fp16, 1e-5 fp32), with the LayerNorm tests' two
+printed exceptions: near-constant rows of the edge-case tests (rstd >= 8; here also the zero
+rows, rstd = 1/sqrt(eps)) may add the fp32 formula's rounding term to dx, 16 * 2^-24 * rstd_i
+* max_j (|g_ij| + |xhat_ij b_i|) with b = mean(g * xhat); and the chained dgamma over 32768
+fp32 rows is norm-wise.
 """
 import numpy as np
 import pytest
 import torch
 
+import gpu_cases
 import layernorm_reduction_amd as lnr
 import oracle
 from layernorm_reduction_amd import workloads as W
-from parity_utils import TOL, assert_close, colsum_slack, say, to_host64, violations
+from parity_utils import TOL, assert_close, assert_grad_close, say, to_host64, violations
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-U32 = 2.0 ** -24
-
-
-def assert_rms_dx_close(dx, ref, dtype, what, x64, dy64, g64, rstd, scale=1.0):
-    atol, rtol = TOL[dtype]
-    got = to_host64(dx)
+def rms_gmax(x64, dy64, g64, rstd):
+    """Per row, max_j (|g_ij| + |xhat_ij * b_i|): the terms the dx formula subtracts."""
     r = np.asarray(rstd, np.float64).reshape(-1, 1)
     gd = dy64 * g64.reshape(1, -1)
     xh = x64 * r
     b = np.mean(gd * xh, axis=1, keepdims=True)
-    cond = 16.0 * U32 * r * np.max(np.abs(gd) + np.abs(xh * b), axis=1, keepdims=True)
-    err = np.abs(got - ref)
-    lim = scale * (atol + rtol * np.abs(ref)) + cond
-    bad = ~(err <= lim)
-    if bad.any():
-        i = np.unravel_index(np.argmax(np.where(bad, err - lim, -np.inf)), err.shape)
-        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} elements outside the bound; "
-                             f"worst at {i}: gpu={got[i]!r} oracle={ref[i]!r} bound={lim[i]:.3e}")
+    return np.max(np.abs(gd) + np.abs(xh * b), axis=1)
 
 
-def run_rms(case, chain=True, chain_dgamma_normwise=False):
+def run_rms(case, chain=True, chain_dgamma_normwise=False, edge=False):
     atol, rtol = TOL[case.dtype]
     say(case.name, "oracle forward")
     x64 = case.x.double().numpy()
@@ -67,10 +57,10 @@ def run_rms(case, chain=True, chain_dgamma_normwise=False):
     dyd = case.dy.to(DEV)
     dx, dg = lnr.rmsnorm_bw(dyd, xd, gd, r32.to(DEV))
     torch.cuda.synchronize()
-    assert_rms_dx_close(dx, dx_ref, case.dtype, f"{case.name} dx", x64, dy64, g64, r32.double().numpy())
-    # fp32 rounding of the N products in each column sum (parity_utils.colsum_slack)
-    slack = colsum_slack(dy64, x64 * r32.double().numpy()[:, None])
-    assert_close(dg, dg_ref, case.dtype, f"{case.name} dgamma", slack=slack)
+    r64 = r32.double().numpy()
+    assert_grad_close(dx, dx_ref, case.dtype, f"{case.name} dx", r64, rms_gmax(x64, dy64, g64, r64),
+                      allow_near_constant=edge)
+    assert_close(dg, dg_ref, case.dtype, f"{case.name} dgamma")
     del dx_ref, dg_ref, dx, dg
 
     if chain:
@@ -78,17 +68,17 @@ def run_rms(case, chain=True, chain_dgamma_normwise=False):
         tdx, tdg = oracle.rmsnorm_bw(x64, dy64, g64, case.eps)
         dx2, dg2 = lnr.rmsnorm_bw(dyd, xd, gd, rstd)
         torch.cuda.synchronize()
-        s = 2.0
-        assert_rms_dx_close(dx2, tdx, case.dtype, f"{case.name} chain dx", x64, dy64, g64, rr_ref, scale=s)
+        assert_grad_close(dx2, tdx, case.dtype, f"{case.name} chain dx", rr_ref,
+                          rms_gmax(x64, dy64, g64, rr_ref), allow_near_constant=edge)
         if chain_dgamma_normwise:
             got = to_host64(dg2)
-            bad, _ = violations(got, tdg, atol * s, rtol * s)
+            bad, _ = violations(got, tdg, atol, rtol)
             print(f"[info] {case.name} chained dgamma element-wise: {case.C - bad}/{case.C} within "
-                  f"atol=rtol={atol * s}", flush=True)
+                  f"atol=rtol={atol}", flush=True)
             err = np.max(np.abs(got - tdg))
-            assert err <= atol * s + rtol * s * np.max(np.abs(tdg)), err
+            assert err <= atol + rtol * np.max(np.abs(tdg)), err
         else:
-            assert_close(dg2, tdg, case.dtype, f"{case.name} chain dgamma", atol=atol * s, rtol=rtol * s)
+            assert_close(dg2, tdg, case.dtype, f"{case.name} chain dgamma")
     del xd, gd, dyd
     torch.cuda.empty_cache()
 
@@ -109,7 +99,7 @@ def test_encoder_rows_fp32():
     run_rms(W.rmsnorm_sweep_case(32768, 1024, torch.float32), chain_dgamma_normwise=True)
 
 
-EDGE_C = [1, 2, 8, 24, 64, 100, 264, 1000, 1024, 2056, 4095, 4096, 8191, 8192]
+EDGE_C = gpu_cases.NORM_EDGE_C
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
@@ -118,7 +108,7 @@ def test_bucket_boundaries_and_ragged_rows(C, dtype):
     for N in (1, 7, 1031):
         case = W.layernorm_case(f"rms-edge-N{N}-C{C}-{dtype}", N, C, dtype=dtype,
                                 seed_base=7500 + C, row_offset_var=1.0, eps=W.RMS_EPS)
-        run_rms(case, chain=False)
+        run_rms(case, chain=False, edge=True)
 
 
 @pytest.mark.parametrize("N,C,dtype", [(6141, 512, torch.float16), (10237, 1000, torch.float16)])
@@ -185,10 +175,9 @@ def test_unaligned_buffers_take_the_fallback(dtype):
     x64, g64, dy64 = case.x.double().numpy(), case.gamma.double().numpy(), case.dy.double().numpy()
     y_ref, _ = oracle.rmsnorm_fw(x64, g64, case.eps)
     dx_ref, dg_ref = oracle.rmsnorm_bw(x64, dy64, g64, case.eps)
-    atol, rtol = TOL[dtype]
     assert_close(y, y_ref, dtype, "unaligned y")
-    assert_close(dx, dx_ref, dtype, "unaligned dx", atol=2 * atol, rtol=2 * rtol)
-    assert_close(dg, dg_ref, dtype, "unaligned dgamma", atol=2 * atol, rtol=2 * rtol)
+    assert_close(dx, dx_ref, dtype, "unaligned dx")
+    assert_close(dg, dg_ref, dtype, "unaligned dgamma")
 
 
 def test_zero_rows_count_gives_zero_dgamma():

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import gpu_cases
 import layernorm_reduction_amd as lnr
 import oracle
 from layernorm_reduction_amd import workloads as W
@@ -93,7 +94,7 @@ def test_workload5_encoder_layer(dtype):
 
 # ------------------------------------------------------------------------- edge cases
 
-EDGE_TK = [1, 2, 8, 16, 24, 31, 32, 33, 40, 100, 264, 520, 1000, 2047, 2048]
+EDGE_TK = gpu_cases.SOFTMAX_EDGE_TK
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])

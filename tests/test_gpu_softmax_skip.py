@@ -22,6 +22,7 @@ import numpy as np
 import pytest
 import torch
 
+import gpu_cases
 import layernorm_reduction_amd as lnr
 import oracle
 from layernorm_reduction_amd import workloads as W
@@ -112,7 +113,7 @@ def test_workload5_padded_encoder(dtype):
     run_skip(W.workload5_softmax(dtype), check_chain=False)
 
 
-EDGE_TK = [8, 16, 24, 32, 40, 264, 520, 1000, 2048, 1, 31, 33, 100, 2047]
+EDGE_TK = gpu_cases.SKIP_EDGE_TK
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
