@@ -35,8 +35,7 @@
  *   - Any buffer may start at any address aligned to its element size. Rows whose byte
  *     length is a multiple of 16 and buffers aligned to 16 bytes take the 128-bit vector
  *     kernels; anything else takes a slower element-wise kernel with identical results
- *     up to rounding order. The bias-dropout-residual entry points have no element-wise
- *     kernel and reject such shapes instead (see there).
+ *     up to rounding order.
  */
 #ifndef LNR_H
 #define LNR_H
@@ -220,8 +219,9 @@ LNR_API int rmsnorm_bw(void *dx, void *dgamma, const void *dy, const void *x, co
  *   y      [N, C] dtype, written. mean, rstd [N] float32 of s, written, or both NULL.
  *   x, residual [N, C] dtype, read. bias, gamma, beta [C] dtype, read.
  *   keep_mask [N, ceil(C/8)] bytes, read.  p  drop probability, 0 <= p < 1.
- *   Vector path only: C a multiple of 8 (fp16) or 4 (fp32) -- else LNR_ERR_UNSUPPORTED --
- *   and every [N, C] and [C] buffer 16-byte aligned -- else LNR_ERR_ALIGN. 1 <= C <= 8192.
+ *   Limits: 1 <= C <= LNR_LAYERNORM_MAX_C; N >= 0. C a multiple of 8 (fp16) or 4 (fp32)
+ *   with every [N, C] and [C] buffer 16-byte aligned takes the vector kernel, anything else
+ *   the element-wise kernel.
  */
 LNR_API int bdr_layernorm_fw(void *s, void *y, float *mean, float *rstd, const void *x,
                              const void *residual, const void *bias, const uint8_t *keep_mask,
@@ -248,7 +248,8 @@ LNR_API size_t bdr_layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype 
  *   dy, s [N, C] dtype, read.  ds_extra [N, C] dtype, read, or NULL (no other path into s).
  *   keep_mask, p as in the forward.  gamma [C] dtype; mean, rstd [N] float32, read.
  *   workspace  bdr_layernorm_bw_workspace_bytes(N, C, dtype) bytes, 8-byte aligned, caller
- *   owned; contents on entry do not matter. Same vector-path limits as the forward.
+ *   owned; contents on entry do not matter; must not overlap any other argument.
+ *   Limits and the choice of kernel as in the forward.
  */
 LNR_API int bdr_layernorm_bw(void *dresidual, void *dx, void *dgamma, void *dbeta, void *dbias,
                              const void *dy, const void *ds_extra, const void *s,

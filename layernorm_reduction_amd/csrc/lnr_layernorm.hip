@@ -801,6 +801,119 @@ __global__ __launch_bounds__(kLnGenericWG) void layernorm_bw_colpart_generic(
 }
 
 // ------------------------------------------------------------------------------------------
+// Bias + dropout + residual feeding LayerNorm, element-wise fallback (any C, any element
+// alignment). Forward: one workgroup per row, s formed in fp32 as the vector kernel forms it,
+// stored, and normalised in fp32 (s is formed again in the second pass from the same inputs,
+// so the value normalised is the fp32 one, not the stored rounding). Backward: one workgroup
+// per chunk of rows; every thread owns columns j = tid, tid + WG, ... in every row, so it
+// accumulates its columns' dgamma, dbeta and dbias terms in the workgroup's own partial row
+// of the workspace, in row order (no atomics), for layernorm_bw_colsum to sum.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ bool keep_bit_of(const uint8_t *mrow, int j) {
+    return (mrow[j >> 3] >> (j & 7)) & 1u;
+}
+
+constexpr int kBdrGenericPer = LNR_LAYERNORM_MAX_C / kLnGenericWG;  // row elements per thread
+
+template <typename T>
+__global__ __launch_bounds__(kLnGenericWG) void bdr_layernorm_fw_generic(
+    T *s_out, T *y, float *__restrict__ mean, float *__restrict__ rstd, const T *x,
+    const T *residual, const T *__restrict__ bias, const uint8_t *__restrict__ mask,
+    float keep_scale, const T *__restrict__ gamma, const T *__restrict__ beta, int64_t N,
+    int32_t C, float eps) {
+    __shared__ float red[2 * (kLnGenericWG / 64)];
+    const int64_t row = blockIdx.x;
+    const int64_t base = row * static_cast<int64_t>(C);
+    const uint8_t *mrow = mask + row * static_cast<int64_t>((C + 7) / 8);
+    auto s_of = [&](int j) {
+        const float r = to_f32(residual[base + j]);
+        return r + (keep_bit_of(mrow, j) ? (to_f32(x[base + j]) + to_f32(bias[j])) * keep_scale : 0.f);
+    };
+    // The shift K is the row's first s element. s may replace residual in place, so every
+    // thread reads element 0 before any thread stores, and the row's fp32 s stays in
+    // registers (element j = tid + k * WG) for the second pass.
+    const float K = s_of(0);
+    __syncthreads();
+    float sv[kBdrGenericPer];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < kBdrGenericPer; ++k) {
+        const int j = threadIdx.x + k * kLnGenericWG;
+        if (j < C) {
+            sv[k] = s_of(j);
+            const float d = sv[k] - K;
+            s1 += d;
+            s2 += d * d;
+            s_out[base + j] = from_f32<T>(sv[k]);
+        }
+    }
+    float m1;
+    row_allreduce_sum2<kLnGenericWG>(s1, s2, red);
+    const float rs = ln_stats(s1, s2, 1.0f / static_cast<float>(C), eps, m1);
+#pragma unroll
+    for (int k = 0; k < kBdrGenericPer; ++k) {
+        const int j = threadIdx.x + k * kLnGenericWG;
+        if (j < C) y[base + j] = from_f32<T>(((sv[k] - K) - m1) * rs * to_f32(gamma[j]) + to_f32(beta[j]));
+    }
+    if (threadIdx.x == 0 && rstd != nullptr) {
+        mean[row] = K + m1;
+        rstd[row] = rs;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kLnGenericWG) void bdr_layernorm_bw_generic(
+    T *dres, T *dx, typename Accum<T>::type *part, const T *dy, const T *ds_extra, const T *s,
+    const uint8_t *__restrict__ mask, float keep_scale, const T *__restrict__ gamma,
+    const float *__restrict__ mean, const float *__restrict__ rstd, int64_t N, int32_t C,
+    int64_t rows_per_block) {
+#pragma clang fp contract(off)
+    using A = typename Accum<T>::type;
+    __shared__ float red[2 * (kLnGenericWG / 64)];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+    const int64_t r1 = (r0 + rows_per_block < N) ? r0 + rows_per_block : N;
+    A *pg = part + static_cast<int64_t>(blockIdx.x) * 3 * C;
+    A *pb = pg + C;
+    A *px = pg + 2 * static_cast<int64_t>(C);
+    for (int j = threadIdx.x; j < C; j += kLnGenericWG) pg[j] = pb[j] = px[j] = A(0);
+    const float invC = 1.0f / static_cast<float>(C);
+    const int64_t mb = (C + 7) / 8;
+    for (int64_t row = r0; row < r1; ++row) {
+        const int64_t base = row * static_cast<int64_t>(C);
+        const float mu = mean[row], rs = rstd[row];
+        float sg = 0.f, sgx = 0.f;
+        for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
+            const float g = to_f32(gamma[j]) * to_f32(dy[base + j]);
+            sg += g;
+            sgx = __builtin_fmaf(g, (to_f32(s[base + j]) - mu) * rs, sgx);
+        }
+        row_allreduce_sum2<kLnGenericWG>(sg, sgx, red);
+        const float a = sg * invC, b = sgx * invC;
+        const uint8_t *mrow = mask + row * mb;
+        for (int j = threadIdx.x; j < C; j += kLnGenericWG) {
+            const float d = to_f32(dy[base + j]);
+            const float sv = to_f32(s[base + j]);
+            const float sh = (sv - mu) * rs;
+            const float g = to_f32(gamma[j]) * d;
+            float ds = rs * __builtin_fmaf(-sh, b, g - a);
+            if (ds_extra != nullptr) ds += to_f32(ds_extra[base + j]);
+            const float o2 = keep_bit_of(mrow, j) ? ds * keep_scale : 0.f;
+            // written after every read of this element: dres may replace dy or ds_extra
+            dres[base + j] = from_f32<T>(ds);
+            dx[base + j] = from_f32<T>(o2);
+            if constexpr (std::is_same_v<A, double>) {
+                const double shd = (static_cast<double>(sv) - static_cast<double>(mu)) * static_cast<double>(rs);
+                pg[j] = __builtin_fma(static_cast<double>(d), shd, pg[j]);
+            } else {
+                pg[j] += static_cast<A>(d * sh);
+            }
+            pb[j] += static_cast<A>(d);
+            px[j] += static_cast<A>(o2);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Hidden-size buckets.
 // ------------------------------------------------------------------------------------------
 struct LnPlan {
@@ -1152,11 +1265,13 @@ static size_t bdr_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype) {
     if (!valid_dtype(dtype) || N < 0 || C < 1 || C > LNR_LAYERNORM_MAX_C) return 0;
     int64_t pv, pg, rv, rg;
     bw_partials(N, C, dtype, pv, pg, rv, rg, true);
-    return static_cast<size_t>(pv) * 3 * static_cast<size_t>(C) * accum_size(dtype);
+    const int64_t P = pv > pg ? pv : pg;
+    return static_cast<size_t>(P) * 3 * static_cast<size_t>(C) * accum_size(dtype);
 }
 
-// The fused op runs on the vector path only: every [N, C] and [C] buffer 16-byte aligned and
-// C * element size a multiple of 16 (C a multiple of 8 for fp16, of 4 for fp32).
+// The fused op's vector path: every [N, C] and [C] buffer 16-byte aligned and C * element
+// size a multiple of 16 (C a multiple of 8 for fp16, of 4 for fp32). Anything else takes the
+// element-wise kernels.
 static bool bdr_vec_ok(int64_t C, size_t es, std::initializer_list<const void *> bufs) {
     if ((static_cast<size_t>(C) * es) % 16 != 0) return false;
     for (const void *b : bufs)
@@ -1178,10 +1293,9 @@ static int bdr_fw(void *s_out, void *y, float *mean, float *rstd, const void *x,
         bias == nullptr || mask == nullptr || gamma == nullptr || beta == nullptr)
         return LNR_ERR_NULL;
     const size_t es = dtype_size(dtype);
-    if ((static_cast<size_t>(C) * es) % 16 != 0) return LNR_ERR_UNSUPPORTED;
-    if (!bdr_vec_ok(C, es, {s_out, y, x, residual, bias, gamma, beta}) || !aligned_to(mean, 4) ||
-        !aligned_to(rstd, 4))
-        return LNR_ERR_ALIGN;
+    for (const void *b : std::initializer_list<const void *>{s_out, y, x, residual, bias, gamma, beta})
+        if (!aligned_to(b, es)) return LNR_ERR_ALIGN;
+    if (!aligned_to(mean, 4) || !aligned_to(rstd, 4)) return LNR_ERR_ALIGN;
     const size_t nb = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
     const size_t cb = static_cast<size_t>(C) * es;
     const size_t mbytes = static_cast<size_t>(N) * static_cast<size_t>((C + 7) / 8);
@@ -1203,8 +1317,23 @@ static int bdr_fw(void *s_out, void *y, float *mean, float *rstd, const void *x,
     a.mask = mask;
     a.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p)));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = dtype == LNR_F16 ? dispatch_ln_fw<f16, kBdrLayerNorm, 0>(a, st)
-                                          : dispatch_ln_fw<float, kBdrLayerNorm, 0>(a, st);
+    hipError_t e;
+    if (bdr_vec_ok(C, es, {s_out, y, x, residual, bias, gamma, beta})) {
+        e = dtype == LNR_F16 ? dispatch_ln_fw<f16, kBdrLayerNorm, 0>(a, st)
+                             : dispatch_ln_fw<float, kBdrLayerNorm, 0>(a, st);
+    } else if (dtype == LNR_F16) {
+        e = launch(bdr_layernorm_fw_generic<f16>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), st,
+                   static_cast<f16 *>(s_out), static_cast<f16 *>(y), mean, rstd,
+                   static_cast<const f16 *>(x), static_cast<const f16 *>(residual),
+                   static_cast<const f16 *>(bias), mask, a.keep_scale, static_cast<const f16 *>(gamma),
+                   static_cast<const f16 *>(beta), N, a.C, eps);
+    } else {
+        e = launch(bdr_layernorm_fw_generic<float>, dim3(static_cast<uint32_t>(N)), dim3(kLnGenericWG), st,
+                   static_cast<float *>(s_out), static_cast<float *>(y), mean, rstd,
+                   static_cast<const float *>(x), static_cast<const float *>(residual),
+                   static_cast<const float *>(bias), mask, a.keep_scale,
+                   static_cast<const float *>(gamma), static_cast<const float *>(beta), N, a.C, eps);
+    }
     return status_of(e);
 }
 
@@ -1221,11 +1350,9 @@ static int bdr_bw(void *dres, void *dx, void *dgamma, void *dbeta, void *dbias, 
                   mask == nullptr || gamma == nullptr || mean == nullptr || rstd == nullptr))
         return LNR_ERR_NULL;
     const size_t es = dtype_size(dtype);
-    if ((static_cast<size_t>(C) * es) % 16 != 0) return LNR_ERR_UNSUPPORTED;
-    if (!bdr_vec_ok(C, es, {dres, dx, dy, ds_extra, s_in, gamma}) || !aligned_to(dgamma, es) ||
-        !aligned_to(dbeta, es) || !aligned_to(dbias, es) || !aligned_to(mean, 4) ||
-        !aligned_to(rstd, 4))
-        return LNR_ERR_ALIGN;
+    for (const void *b : std::initializer_list<const void *>{dres, dx, dy, ds_extra, s_in, gamma, dgamma, dbeta, dbias})
+        if (!aligned_to(b, es)) return LNR_ERR_ALIGN;
+    if (!aligned_to(mean, 4) || !aligned_to(rstd, 4)) return LNR_ERR_ALIGN;
     const size_t need = bdr_workspace_bytes(N, C, dtype);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LNR_ERR_WORKSPACE;
     if (need > 0 && !aligned_to(workspace, 8)) return LNR_ERR_ALIGN;
@@ -1266,14 +1393,34 @@ static int bdr_bw(void *dres, void *dx, void *dgamma, void *dbeta, void *dbias, 
     }
     int64_t pv, pg, rv, rg;
     bw_partials(N, C, dtype, pv, pg, rv, rg, true);
-    LnBwArgs a{dres, dgamma, dbeta, workspace, dy, s_in, gamma, mean, rstd, N, C32, rv, pv};
-    a.dx2 = dx;
-    a.dbias = dbias;
-    a.ds_extra = ds_extra;
-    a.mask = mask;
-    a.keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p)));
-    const hipError_t e = dtype == LNR_F16 ? dispatch_ln_bw<f16, kBdrLayerNorm, 0>(a, st)
-                                          : dispatch_ln_bw<float, kBdrLayerNorm, 0>(a, st);
+    const float keep_scale = static_cast<float>(1.0 / (1.0 - static_cast<double>(p)));
+    hipError_t e;
+    if (bdr_vec_ok(C, es, {dres, dx, dy, ds_extra, s_in, gamma})) {
+        LnBwArgs a{dres, dgamma, dbeta, workspace, dy, s_in, gamma, mean, rstd, N, C32, rv, pv};
+        a.dx2 = dx;
+        a.dbias = dbias;
+        a.ds_extra = ds_extra;
+        a.mask = mask;
+        a.keep_scale = keep_scale;
+        e = dtype == LNR_F16 ? dispatch_ln_bw<f16, kBdrLayerNorm, 0>(a, st)
+                             : dispatch_ln_bw<float, kBdrLayerNorm, 0>(a, st);
+    } else {
+        if (dtype == LNR_F16)
+            e = launch(bdr_layernorm_bw_generic<f16>, dim3(static_cast<uint32_t>(pg)), dim3(kLnGenericWG), st,
+                       static_cast<f16 *>(dres), static_cast<f16 *>(dx), static_cast<float *>(workspace),
+                       static_cast<const f16 *>(dy), static_cast<const f16 *>(ds_extra),
+                       static_cast<const f16 *>(s_in), mask, keep_scale, static_cast<const f16 *>(gamma),
+                       mean, rstd, N, C32, rg);
+        else
+            e = launch(bdr_layernorm_bw_generic<float>, dim3(static_cast<uint32_t>(pg)), dim3(kLnGenericWG), st,
+                       static_cast<float *>(dres), static_cast<float *>(dx), static_cast<double *>(workspace),
+                       static_cast<const float *>(dy), static_cast<const float *>(ds_extra),
+                       static_cast<const float *>(s_in), mask, keep_scale,
+                       static_cast<const float *>(gamma), mean, rstd, N, C32, rg);
+        if (e == hipSuccess)
+            e = dtype == LNR_F16 ? launch_colsum<f16>(dgamma, dbeta, dbias, workspace, pg, C32, 3, 3, st)
+                                 : launch_colsum<float>(dgamma, dbeta, dbias, workspace, pg, C32, 3, 3, st);
+    }
     return status_of(e);
 }
 

@@ -274,11 +274,12 @@ def test_bdr_layernorm_fw_validation(lib):
     assert bfw(lib, C=0) == SHAPE
     assert bfw(lib, p=1.0) == SHAPE
     assert bfw(lib, p=-0.1) == SHAPE
-    assert bfw(lib, C=100) == UNSUP                          # fp16 rows must be whole vectors
+    assert bfw(lib, C=100, x=A + 2 ** 30 + 1) == ALIGN       # odd widths take the element-wise
+                                                             # kernel; element alignment is still required
     assert bfw(lib, C=9000) == UNSUP
     assert bfw(lib, m=None) == NULL
     assert bfw(lib, mean=None) == NULL                       # mean and rstd: both or neither
-    assert bfw(lib, x=A + 2 ** 30 + 2) == ALIGN              # vector path needs 16 bytes
+    assert bfw(lib, x=A + 2 ** 30 + 1) == ALIGN              # not aligned to its element size
     assert bfw(lib, s=A + 2 ** 31 + 64) == ALIAS             # s partially over residual
     assert bfw(lib, y=A + 64) == ALIAS                       # y over s
     assert bfw(lib, N=0) == OK
@@ -297,10 +298,10 @@ def bbw(lib, dr=A, dx=A + 2 ** 28, dg=A + 2 ** 29, db=A + 2 ** 29 + 2 ** 16,
 def test_bdr_layernorm_bw_validation(lib):
     assert bbw(lib, dtype=9) == DTYPE
     assert bbw(lib, p=1.5) == SHAPE
-    assert bbw(lib, C=36) == UNSUP
+    assert bbw(lib, C=36, dy=A + 2 ** 30 + 1) == ALIGN
     assert bbw(lib, dbias=None) == NULL
     assert bbw(lib, m=None) == NULL
-    assert bbw(lib, s=A + 2 ** 31 + 8) == ALIGN
+    assert bbw(lib, s=A + 2 ** 31 + 1) == ALIGN
     need = lib.bdr_layernorm_bw_workspace_bytes(64, 64, F16)
     assert need > 0                                          # vector path only: 3 slots per partial row
     assert bbw(lib, ws_bytes=need - 1) == WS

@@ -36,7 +36,17 @@ def gmax_of(dy64, g64):
     return np.max(np.abs(dy64 * g64.reshape(1, -1)), axis=1)
 
 
-def run_bdr(case, extra=True, chain=True, edge=False):
+def on_device(t, shift=False):
+    """t on the GPU; with shift, at an address one element past a 16-byte boundary (the
+    element-wise kernels)."""
+    if not shift:
+        return t.to(DEV)
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+    buf[1:].copy_(t.reshape(-1).to(DEV))
+    return buf[1:].view(t.shape)
+
+
+def run_bdr(case, extra=True, chain=True, edge=False, shift=False):
     dt = case.dtype
     atol, rtol = TOL[dt]
     m = case.mask.numpy()
@@ -46,9 +56,10 @@ def run_bdr(case, extra=True, chain=True, edge=False):
     s_ref, y_ref, mean_ref, rstd_ref = oracle.bdr_ln_fw(x64, r64, b64, m, case.p, g64, be64, case.eps)
 
     say(case.name, "GPU forward")
-    xd, rd, bd = case.x.to(DEV), case.residual.to(DEV), case.bias.to(DEV)
-    gd, bed, md = case.gamma.to(DEV), case.beta.to(DEV), case.mask.to(DEV)
-    s, y, mean, rstd = lnr.bdr_layernorm_fw(xd, rd, bd, md, case.p, gd, bed, case.eps)
+    xd, rd, bd = (on_device(t, shift) for t in (case.x, case.residual, case.bias))
+    gd, bed, md = on_device(case.gamma, shift), on_device(case.beta, shift), case.mask.to(DEV)
+    s, y, mean, rstd = lnr.bdr_layernorm_fw(xd, rd, bd, md, case.p, gd, bed, case.eps,
+                                            s=on_device(case.x, shift), y=on_device(case.x, shift))
     torch.cuda.synchronize()
     assert_close(s, s_ref, dt, f"{case.name} s")
     assert_close(y, y_ref, dt, f"{case.name} y")
@@ -65,9 +76,10 @@ def run_bdr(case, extra=True, chain=True, edge=False):
     de64 = case.ds_extra.double().numpy() if extra else None
     refs = oracle.bdr_ln_bw(s_in64, dy64, de64, m, case.p, g64, mu32.numpy(), rs32.numpy())
     say(case.name, "GPU backward")
-    dyd = case.dy.to(DEV)
-    ded = case.ds_extra.to(DEV) if extra else None
-    got = lnr.bdr_layernorm_bw(dyd, s_in.to(DEV), md, case.p, gd, mu32.to(DEV), rs32.to(DEV), ded)
+    dyd = on_device(case.dy, shift)
+    ded = on_device(case.ds_extra, shift) if extra else None
+    got = lnr.bdr_layernorm_bw(dyd, on_device(s_in, shift), md, case.p, gd, mu32.to(DEV), rs32.to(DEV), ded,
+                               dresidual=on_device(case.dy, shift), dx=on_device(case.dy, shift))
     torch.cuda.synchronize()
     inv_keep = 1.0 / (1.0 - case.p)
     r32 = rs32.double().numpy()
@@ -158,23 +170,47 @@ def test_in_place_and_determinism(dtype):
         assert torch.equal(u, v) and torch.equal(u, w)
 
 
-def test_unsupported_shapes_and_alignment_are_rejected():
-    N, C = 16, 100  # fp16: 100 is not a multiple of 8
-    z = torch.zeros(N, C, dtype=torch.float16, device=DEV)
-    c = torch.zeros(C, dtype=torch.float16, device=DEV)
-    mk = torch.zeros(N, (C + 7) // 8, dtype=torch.uint8, device=DEV)
-    with pytest.raises(lnr.LnrError) as e:
-        lnr.bdr_layernorm_fw(z, z, c, mk, 0.1, c, c)
-    assert e.value.status == 3
-    C = 64
-    buf = torch.zeros(N * C + 8, dtype=torch.float16, device=DEV)
-    xs = buf[1:1 + N * C].view(N, C)               # 2-byte aligned, not 16
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+@pytest.mark.parametrize("C", [1, 7, 100, 1000])
+def test_element_wise_fallback(C, dtype):
+    """Widths whose rows are not whole 16-byte vectors, and buffers one element past a 16-byte
+    boundary, take the element-wise kernels: parity with the oracle, forward and backward,
+    with and without the second gradient of s."""
+    for N in (7, 1031):
+        for shift in (False, True):
+            case = W.bdr_case(f"bdr-generic-{N}x{C}-{dtype}-{'unaligned' if shift else 'aligned'}", N, C,
+                              dtype=dtype, seed_base=9900 + C)
+            run_bdr(case, extra=(N == 1031), chain=(N == 1031), edge=True, shift=shift)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+def test_element_wise_fallback_in_place(dtype):
+    """s over residual and dresidual over dy on the element-wise kernels (C = 100): bitwise
+    equal to the out-of-place results."""
+    case = W.bdr_case("bdr-generic-inplace", 513, 100, dtype=dtype, seed_base=9950)
+    xd, rd, bd = case.x.to(DEV), case.residual.to(DEV), case.bias.to(DEV)
+    gd, bed, md = case.gamma.to(DEV), case.beta.to(DEV), case.mask.to(DEV)
+    say(case.name, dtype)
+    s1, y1, m1, r1 = lnr.bdr_layernorm_fw(xd, rd, bd, md, case.p, gd, bed)
+    ri = rd.clone()
+    si, yi, mi, rri = lnr.bdr_layernorm_fw(xd, ri, bd, md, case.p, gd, bed, s=ri)
+    dyd, ded = case.dy.to(DEV), case.ds_extra.to(DEV)
+    a = lnr.bdr_layernorm_bw(dyd, s1, md, case.p, gd, m1, r1, ded)
+    dyi = dyd.clone()
+    c = lnr.bdr_layernorm_bw(dyi, s1, md, case.p, gd, m1, r1, ded, dresidual=dyi)
+    dei = ded.clone()
+    d = lnr.bdr_layernorm_bw(dyd, s1, md, case.p, gd, m1, r1, dei, dresidual=dei)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, ri) and torch.equal(y1, yi) and torch.equal(m1, mi) and torch.equal(r1, rri)
+    for u, v, w in zip(a, c, d):
+        assert torch.equal(u, v) and torch.equal(u, w)
+
+
+def test_invalid_p_is_rejected():
+    N, C = 16, 64
     z = torch.zeros(N, C, dtype=torch.float16, device=DEV)
     c = torch.zeros(C, dtype=torch.float16, device=DEV)
     mk = torch.zeros(N, C // 8, dtype=torch.uint8, device=DEV)
-    with pytest.raises(lnr.LnrError) as e:
-        lnr.bdr_layernorm_fw(xs, z, c, mk, 0.1, c, c)
-    assert e.value.status == 5
     with pytest.raises(lnr.LnrError) as e:
         lnr.bdr_layernorm_fw(z, z.clone(), c, mk, 1.0, c, c)   # p must be < 1
     assert e.value.status == 2
