@@ -175,12 +175,14 @@ def test_in_place_and_determinism(dtype):
 def test_element_wise_fallback(C, dtype):
     """Widths whose rows are not whole 16-byte vectors, and buffers one element past a 16-byte
     boundary, take the element-wise kernels: parity with the oracle, forward and backward,
-    with and without the second gradient of s."""
+    with and without the second gradient of s. No chained comparison at C = 1: a one-element
+    row has variance 0, so rstd = 1/sqrt(eps) = 1e4 multiplies the storage rounding of s,
+    which the chained reference pairs with the exact statistics, by 1e4."""
     for N in (7, 1031):
         for shift in (False, True):
             case = W.bdr_case(f"bdr-generic-{N}x{C}-{dtype}-{'unaligned' if shift else 'aligned'}", N, C,
                               dtype=dtype, seed_base=9900 + C)
-            run_bdr(case, extra=(N == 1031), chain=(N == 1031), edge=True, shift=shift)
+            run_bdr(case, extra=(N == 1031), chain=(N == 1031 and C > 1), edge=True, shift=shift)
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
