@@ -61,7 +61,8 @@ typedef enum {
     LNR_ERR_ALIGN = 5,       /* a pointer is not aligned to its element size */
     LNR_ERR_ALIAS = 6,       /* buffers overlap in a way the operation forbids */
     LNR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than layernorm_bw_workspace_bytes() */
-    LNR_ERR_HIP = 8          /* the HIP runtime rejected a launch */
+    LNR_ERR_HIP = 8,         /* the HIP runtime rejected a launch */
+    LNR_ERR_SCRATCH = 9      /* the shape needs more than the library's fixed scratch array */
 } lnr_status;
 
 #define LNR_SOFTMAX_MAX_TK 2048  /* longest row in the HW4 page's row-length template list */
@@ -156,6 +157,28 @@ LNR_API int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, co
                  const void *gamma, const float *mean, const float *rstd, int64_t N,
                  int64_t C, lnr_dtype dtype, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/*
+ * layernorm_bw_noalloc -- layernorm_bw for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ *   Same arguments, results, aliasing rules and errors as layernorm_bw, without the workspace:
+ *   the column partials go to a device array that the library owns,
+ *   LNR_NOALLOC_SCRATCH_BYTES bytes per GPU, held by every GPU the library runs on until the
+ *   process ends. The call allocates nothing. Shapes whose layernorm_bw_workspace_bytes()
+ *   exceeds LNR_NOALLOC_SCRATCH_BYTES return LNR_ERR_SCRATCH and enqueue nothing (at 256 or
+ *   more rows: C <= 8192 for fp16, C <= 4096 for fp32).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap in time on one GPU
+ *   (from two streams or two threads) race on it and give wrong results; calls on one stream
+ *   are ordered and safe. The array keeps the last call's partials; nothing in it needs to be
+ *   cleared between calls. The first call on a device looks the array's address up on that
+ *   device (the device of `stream`); that call may not be under graph capture.
+ */
+#define LNR_NOALLOC_SCRATCH_BYTES (16u << 20)
+LNR_API int layernorm_bw_noalloc(void *dx, void *dgamma, void *dbeta, const void *dy,
+                                 const void *x, const void *gamma, const float *mean,
+                                 const float *rstd, int64_t N, int64_t C, lnr_dtype dtype,
+                                 void *stream);
 
 /*
  * rmsnorm_fw -- RMSNorm forward: per row, one reduction of the sum of squares, then

@@ -13,6 +13,8 @@ Functions mirror the C entry points:
     layernorm_bw(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None,
                  workspace=None) -> (dx, dgamma, dbeta)
     layernorm_bw_workspace_bytes(N, C, dtype) -> int
+    layernorm_bw_noalloc(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None)
+                 -> (dx, dgamma, dbeta)   (the library's own scratch array, no workspace)
     rmsnorm_fw(x, gamma, eps=1e-6, y=None, rstd=None) -> (y, rstd)
     rmsnorm_bw(dy, x, gamma, rstd, dx=None, dgamma=None, workspace=None) -> (dx, dgamma)
     rmsnorm_bw_workspace_bytes(N, C, dtype) -> int
@@ -34,7 +36,7 @@ import os
 
 __all__ = [
     "LnrError", "load", "library_path", "attn_softmax_fw", "attn_softmax_bw", "layernorm_fw",
-    "layernorm_bw", "layernorm_bw_workspace_bytes", "rmsnorm_fw", "rmsnorm_bw",
+    "layernorm_bw", "layernorm_bw_workspace_bytes", "layernorm_bw_noalloc", "rmsnorm_fw", "rmsnorm_bw",
     "rmsnorm_bw_workspace_bytes", "cross_entropy_fw", "cross_entropy_bw",
     "cross_entropy_fw_workspace_bytes", "bdr_layernorm_fw", "bdr_layernorm_bw",
     "bdr_layernorm_bw_workspace_bytes", "copy_bytes", "xor_bytes", "softmax_plan",
@@ -51,7 +53,7 @@ LAYERNORM_MAX_C = 8192
 STATUS_NAMES = {
     0: "LNR_OK", 1: "LNR_ERR_NULL", 2: "LNR_ERR_SHAPE", 3: "LNR_ERR_UNSUPPORTED",
     4: "LNR_ERR_DTYPE", 5: "LNR_ERR_ALIGN", 6: "LNR_ERR_ALIAS", 7: "LNR_ERR_WORKSPACE",
-    8: "LNR_ERR_HIP",
+    8: "LNR_ERR_HIP", 9: "LNR_ERR_SCRATCH",
 }
 
 
@@ -87,6 +89,7 @@ def load():
     lib.layernorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
     lib.layernorm_bw_workspace_bytes.restype = sz
     lib.layernorm_bw.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
+    lib.layernorm_bw_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, vp]
     lib.rmsnorm_fw.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, ci, vp]
     lib.rmsnorm_bw_workspace_bytes.argtypes = [i64, i64, ci]
     lib.rmsnorm_bw_workspace_bytes.restype = sz
@@ -111,7 +114,8 @@ def load():
     ip = ctypes.POINTER(ctypes.c_int)
     lib.lnr_softmax_plan.argtypes = [i64, ci, ci, ip, ip, ip]
     lib.lnr_layernorm_plan.argtypes = [i64, i64, ci, ci, ip, ip, ip, ip, ctypes.POINTER(i64)]
-    for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw", "rmsnorm_fw",
+    for f in ("attn_softmax_fw", "attn_softmax_bw", "layernorm_fw", "layernorm_bw",
+              "layernorm_bw_noalloc", "rmsnorm_fw",
               "rmsnorm_bw", "cross_entropy_fw", "cross_entropy_bw", "bdr_layernorm_fw",
               "bdr_layernorm_bw", "lnr_copy",
               "lnr_xor2", "lnr_softmax_plan", "lnr_layernorm_plan"):
@@ -353,6 +357,36 @@ def layernorm_bw(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None, wor
                              _ptr(mean), _ptr(rstd), N, C, code, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(x))
     _check(st, "layernorm_bw")
+    return dx, dgamma, dbeta
+
+
+def layernorm_bw_noalloc(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None):
+    """layernorm_bw with the column partials in the library's own device array instead of a
+    workspace (for callers that cannot allocate: pass dx, dgamma and dbeta, and this function
+    allocates nothing either). Calls that overlap in time on one GPU race on that array.
+    Returns (dx, dgamma, dbeta)."""
+    torch = _torch()
+    _dev(x, "x")
+    _dev(dy, "dy", like=x)
+    if x.dim() != 2 or dy.shape != x.shape:
+        raise ValueError("x and dy must both be [N, C]")
+    N, C = x.shape
+    _dev(gamma, "gamma", like=x)
+    if gamma.numel() != C:
+        raise ValueError("gamma must have C elements")
+    _f32(mean, "mean", x)
+    _f32(rstd, "rstd", x)
+    if mean.numel() != N or rstd.numel() != N:
+        raise ValueError("mean and rstd must have N elements")
+    dx = torch.empty_like(x) if dx is None else dx
+    dgamma = torch.empty(C, dtype=x.dtype, device=x.device) if dgamma is None else dgamma
+    dbeta = torch.empty(C, dtype=x.dtype, device=x.device) if dbeta is None else dbeta
+    for t, nm in ((dx, "dx"), (dgamma, "dgamma"), (dbeta, "dbeta")):
+        _dev(t, nm, like=x)
+    st = load().layernorm_bw_noalloc(_ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(dy), _ptr(x),
+                                     _ptr(gamma), _ptr(mean), _ptr(rstd), N, C, _dtype_code(x),
+                                     _stream(x))
+    _check(st, "layernorm_bw_noalloc")
     return dx, dgamma, dbeta
 
 

@@ -102,6 +102,7 @@ extern "C" const char *lnr_strerror(int status) {
         case LNR_ERR_ALIAS: return "buffers overlap in a way the operation forbids";
         case LNR_ERR_WORKSPACE: return "workspace missing or smaller than layernorm_bw_workspace_bytes()";
         case LNR_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+        case LNR_ERR_SCRATCH: return "the shape needs more than the library's fixed scratch array (LNR_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

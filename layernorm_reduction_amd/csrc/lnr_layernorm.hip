@@ -27,7 +27,9 @@
 //     reduction (sum of x^2 forward, sum of gamma*dy*xhat backward), no beta and no dbeta.
 #include <math.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 
 #include "lnr_common.h"
@@ -1181,11 +1183,14 @@ static int norm_fw(void *y, float *mean, float *rstd, const void *x, const void 
     return status_of(e);
 }
 
-// Backward of either norm. RMSNorm (rms): dbeta and mean are NULL.
+// Backward of either norm. RMSNorm (rms): dbeta and mean are NULL. With check_only, every
+// check that does not involve the workspace runs and nothing is launched (the no-allocation
+// entry point validates its arguments this way before it touches a device).
 template <bool RMS>
 static int norm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const void *x,
                    const void *gamma, const float *mean, const float *rstd, int64_t N, int64_t C,
-                   lnr_dtype dtype, void *workspace, size_t workspace_bytes, void *stream) {
+                   lnr_dtype dtype, void *workspace, size_t workspace_bytes, void *stream,
+                   bool check_only = false) {
     if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
     if (N < 0 || C < 1) return LNR_ERR_SHAPE;
     if (C > LNR_LAYERNORM_MAX_C) return LNR_ERR_UNSUPPORTED;
@@ -1199,7 +1204,7 @@ static int norm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const vo
         !aligned_to(dy, es) || !aligned_to(x, es) || !aligned_to(gamma, es) ||
         !aligned_to(mean, 4) || !aligned_to(rstd, 4))
         return LNR_ERR_ALIGN;
-    const size_t need = bw_workspace_bytes(N, C, dtype);
+    const size_t need = check_only ? 0 : bw_workspace_bytes(N, C, dtype);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LNR_ERR_WORKSPACE;
     if (need > 0 && !aligned_to(workspace, 8)) return LNR_ERR_ALIGN;
     const size_t nbytes = static_cast<size_t>(N) * static_cast<size_t>(C) * es;
@@ -1216,6 +1221,7 @@ static int norm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const vo
         if (overlap(out, cbytes, x, nbytes) || overlap(out, cbytes, dy, nbytes) ||
             overlap(out, cbytes, dx, nbytes) || overlap(out, cbytes, gamma, cbytes))
             return LNR_ERR_ALIAS;
+    if (check_only) return LNR_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int slots = RMS ? 1 : 2;
@@ -1424,9 +1430,77 @@ static int bdr_bw(void *dres, void *dx, void *dgamma, void *dbeta, void *dbias, 
     return status_of(e);
 }
 
+// ------------------------------------------------------------------------------------------
+// layernorm_bw without a caller workspace, for callers that cannot allocate. The column
+// partials go to `scratch`, a file-scope device array: every GPU the library runs on holds its
+// own copy until the process ends. Its address on a device is looked up once, with that device
+// current, and kept per device; host code never passes the array's name itself to a kernel
+// (on the host it names a stand-in, not device memory). Nothing in it needs clearing: the
+// backward's row kernel writes every partial row the column sum reads.
+// ------------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = LNR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void *> g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The device `stream` runs on (the current device for the default stream).
+static hipError_t stream_device(hipStream_t stream, int &dev) {
+    if (stream == nullptr) return hipGetDevice(&dev);
+    hipDevice_t d = 0;
+    const hipError_t e = hipStreamGetDevice(stream, &d);
+    dev = static_cast<int>(d);
+    return e;
+}
+
+// Address of `scratch` on device `dev`, looked up on the first call for that device.
+static int scratch_on(int dev, void **out) {
+    if (dev < 0 || dev >= kMaxDevices) return LNR_ERR_UNSUPPORTED;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            int prev = 0;
+            if (hipGetDevice(&prev) != hipSuccess) return LNR_ERR_HIP;
+            if (prev != dev && hipSetDevice(dev) != hipSuccess) return LNR_ERR_HIP;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (prev != dev && hipSetDevice(prev) != hipSuccess) return LNR_ERR_HIP;
+            if (e != hipSuccess || p == nullptr) return LNR_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return LNR_OK;
+}
+
+static int layernorm_bw_scratch(void *dx, void *dgamma, void *dbeta, const void *dy, const void *x,
+                                const void *gamma, const float *mean, const float *rstd, int64_t N,
+                                int64_t C, lnr_dtype dtype, void *stream) {
+    int st = norm_bw<false>(dx, dgamma, dbeta, dy, x, gamma, mean, rstd, N, C, dtype, nullptr, 0,
+                            stream, true);
+    if (st != LNR_OK) return st;
+    if (bw_workspace_bytes(N, C, dtype) > kScratchBytes) return LNR_ERR_SCRATCH;
+    int dev = 0;
+    if (stream_device(static_cast<hipStream_t>(stream), dev) != hipSuccess) return LNR_ERR_HIP;
+    void *ws = nullptr;
+    st = scratch_on(dev, &ws);
+    if (st != LNR_OK) return st;
+    return norm_bw<false>(dx, dgamma, dbeta, dy, x, gamma, mean, rstd, N, C, dtype, ws, kScratchBytes,
+                          stream);
+}
+
 }  // namespace lnr
 
 using namespace lnr;
+
+extern "C" int layernorm_bw_noalloc(void *dx, void *dgamma, void *dbeta, const void *dy,
+                                    const void *x, const void *gamma, const float *mean,
+                                    const float *rstd, int64_t N, int64_t C, lnr_dtype dtype,
+                                    void *stream) {
+    return layernorm_bw_scratch(dx, dgamma, dbeta, dy, x, gamma, mean, rstd, N, C, dtype, stream);
+}
 
 extern "C" int bdr_layernorm_fw(void *s, void *y, float *mean, float *rstd, const void *x,
                                 const void *residual, const void *bias, const uint8_t *keep_mask,

@@ -19,6 +19,7 @@ HEADER = os.path.join(ROOT, "include", "lnr.h")
 GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_constants.json")))
 
 OK, NULL, SHAPE, UNSUP, DTYPE, ALIGN, ALIAS, WS = 0, 1, 2, 3, 4, 5, 6, 7
+SCRATCH = 9
 F32, F16 = lnr.LNR_F32, lnr.LNR_F16
 A = 0x7F0000000000  # a fake, 256-byte aligned device address; never dereferenced
 
@@ -40,7 +41,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -174,6 +175,30 @@ def test_layernorm_bw_validation(lib):
     assert lbw(lib, ws=A + 2 ** 32) == ALIAS                 # workspace over gamma
     assert lbw(lib, ws=A + 2 ** 32 + 2 ** 20) == ALIAS       # workspace over mean
     assert lbw(lib, ws=A + 2 ** 32 + 2 ** 21) == ALIAS       # workspace over rstd
+
+
+def lbw0(lib, dx=A, dg=A + 2 ** 33, db=A + 2 ** 33 + 2 ** 20, dy=A + 2 ** 30, x=A + 2 ** 31,
+         g=A + 2 ** 32, mean=A + 2 ** 32 + 2 ** 20, rstd=A + 2 ** 32 + 2 ** 21, N=64, C=64, dtype=F16):
+    return lib.layernorm_bw_noalloc(dx, dg, db, dy, x, g, mean, rstd, N, C, dtype, None)
+
+
+def test_layernorm_bw_noalloc_validation(lib):
+    # every argument error is reported before any device is touched (no GPU here)
+    assert lbw0(lib, dtype=9) == DTYPE
+    assert lbw0(lib, C=0) == SHAPE
+    assert lbw0(lib, N=-1) == SHAPE
+    assert lbw0(lib, C=10000) == UNSUP
+    assert lbw0(lib, dg=None) == NULL
+    assert lbw0(lib, mean=None) == NULL
+    assert lbw0(lib, x=A + 2 ** 31 + 1) == ALIGN
+    assert lbw0(lib, dx=A + 2 ** 31) == ALIAS                # dx over x
+    assert lbw0(lib, db=A + 2 ** 33 + 2) == ALIAS            # dbeta over dgamma
+    # beyond the fixed scratch array: fp32 partials of 8192 columns over 256 workgroups
+    assert lib.layernorm_bw_workspace_bytes(4096, 8192, F32) > (16 << 20)
+    assert lbw0(lib, N=4096, C=8192, dtype=F32) == SCRATCH
+    assert lib.layernorm_bw_workspace_bytes(32768, 8192, F16) <= (16 << 20)
+    assert lib.layernorm_bw_workspace_bytes(32768, 4096, F32) <= (16 << 20)
+    assert lib.lnr_strerror(SCRATCH) != lib.lnr_strerror(99)
 
 
 def rfw(lib, y=A, rstd=A + 2 ** 32, x=A + 2 ** 30, g=A + 2 ** 31, N=64, C=64, eps=1e-6, dtype=F16):
