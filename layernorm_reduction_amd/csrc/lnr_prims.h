@@ -74,6 +74,40 @@ __device__ __forceinline__ void store_stream(T *p, const float (&in)[Vec16<T>::N
     __builtin_nontemporal_store(v, reinterpret_cast<RawVec<T> *>(p));
 }
 
+// Branch-free stores. A row kernel whose stores sit behind a branch (a row past the end, a
+// vector slot past the row) pays for it at every later wait: after the join, the compiler's
+// wait counts must assume that the stores were skipped, so a wait for data loaded before them
+// also waits for everything issued since. Stores through a buffer descriptor need no branch: a
+// lane with nothing to store passes an offset beyond the descriptor's range and the hardware
+// drops its store. `wave_base` must be the same for every lane of the wave; offsets are bytes.
+constexpr uint32_t kDropOffset = 0xFFFFFFF0u;
+constexpr int32_t kBufferRange = 0x7FFFFFFF;    // valid offsets stay below it
+constexpr int32_t kBufferDword3 = 0x00020000;   // untyped 32-bit data (gfx9 family)
+constexpr int kBufferNonTemporal = 2;           // cache policy bits of a streaming store
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *wave_base, int32_t range = kBufferRange) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(wave_base), 0, range, kBufferDword3);
+}
+template <typename RV>
+__device__ __forceinline__ void store16_or_drop(const void *wave_base, uint32_t off, const RV &v) {
+    static_assert(sizeof(RV) == 16, "16-byte vectors");
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), wave_rsrc(wave_base), off, 0,
+                                           kBufferNonTemporal);
+}
+// A float through a descriptor of `range` bytes (0: every store dropped), cached.
+__device__ __forceinline__ void store4_or_drop(const void *wave_base, int32_t range, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), wave_rsrc(wave_base, range), off, 0, 0);
+}
+// Round fp32 values to T (nearest even) as one 16-byte vector.
+template <typename T>
+__device__ __forceinline__ RawVec<T> pack16(const float (&in)[Vec16<T>::N]) {
+    RawVec<T> v;
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::N; ++e) v[e] = static_cast<T>(in[e]);
+    return v;
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
 template <typename T> __device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
 
