@@ -439,11 +439,11 @@ def table_cases():
         for C in (1024, 4096):
             cases.append((f"rmsnorm [32768,{C}] {tag}", "rmsnorm", (32768, C), dt, {}))
     # Softmax cross-entropy over a vocabulary: the GPT-2 batch of tokens, two vocabularies,
-    # and a 64-row decoding batch whose rows are split over workgroups.
+    # and a 64-row decoding batch (its backward splits rows over workgroups).
     for V in W.XENT_VOCABS:
         cases.append((f"xent [8192,{V}] fp16", "xent", (8192, V), torch.float16, {}))
     cases.append(("xent [8192,32000] fp32", "xent", (8192, 32000), torch.float32, {}))
-    cases.append(("xent [64,32000] fp16 (split rows)", "xent", (64, 32000), torch.float16, {}))
+    cases.append(("xent [64,32000] fp16 (decoding batch)", "xent", (64, 32000), torch.float16, {}))
     # Bias + dropout + residual feeding LayerNorm: post-LN (s has one consumer) and pre-LN (s
     # is the residual stream, so a second gradient reaches it) at the model shape, then wider.
     for extra in (False, True):

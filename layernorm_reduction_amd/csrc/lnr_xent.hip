@@ -9,9 +9,10 @@
 // [0, V) otherwise gives NaN (a visible result; a kernel cannot raise).
 //
 // Design on CDNA4:
-//   * Rows are long (10^4 - 10^5 logits, 20-400 KB): a workgroup streams one row (or one
-//     chunk of a row when there are too few rows to fill the chip), 16-byte non-temporal
-//     loads, U vectors in flight per thread per iteration.
+//   * Rows are long (10^4 - 10^5 logits, 20-400 KB): a workgroup streams one row, 16-byte
+//     non-temporal loads, U vectors in flight per thread per iteration. With too few rows to
+//     fill the chip, the backward streams chunks of a row in separate workgroups, and so
+//     does the forward for rows above 256 KB.
 //   * Forward, one pass: each thread keeps a running maximum m and a sum s of exp(z - m);
 //     per iteration it takes the maximum of its U*VE new logits and rescales s once, so the
 //     cost is one exp per logit plus one per U*VE. Then the workgroup reduces (m, s): the
@@ -305,6 +306,12 @@ constexpr int kXentBwU = 4;       // whole rows (S == 1)
 constexpr int kXentBwSplitU = 2;  // split rows (S > 1)
 constexpr uint32_t kXentLine = 128;  // bytes: the row split's alignment
 constexpr int64_t kXentTargetBlocks = 1024;  // split rows until about this many workgroups
+// The forward splits rows only above this size: a split row needs a second kernel to combine
+// its chunks, and that launch costs more than one workgroup takes to stream a shorter row.
+// Measured on MI355X: one workgroup per row is faster at [64, 32000] fp16 (5.2 against 8.4 us),
+// [256, 32000] (6.2 / 10.6), [64, 32000] fp32 (6.0 / 11.0) and still at [8, 128256] fp16
+// (256 KB rows: 10.8 / 12.5). The backward has no second kernel and keeps splitting.
+constexpr int64_t kXentFwSplitRowBytes = 256 << 10;
 
 // Chunks per row: 1 when there are enough rows, else enough to reach kXentTargetBlocks
 // workgroups while every chunk keeps at least one vector per thread (min_vectors = WG).
@@ -328,9 +335,14 @@ static bool xent_shape_ok(int64_t N, int64_t V) {
 
 using namespace lnr;
 
+static int32_t xent_fw_chunks(int64_t N, int64_t V, size_t es) {
+    if (V * static_cast<int64_t>(es) <= kXentFwSplitRowBytes) return 1;
+    return xent_chunks(N, V, es, kXentFwWG);
+}
+
 extern "C" size_t cross_entropy_fw_workspace_bytes(int64_t N, int64_t V, lnr_dtype dtype) {
     if (!valid_dtype(dtype) || !xent_shape_ok(N, V)) return 0;
-    const int32_t S = xent_chunks(N, V, dtype_size(dtype), kXentFwWG);
+    const int32_t S = xent_fw_chunks(N, V, dtype_size(dtype));
     return S > 1 ? static_cast<size_t>(N) * static_cast<size_t>(S) * 2 * sizeof(float) : 0;
 }
 
@@ -358,7 +370,7 @@ extern "C" int cross_entropy_fw(float *loss, float *lse, const void *logits, con
         overlap(workspace, need, lse, nb) || overlap(workspace, need, target, N * 8))
         return LNR_ERR_ALIAS;
 
-    const int32_t S = xent_chunks(N, V, es, kXentFwWG);
+    const int32_t S = xent_fw_chunks(N, V, es);
     const int32_t V32 = static_cast<int32_t>(V);
     float *part = static_cast<float *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -263,11 +263,12 @@ def test_cross_entropy_fw_validation(lib):
     assert xfw(lib, z=A + 2 ** 30 + 1) == ALIGN
     assert xfw(lib, lse=A + 64) == ALIAS                     # lse over loss
     assert xfw(lib, z=A + 2 ** 20 + 8) == ALIAS              # logits over lse
-    need = lib.cross_entropy_fw_workspace_bytes(64, 32000, F16)
-    assert need > 0                                          # 64 rows: split over workgroups
-    assert xfw(lib, V=32000, ws_bytes=need - 8) == WS
-    assert xfw(lib, V=32000, ws=None) == WS
-    assert lib.cross_entropy_fw_workspace_bytes(8192, 32000, F16) == 0   # one workgroup per row
+    need = lib.cross_entropy_fw_workspace_bytes(64, 200000, F16)
+    assert need > 0                                          # rows above 256 KB: split
+    assert xfw(lib, V=200000, ws_bytes=need - 8) == WS
+    assert xfw(lib, V=200000, ws=None) == WS
+    assert lib.cross_entropy_fw_workspace_bytes(64, 32000, F16) == 0     # one workgroup per row
+    assert lib.cross_entropy_fw_workspace_bytes(8192, 32000, F16) == 0
     assert xfw(lib, N=0) == OK
 
 

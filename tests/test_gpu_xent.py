@@ -94,10 +94,19 @@ def test_tokens_fp32():
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
 @pytest.mark.parametrize("V", W.XENT_VOCABS)
 def test_few_rows_split_over_workgroups(V, dtype):
-    """64 rows (a decoding batch): each row is split over several workgroups, the forward
-    combines chunk partials in a second kernel."""
-    assert lnr.cross_entropy_fw_workspace_bytes(64, V, dtype) > 0
+    """64 rows (a decoding batch): the backward splits each row over several workgroups; the
+    forward streams each row in one workgroup (rows of up to 256 KB are not split)."""
+    assert lnr.cross_entropy_fw_workspace_bytes(64, V, dtype) == 0
     run_xent(W.xent_case(f"xent-split-64x{V}-{dtype}", 64, V, dtype=dtype, seed_base=7800 + V % 97))
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+@pytest.mark.parametrize("N", [1, 5])
+def test_long_rows_split_forward(N, dtype):
+    """Rows above 256 KB (140001 logits) with few rows: the forward splits each row over
+    workgroups and combines the chunk partials in a second kernel, in chunk order."""
+    assert lnr.cross_entropy_fw_workspace_bytes(N, 140001, dtype) > 0
+    run_xent(W.xent_case(f"xent-long-{N}x140001-{dtype}", N, 140001, dtype=dtype, seed_base=7700 + N))
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
@@ -125,14 +134,15 @@ def test_in_place_backward_and_determinism(dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
-@pytest.mark.parametrize("NV", [(50, 1001), (20, 20011)])
+@pytest.mark.parametrize("NV", [(50, 1001), (20, 20011), (3, 140001)])
 @pytest.mark.parametrize("dz_phase", ["line", "16B", "scalar"])
 def test_unaligned_and_phase_shifted_buffers(dz_phase, NV, dtype):
     """Logits one element past a 16-byte boundary (vector middle after a scalar head of up to
     a 128-byte line), and the gradient buffer at the logits' 128-byte phase ("line"), at their
     16-byte phase only ("16B": 16-byte vectors from dz's first 16-byte boundary), or at
-    another 16-byte phase ("scalar": every element on its own). 20 x 20011 also splits each
-    row over several workgroups, whose inner boundaries are rounded to lines."""
+    another 16-byte phase ("scalar": every element on its own). 20 x 20011 splits each row
+    of the backward over several workgroups, 3 x 140001 those of both passes; inner chunk
+    boundaries are rounded to lines."""
     N, V = NV
     case = W.xent_case(f"xent-unaligned-{N}x{V}", N, V, dtype=dtype, seed_base=8200 + N)
     es = torch.empty((), dtype=dtype).element_size()
