@@ -95,6 +95,13 @@ __device__ __forceinline__ void store16_or_drop(const void *wave_base, uint32_t 
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), wave_rsrc(wave_base), off, 0,
                                            kBufferNonTemporal);
 }
+// A 16-byte vector through the same kind of descriptor, non-temporal: a lane whose offset is
+// beyond the range (kDropOffset) reads zeros and touches no memory.
+template <typename T>
+__device__ __forceinline__ RawVec<T> load16_or_zero(const void *wave_base, uint32_t off) {
+    return __builtin_bit_cast(RawVec<T>, __builtin_amdgcn_raw_buffer_load_b128(wave_rsrc(wave_base), off, 0,
+                                                                               kBufferNonTemporal));
+}
 // A float through a descriptor of `range` bytes (0: every store dropped), cached.
 __device__ __forceinline__ void store4_or_drop(const void *wave_base, int32_t range, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), wave_rsrc(wave_base, range), off, 0, 0);

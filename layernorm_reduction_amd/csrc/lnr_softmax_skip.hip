@@ -19,9 +19,11 @@
 //
 // The causal limit is an index test. The mask test needs the mask vector first: it is read
 // through the caches (one [B, Tk] row serves all H*Tq rows of a batch), and the score load
-// waits for it. Each conditional load fills a raw 16-byte register vector that already holds
-// the skipped value, and nothing is converted until every load of the row is issued: a
-// conversion inside the branch would make the compiler wait for each load in turn.
+// waits for it. The score loads are buffer loads through a descriptor based at the row of the
+// wave's first row group: a skipped vector's lane passes an offset beyond the descriptor's
+// range and reads zeros without touching memory. So every load of a row is issued at once,
+// with no branch: with a branch around each load, the compiler waited for each load (or pair
+// of loads) in turn.
 #include <math.h>
 
 #include <type_traits>
@@ -93,22 +95,32 @@ __global__ __launch_bounds__(WG) void softmax_fw_skip(T *out, const T *inp,
     RawVec<T> m[IT];
     if (mask != nullptr)
         mask_runs<T, G, IT>(mask + static_cast<int64_t>(divu32(r, per_batch)) * Tk, lane, need, m);
+    else
+#pragma unroll
+        for (int k = 0; k < IT; ++k) m[k] = splat<T>(0.f);
+    // The wave's row base (its first row group's row; rows of one wave are consecutive).
+    const uint32_t wrow = __builtin_amdgcn_readfirstlane(r);
     RawVec<T> xr[IT];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
-        xr[k] = splat<T>(-INFINITY);
-        if (need[k]) xr[k] = load_stream_raw<T>(inp + base + static_cast<int64_t>(k * G + lane) * V);
+        const uint32_t off = need[k] ? static_cast<uint32_t>(((r - wrow) * static_cast<int64_t>(Tk) +
+                                                              static_cast<int64_t>(k * G + lane) * V) *
+                                                             static_cast<int64_t>(sizeof(T)))
+                                     : kDropOffset;
+        xr[k] = load16_or_zero<T>(inp + static_cast<int64_t>(wrow) * Tk, off);
     }
+    // Skipped vectors take -inf (they read zeros). At fp16 the widening and the mask add are
+    // one mixed-precision fma, as in the dense kernel (x * 1 + m, both exact in fp32, rounded
+    // once like the plain sum); the mask of a skipped vector is -inf or 0, so -inf stays.
+    float one = 1.0f;
+    if constexpr (V == 8) asm("" : "+v"(one));
     float z[IT][V];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
-        widen<T>(xr[k], z[k]);
-        if (mask != nullptr && need[k]) {
-            float mf[V];
-            widen<T>(m[k], mf);
+        xr[k] = need[k] ? xr[k] : splat<T>(-INFINITY);
 #pragma unroll
-            for (int e = 0; e < V; ++e) z[k][e] += mf[e];
-        }
+        for (int e = 0; e < V; ++e)
+            z[k][e] = __builtin_fmaf(static_cast<float>(xr[k][e]), one, static_cast<float>(m[k][e]));
     }
     if (causal) {
 #pragma unroll
@@ -176,15 +188,17 @@ __global__ __launch_bounds__(WG) void softmax_bw_skip(T *dinp, const T *dout,
         RawVec<T> m[IT];
         mask_runs<T, G, IT>(mask + static_cast<int64_t>(divu32(r, per_batch)) * Tk, lane, need, m);
     }
+    // Skipped vectors read zeros (y = 0 and dy = 0 give dx = 0) without touching memory.
+    const uint32_t wrow = __builtin_amdgcn_readfirstlane(r);
     RawVec<T> yr[IT], gr[IT];
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
-        yr[k] = gr[k] = splat<T>(0.f);
-        if (need[k]) {
-            const int64_t off = base + static_cast<int64_t>(k * G + lane) * V;
-            yr[k] = load_stream_raw<T>(y + off);
-            gr[k] = load_stream_raw<T>(dout + off);
-        }
+        const uint32_t off = need[k] ? static_cast<uint32_t>(((r - wrow) * static_cast<int64_t>(Tk) +
+                                                              static_cast<int64_t>(k * G + lane) * V) *
+                                                             static_cast<int64_t>(sizeof(T)))
+                                     : kDropOffset;
+        yr[k] = load16_or_zero<T>(y + static_cast<int64_t>(wrow) * Tk, off);
+        gr[k] = load16_or_zero<T>(dout + static_cast<int64_t>(wrow) * Tk, off);
     }
     float yv[IT][V], gv[IT][V];
 #pragma unroll
