@@ -191,6 +191,10 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
     if constexpr (V == 8) asm("" : "+v"(one));
     // Stores are branch-free (store16_or_drop): offsets count from the row of the wave's first
     // row group; a lane of a row past the end, or of a vector slot past the row, is dropped.
+    // Rows over eight or more waves (fp32 from 4096 columns) store under a branch instead:
+    // measured in one process at [32768,4096] fp32, 169.5 us against 175.0 branch-free, while
+    // the fp16 plans (up to four waves per row) run 0.5-1.2% faster branch-free.
+    constexpr bool kBranchStores = G >= 512;
     const int grp0 = __builtin_amdgcn_readfirstlane(grp);
     const int32_t stat_range = rstd != nullptr ? kBufferRange : 0;  // statistics not wanted: dropped
     fetch(r0 + grp, r0 + grp < r1);
@@ -279,12 +283,25 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
                 else
                     o[e] = __builtin_fmaf(__builtin_fmaf(d[k][e], rs, nmr), gm[k][e], bt[k][e]);
             }
-            store16_or_drop(y + wrow * static_cast<int64_t>(C), off_of(k), pack16<T>(o));
+            if constexpr (kBranchStores) {
+                const int c = k * G + lane;
+                if (live && c < nvec)
+                    store_stream<T>(y + row * static_cast<int64_t>(C) + static_cast<int64_t>(c) * V, o);
+            } else {
+                store16_or_drop(y + wrow * static_cast<int64_t>(C), off_of(k), pack16<T>(o));
+            }
         }
-        // One lane per row stores its statistics (RMSNorm: no mean); the others are dropped.
-        const uint32_t soff = (live && lane == 0) ? static_cast<uint32_t>((row - wrow) * 4) : kDropOffset;
-        if constexpr (!RMS) store4_or_drop(stat_range ? mean + wrow : rstd, stat_range, soff, K + m1);
-        store4_or_drop(stat_range ? rstd + wrow : mean, stat_range, soff, rs);
+        // One lane per row stores its statistics (RMSNorm: no mean).
+        if constexpr (kBranchStores) {
+            if (live && lane == 0 && rstd != nullptr) {
+                if constexpr (!RMS) mean[row] = K + m1;
+                rstd[row] = rs;
+            }
+        } else {
+            const uint32_t soff = (live && lane == 0) ? static_cast<uint32_t>((row - wrow) * 4) : kDropOffset;
+            if constexpr (!RMS) store4_or_drop(stat_range ? mean + wrow : rstd, stat_range, soff, K + m1);
+            store4_or_drop(stat_range ? rstd + wrow : mean, stat_range, soff, rs);
+        }
     }
 }
 
@@ -937,6 +954,8 @@ struct LnPlan {
     int WG;      // workgroup size
     int R;       // forward: rows per row group per workgroup (1 = one row each);
                  // backward: rows fetched ahead of the row being reduced (1 or 2)
+    int64_t min_rows = 0;  // taken only by launches of at least this many rows (a bucket's
+                           // plans are listed longest-launch first)
 };
 
 // Measured on MI355X (fp16, N = 8192..32768): both LayerNorm kernels run best with one or
@@ -964,20 +983,29 @@ template <> struct LnFwTable<float> {  // V = 4
 // The backward row kernel runs within 2-11% of a read-two-write-one stream of the same size
 // (N = 16384..32768). Up to 1024 columns (fp16) and 512 (fp32) a row sits inside one wave and
 // its dx stores are deferred (DEFER in the kernel): with that, two vectors per lane over 512
-// threads beat a row over two waves at fp16 1024 columns (-0.5 to -2.4%) and at fp32 512
-// columns (-9%). Four fp32 vectors per lane at 1024 columns spill and lose (+3%).
+// threads beat a row over two waves at fp16 1024 columns up to 16384 rows (-0.5 to -2.4%) and
+// at fp32 512 columns (-9%). Four fp32 vectors per lane at 1024 columns spill and lose (+3%).
+// Longer fp16 launches at 1024 columns take a row over two waves with two rows fetched ahead:
+// each load instruction of the workgroup then covers four whole consecutive rows (8 KB), and
+// the deeper prefetch hides the cross-wave reduction (measured in one process against the
+// one-wave plan: 24576 rows -4.4%, 32768 -3.6%, 65536 -7.2%; 16384 +2.5%). Rows of 4-8 KB
+// over four or eight waves likewise take two rows ahead in 512-thread workgroups instead of
+// one row ahead in 1024-thread ones: fp16 2048 columns -7 to -8%, fp32 1024 columns -4%,
+// fp32 2048 columns -5 to -6% (16384 and 32768 rows); at fp32 512 columns two waves with two
+// rows ahead lose (+4%) to the one-wave plan.
 template <typename T> struct LnBwTable;
 template <> struct LnBwTable<f16> {
     static constexpr LnPlan plans[] = {
         {64, 8, 1, 512, 1},      {128, 16, 1, 512, 1},    {256, 32, 1, 512, 1},
-        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 64, 2, 512, 1},
-        {2048, 256, 1, 1024, 1}, {4096, 256, 2, 512, 2},  {8192, 512, 2, 512, 2}};
+        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 128, 1, 512, 2, 24576},
+        {1024, 64, 2, 512, 1},   {2048, 256, 1, 512, 2},  {4096, 256, 2, 512, 2},
+        {8192, 512, 2, 512, 2}};
 };
 template <> struct LnBwTable<float> {
     static constexpr LnPlan plans[] = {
         {64, 16, 1, 512, 1},     {128, 32, 1, 512, 1},    {256, 64, 1, 512, 1},
-        {512, 64, 2, 512, 1},    {768, 64, 3, 512, 1},    {1024, 256, 1, 1024, 1},
-        {2048, 512, 1, 1024, 1}, {4096, 1024, 1, 1024, 1}, {8192, 1024, 2, 1024, 1}};
+        {512, 64, 2, 512, 1},    {768, 64, 3, 512, 1},    {1024, 256, 1, 512, 2},
+        {2048, 512, 1, 512, 2},  {4096, 1024, 1, 1024, 1}, {8192, 1024, 2, 1024, 1}};
 };
 
 // Backward plans of the fused bias-dropout-residual LayerNorm. Its third column partial
@@ -1004,9 +1032,9 @@ template <> struct BdrBwTable<float> {
 constexpr int64_t kLnBwTargetBlocks = 256;  // one partial row per CU
 
 template <typename Table>
-static bool find_plan(int64_t C, LnPlan &out) {
+static bool find_plan(int64_t C, int64_t N, LnPlan &out) {
     for (const LnPlan &p : Table::plans)
-        if (C <= p.bucket) {
+        if (C <= p.bucket && N >= p.min_rows) {
             out = p;
             return true;
         }
@@ -1029,9 +1057,9 @@ static void bw_partials(int64_t N, int64_t C, lnr_dtype dtype, int64_t &p_vec, i
     LnPlan p{};
     bool ok;
     if (bdr)
-        ok = dtype == LNR_F16 ? find_plan<BdrBwTable<f16>>(C, p) : find_plan<BdrBwTable<float>>(C, p);
+        ok = dtype == LNR_F16 ? find_plan<BdrBwTable<f16>>(C, N, p) : find_plan<BdrBwTable<float>>(C, N, p);
     else
-        ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, p) : find_plan<LnBwTable<float>>(C, p);
+        ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, N, p) : find_plan<LnBwTable<float>>(C, N, p);
     const int64_t groups = ok ? p.WG / p.G : 1;
     rpb_vec = bw_rows_per_block(N, groups);
     p_vec = bw_blocks(N, rpb_vec);
@@ -1073,7 +1101,7 @@ struct LnBwArgs {
 template <typename T, int MODE, int I>
 static hipError_t dispatch_ln_fw(const LnFwArgs &a, hipStream_t st) {
     constexpr LnPlan p = LnFwTable<T>::plans[I];
-    if (a.C <= p.bucket) {
+    if (a.C <= p.bucket && a.N >= p.min_rows) {
         static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && p.R >= 1, "bad forward plan");
         constexpr int64_t RPB = static_cast<int64_t>(p.WG / p.G) * p.R;
         const int64_t blocks = (a.N + RPB - 1) / RPB;
@@ -1123,7 +1151,7 @@ template <typename T, int MODE, int I>
 static hipError_t dispatch_ln_bw(const LnBwArgs &a, hipStream_t st) {
     using Table = std::conditional_t<MODE == kBdrLayerNorm, BdrBwTable<T>, LnBwTable<T>>;
     constexpr LnPlan p = Table::plans[I];
-    if (a.C <= p.bucket) {
+    if (a.C <= p.bucket && a.N >= p.min_rows) {
         static_assert(p.WG % p.G == 0 && p.WG % 64 == 0 && (p.R == 1 || p.R == 2), "bad backward plan");
         static_assert(2 * (p.WG / 64) >= 2, "reduction slots");
         hipError_t e;
@@ -1585,9 +1613,9 @@ extern "C" int lnr_layernorm_plan(int64_t N, int64_t C, lnr_dtype dtype, int whi
     bool ok = false;
     if (vec) {
         if (which == 0)
-            ok = dtype == LNR_F16 ? find_plan<LnFwTable<f16>>(C, p) : find_plan<LnFwTable<float>>(C, p);
+            ok = dtype == LNR_F16 ? find_plan<LnFwTable<f16>>(C, N, p) : find_plan<LnFwTable<float>>(C, N, p);
         else
-            ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, p) : find_plan<LnBwTable<float>>(C, p);
+            ok = dtype == LNR_F16 ? find_plan<LnBwTable<f16>>(C, N, p) : find_plan<LnBwTable<float>>(C, N, p);
     }
     if (!ok) p = LnPlan{0, kLnGenericWG, 0, kLnGenericWG, 1};
     *bucket = p.bucket;

@@ -7,6 +7,11 @@ workload shapes, they reach every instantiation of the row-length dispatch."""
 NORM_EDGE_C = [1, 2, 8, 24, 64, 100, 128, 200, 264, 768, 1000, 1024, 1536, 2048, 2056, 4095,
                4096, 8191, 8192]
 
+# Launches long enough for the backward's long-launch plans (fp16, 24576 rows or more at up to
+# 1024 columns): ragged row counts (not whole row groups, a partial last band) at a width with
+# idle lanes and at the bucket's full width.
+NORM_LONG_F16 = [(24577, 1000), (24579, 1024)]
+
 # Softmax row lengths: every bucket of the template list at fp16 and fp32, its neighbours,
 # and odd lengths (element-wise kernel).
 SOFTMAX_EDGE_TK = [1, 2, 8, 16, 24, 31, 32, 33, 40, 100, 200, 256, 264, 520, 1000, 2047, 2048]

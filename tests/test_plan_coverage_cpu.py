@@ -22,12 +22,23 @@ def norm_buckets(dtype, backward):
             for c in range(1, lnr.LAYERNORM_MAX_C + 1)} - {0}
 
 
+# Row counts at which a bucket's plan may change (the backward's long-launch plans start at
+# 24576 rows); every (bucket, lanes, vectors, workgroup) instantiation a launch can take.
+PLAN_ROWS = (64, 16384, 24576, 32768, 65536)
+
+
+def norm_plans(dtype, backward):
+    return {lnr.layernorm_plan(n, c, dtype, backward=backward)[:4]
+            for n in PLAN_ROWS for c in range(1, lnr.LAYERNORM_MAX_C + 1)} - {(0, 256, 0, 256)}
+
+
 def reached_softmax(lengths, dtype, backward):
     return {lnr.softmax_plan(t, dtype, backward=backward)[0] for t in lengths} - {0}
 
 
-def reached_norm(widths, dtype, backward):
-    return {lnr.layernorm_plan(64, c, dtype, backward=backward)[0] for c in widths} - {0}
+def reached_norm(cases, dtype, backward):
+    """cases: (rows, width) pairs."""
+    return {lnr.layernorm_plan(n, c, dtype, backward=backward)[:4] for n, c in cases} - {(0, 256, 0, 256)}
 
 
 def test_plan_tables_have_the_template_buckets():
@@ -52,20 +63,44 @@ def test_softmax_gpu_cases_reach_every_bucket():
             assert not missing, ("skip", dt, bw, sorted(missing))
 
 
-def test_norm_gpu_cases_reach_every_bucket():
-    edge = set(gpu_cases.NORM_EDGE_C)
-    # LayerNorm: workloads 1 (fp32, 64), 2 (fp16, 256), 4 (fp16 sweep), 5 (both, 1024, 4096)
-    ln = {F16: edge | {256, 1024, 4096} | set(W.LAYERNORM_C_SWEEP), F32: edge | {64, 1024, 4096}}
-    # RMSNorm: the page's model shape (256, both), the sweep (fp16), [32768, 1024] fp32
-    rms = {F16: edge | {256} | set(W.LAYERNORM_C_SWEEP), F32: edge | {256, 1024}}
-    # bias + dropout + residual: [8192, 256] and [16384, 768/1024/4096] fp16, 1024/8192 fp32
-    bdr = {F16: {256, 768, 1024, 4096} | {c for d, c in gpu_cases.BDR_EDGE if d == "fp16"},
-           F32: {1024, 8192} | {c for d, c in gpu_cases.BDR_EDGE if d == "fp32"}}
+def test_norm_gpu_cases_reach_every_plan():
+    # edge widths run at 1, 7 and 1031 rows
+    edge = {(n, c) for c in gpu_cases.NORM_EDGE_C for n in (1, 7, 1031)}
+    sweep = {(16384, c) for c in W.LAYERNORM_C_SWEEP}
+    long16 = set(gpu_cases.NORM_LONG_F16)
+    # LayerNorm: workloads 1 (fp32 [64,64]), 2 (fp16 [8192,256]), 4 (fp16 sweep), 5 (both,
+    # [32768, 1024/4096])
+    w5 = {(32768, 1024), (32768, 4096)}
+    ln = {F16: edge | {(8192, 256)} | sweep | w5 | long16, F32: edge | {(64, 64)} | w5}
+    # RMSNorm: the page's model shape [8192,256] (both), the sweep (fp16), [32768,1024] fp32
+    rms = {F16: edge | {(8192, 256)} | sweep | long16, F32: edge | {(8192, 256), (32768, 1024)}}
+    # bias + dropout + residual: [8192,256] and [16384, 768/1024/4096] fp16, [8192,1024] and
+    # [2048,8192] fp32, its edge widths at 1, 7 and 1031 rows
+    bdr = {F16: {(8192, 256), (16384, 768), (16384, 1024), (16384, 4096)}
+           | {(n, c) for d, c in gpu_cases.BDR_EDGE if d == "fp16" for n in (1, 7, 1031)},
+           F32: {(8192, 1024), (2048, 8192)}
+           | {(n, c) for d, c in gpu_cases.BDR_EDGE if d == "fp32" for n in (1, 7, 1031)}}
     for name, table in (("layernorm", ln), ("rmsnorm", rms), ("bdr", bdr)):
         for dt in (F16, F32):
             for bw in (False, True):
-                missing = norm_buckets(dt, bw) - reached_norm(table[dt], dt, bw)
+                if name == "bdr" and bw:
+                    # its backward has a plan table of its own over the same buckets, with
+                    # no long-launch plans: every bucket reached
+                    got = {p[0] for p in reached_norm(table[dt], dt, bw)}
+                    missing = norm_buckets(dt, bw) - got
+                else:
+                    missing = norm_plans(dt, bw) - reached_norm(table[dt], dt, bw)
                 assert not missing, (name, dt, bw, sorted(missing))
+
+
+def test_long_launch_plans_exist_and_are_reached():
+    """The fp16 backward changes plan at 24576 rows at 1024 columns; the GPU's long-launch
+    cases sit above that row count and in that bucket."""
+    short = lnr.layernorm_plan(16384, 1024, F16, backward=True)[:4]
+    long = lnr.layernorm_plan(24576, 1024, F16, backward=True)[:4]
+    assert short != long and short[0] == long[0] == 1024
+    for n, c in gpu_cases.NORM_LONG_F16:
+        assert lnr.layernorm_plan(n, c, F16, backward=True)[:4] == long
 
 
 def test_bdr_edge_widths_take_its_vector_path():
