@@ -388,7 +388,9 @@ LNR_API int lnr_time_next_launch(void *start_event, void *stop_event);
  * softmax backward asks for): for rows of Tk elements of `dtype` in 16-byte-aligned
  * buffers, writes the bucket (the longest row of the chosen instantiation; 0 = element-wise
  * fallback), the lanes per row and the 16-byte vectors per lane of the forward (which = 0)
- * or backward (which = 1) kernel. Touches no device.
+ * or backward (which = 1) kernel, or of the read-skipping forward (2) or backward (3), which
+ * call the dense kernels for rows that are not whole 16-byte vectors. `which` outside 0..3
+ * is LNR_ERR_SHAPE. Touches no device.
  */
 LNR_API int lnr_softmax_plan(int64_t Tk, lnr_dtype dtype, int which, int *bucket,
                              int *lanes_per_row, int *vectors_per_lane);

@@ -631,11 +631,13 @@ def xor_bytes(dst, a, b):
     return dst
 
 
-def softmax_plan(Tk: int, dtype_code: int, backward: bool = False):
-    """(bucket, lanes per row, 16-byte vectors per lane) of the forward or backward kernel for
-    aligned buffers; bucket 0 means the element-wise fallback."""
+def softmax_plan(Tk: int, dtype_code: int, backward: bool = False, skip: bool = False):
+    """(bucket, lanes per row, 16-byte vectors per lane) of the forward or backward kernel (of
+    the read-skipping entry points with skip=True) for aligned buffers; bucket 0 means the
+    element-wise fallback."""
     b, g, it = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(load().lnr_softmax_plan(int(Tk), int(dtype_code), int(bool(backward)), ctypes.byref(b),
+    which = int(bool(backward)) + (2 if skip else 0)
+    _check(load().lnr_softmax_plan(int(Tk), int(dtype_code), which, ctypes.byref(b),
                                    ctypes.byref(g), ctypes.byref(it)), "lnr_softmax_plan")
     return b.value, g.value, it.value
 

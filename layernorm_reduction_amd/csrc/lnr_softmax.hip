@@ -288,7 +288,14 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 // at 256 fp16 keys (7-12% slower with four), so the two add a row's products in different
 // orders there and agree to an fp16 ulp; fp32 512 keys over 32 lanes with four vectors was
 // 1-4% faster but not taken, since at fp32 storage the cancellation in dy - sum makes two
-// summation orders differ by more than an ulp.
+// summation orders differ by more than an ulp. At fp16 512 keys both directions take one
+// vector per lane over a whole wave, one row per 64-thread workgroup (forward -2.6 to -3.2%
+// against two vectors over 32 lanes in 256 threads; backward -1 to -2% padded, within 1%
+// causal, against 128 threads), and the 128-key backward 64-thread workgroups (-3.6%); one
+// wave per workgroup elsewhere ties or loses up to 6%. The read-skipping forward keeps two
+// vectors over 32 lanes at 512 keys (one vector per lane made it 22% slower: it loads the
+// row's mask before its scores, so fewer loads per lane expose that latency), so there the
+// two forwards add a row's exponentials in different orders and agree to an fp16 ulp.
 // ------------------------------------------------------------------------------------------
 struct Plan {
     int bucket;  // longest row this instantiation takes; 0 = element-wise fallback
@@ -300,7 +307,7 @@ struct Plan {
 template <typename T> struct SoftmaxFwTable;
 template <> struct SoftmaxFwTable<f16> {   // V = 8
     static constexpr Plan plans[] = {{32, 4, 1, 128},   {64, 8, 1, 128},   {128, 8, 2, 256},
-                                     {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 32, 2, 256},
+                                     {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 64, 1, 64},
                                      {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
 };
 template <> struct SoftmaxFwTable<float> { // V = 4
@@ -310,8 +317,8 @@ template <> struct SoftmaxFwTable<float> { // V = 4
 };
 template <typename T> struct SoftmaxBwTable;
 template <> struct SoftmaxBwTable<f16> {
-    static constexpr Plan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 256},
-                                     {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 64, 1, 128},
+    static constexpr Plan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 64},
+                                     {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 64, 1, 64},
                                      {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
 };
 template <> struct SoftmaxBwTable<float> {
@@ -475,16 +482,26 @@ extern "C" int attn_softmax_bw(void *dinp, const void *dout, const void *out_fw,
     return status_of(e);
 }
 
+// The read-skipping kernels' plan for (Tk, dtype) (lnr_softmax_skip.hip).
+void skip_plan_of(int64_t Tk, lnr_dtype dtype, bool backward, int &bucket, int &G, int &IT);
+
 // Introspection for tests and benchmarks: the bucket, lanes per row and vectors per lane
-// that attn_softmax_fw (which = 0) or attn_softmax_bw (which = 1) use for (Tk, dtype) with
-// aligned buffers; bucket 0 means the element-wise fallback.
+// that attn_softmax_fw (which = 0), attn_softmax_bw (1), attn_softmax_fw_skip (2) or
+// attn_softmax_bw_skip (3) use for (Tk, dtype) with aligned buffers; bucket 0 means the
+// element-wise fallback (the skipping entry points then call the dense ones).
 extern "C" int lnr_softmax_plan(int64_t Tk, lnr_dtype dtype, int which, int *bucket,
                                 int *lanes_per_row, int *vectors_per_lane) {
     if (!valid_dtype(dtype)) return LNR_ERR_DTYPE;
     if (Tk < 1) return LNR_ERR_SHAPE;
     if (Tk > LNR_SOFTMAX_MAX_TK) return LNR_ERR_UNSUPPORTED;
+    if (which < 0 || which > 3) return LNR_ERR_SHAPE;
     if (bucket == nullptr || lanes_per_row == nullptr || vectors_per_lane == nullptr) return LNR_ERR_NULL;
     const bool vec = (static_cast<size_t>(Tk) * dtype_size(dtype)) % 16 == 0;
+    if (which >= 2) {
+        if (!vec) return lnr_softmax_plan(Tk, dtype, which - 2, bucket, lanes_per_row, vectors_per_lane);
+        skip_plan_of(Tk, dtype, which == 3, *bucket, *lanes_per_row, *vectors_per_lane);
+        return LNR_OK;
+    }
     Plan p;
     if (dtype == LNR_F16)
         p = which == 0 ? softmax_plan<SoftmaxFwTable<f16>>(Tk, vec) : softmax_plan<SoftmaxBwTable<f16>>(Tk, vec);

@@ -341,6 +341,25 @@ static bool skip_vec_ok(const void *out, const void *a, const void *b, const voi
 
 using namespace lnr;
 
+// Plan introspection for lnr_softmax_plan (which = 2 and 3); Tk of whole 16-byte vectors.
+void skip_plan_of(int64_t Tk, lnr_dtype dtype, bool backward, int &bucket, int &G, int &IT) {
+    SkipPlan p{0, 64, 0, 0};
+    auto find = [&](const auto &plans) {
+        for (const SkipPlan &q : plans)
+            if (Tk <= q.bucket) {
+                p = q;
+                return;
+            }
+    };
+    if (dtype == LNR_F16)
+        backward ? find(SkipBwTable<f16>::plans) : find(SkipFwTable<f16>::plans);
+    else
+        backward ? find(SkipBwTable<float>::plans) : find(SkipFwTable<float>::plans);
+    bucket = p.bucket;
+    G = p.G;
+    IT = p.IT;
+}
+
 extern "C" int attn_softmax_fw_skip(void *out, const void *inp, const void *mask, int64_t B,
                                     int64_t H, int64_t Tq, int64_t Tk, int causal,
                                     lnr_dtype dtype, void *stream) {

@@ -380,18 +380,22 @@ def test_softmax_buckets_are_the_pages_template_list(lib):
     templates = GOLDEN["softmax_bw_row_length_templates"]["value"]
     for dtype, V in ((F16, 8), (F32, 4)):
         for bw in (False, True):
-            buckets = set()
-            for Tk in templates:
-                b, G, IT = lnr.softmax_plan(Tk, dtype, backward=bw)
-                assert b == Tk and G * IT * V == b, (dtype, bw, Tk, b, G, IT)
-                assert G in (1, 2, 4, 8, 16, 32, 64)
-                buckets.add(b)
-            assert sorted(buckets) == templates
-            # lengths between templates take the next larger bucket; rows whose byte length
-            # is not a multiple of 16 take the element-wise fallback (bucket 0)
-            assert lnr.softmax_plan(264, dtype, backward=bw)[0] == 384
-            assert lnr.softmax_plan(2047, dtype, backward=bw)[0] == 0
-            assert lnr.softmax_plan(33, dtype, backward=bw)[0] == 0
+            for skip in (False, True):
+                buckets = set()
+                for Tk in templates:
+                    b, G, IT = lnr.softmax_plan(Tk, dtype, backward=bw, skip=skip)
+                    assert b == Tk and G * IT * V == b, (dtype, bw, skip, Tk, b, G, IT)
+                    assert G in (1, 2, 4, 8, 16, 32, 64)
+                    buckets.add(b)
+                assert sorted(buckets) == templates
+                # lengths between templates take the next larger bucket; rows whose byte
+                # length is not a multiple of 16 take the element-wise fallback (bucket 0)
+                assert lnr.softmax_plan(264, dtype, backward=bw, skip=skip)[0] == 384
+                assert lnr.softmax_plan(2047, dtype, backward=bw, skip=skip)[0] == 0
+                assert lnr.softmax_plan(33, dtype, backward=bw, skip=skip)[0] == 0
+    # `which` outside 0..3 is rejected
+    b = ctypes.c_int()
+    assert lib.lnr_softmax_plan(256, F16, 4, ctypes.byref(b), ctypes.byref(b), ctypes.byref(b)) == 2
     assert lnr.softmax_plan(16, F16)[0] == 32
     assert lnr.layernorm_plan(16, 100, F16)[0] == 0              # 200 B rows: fallback
     assert lnr.layernorm_plan(16, 100, F32)[0] == 128            # 400 B rows: masked tail

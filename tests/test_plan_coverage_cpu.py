@@ -13,8 +13,9 @@ F32, F16 = lnr.LNR_F32, lnr.LNR_F16
 ES = {F32: 4, F16: 2}
 
 
-def softmax_buckets(dtype, backward):
-    return {lnr.softmax_plan(t, dtype, backward=backward)[0] for t in range(1, lnr.SOFTMAX_MAX_TK + 1)} - {0}
+def softmax_buckets(dtype, backward, skip=False):
+    return {lnr.softmax_plan(t, dtype, backward=backward, skip=skip)[0]
+            for t in range(1, lnr.SOFTMAX_MAX_TK + 1)} - {0}
 
 
 def norm_buckets(dtype, backward):
@@ -32,8 +33,8 @@ def norm_plans(dtype, backward):
             for n in PLAN_ROWS for c in range(1, lnr.LAYERNORM_MAX_C + 1)} - {(0, 256, 0, 256)}
 
 
-def reached_softmax(lengths, dtype, backward):
-    return {lnr.softmax_plan(t, dtype, backward=backward)[0] for t in lengths} - {0}
+def reached_softmax(lengths, dtype, backward, skip=False):
+    return {lnr.softmax_plan(t, dtype, backward=backward, skip=skip)[0] for t in lengths} - {0}
 
 
 def reached_norm(cases, dtype, backward):
@@ -46,6 +47,7 @@ def test_plan_tables_have_the_template_buckets():
     for dt in (F16, F32):
         for bw in (False, True):
             assert softmax_buckets(dt, bw) == tl
+            assert softmax_buckets(dt, bw, skip=True) == tl
             assert norm_buckets(dt, bw) == {64, 128, 256, 512, 768, 1024, 2048, 4096, 8192}
 
 
@@ -59,7 +61,7 @@ def test_softmax_gpu_cases_reach_every_bucket():
         for bw in (False, True):
             missing = softmax_buckets(dt, bw) - reached_softmax(lengths[dt], dt, bw)
             assert not missing, ("dense", dt, bw, sorted(missing))
-            missing = softmax_buckets(dt, bw) - reached_softmax(skip[dt], dt, bw)
+            missing = softmax_buckets(dt, bw, skip=True) - reached_softmax(skip[dt], dt, bw, skip=True)
             assert not missing, ("skip", dt, bw, sorted(missing))
 
 
