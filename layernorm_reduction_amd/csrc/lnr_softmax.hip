@@ -274,28 +274,28 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 // Row-length buckets: (G lanes per row, IT vectors per lane) for each storage type, one
 // table for the forward and one for the backward. Capacity G * IT * V equals the bucket
 // length; rows shorter than their bucket leave the trailing vectors idle. The bucket lengths
-// are the HW4 page's template list. Measured on MI355X: the forward (mask add, max, exp,
-// sum, scale) runs best with 2-4 vectors per lane from 256 columns up, and with 1-2 vectors
-// per lane on short rows, where fewer, wider groups keep each load instruction on whole
-// 128-byte lines; its fp16 32- and 64-key rows run in 128-thread workgroups (-2% against 512;
-// other sizes tie or lose up to 8% at the longer rows, which keep 256). The backward (one
-// product sum) runs best mostly with one vector per lane and as many lanes per row as the row
-// allows. Its exceptions, timed against the previous plan in one process (median of 9): fp16
-// 256 keys take four vectors over eight lanes like the forward (-2 to -3% from 32 to 256
-// MiB), fp16 1024 keys four vectors over 32 lanes (-4%), fp16 2048 and fp32 1024 keys
-// 256-thread workgroups (-4%, -5%). Fewer lanes per row lose on 32-128 fp16 keys
-// (1.04-3.8x slower) and at 512 (+2-5%). The read-skipping backward keeps one vector per lane
-// at 256 fp16 keys (7-12% slower with four), so the two add a row's products in different
-// orders there and agree to an fp16 ulp; fp32 512 keys over 32 lanes with four vectors was
-// 1-4% faster but not taken, since at fp32 storage the cancellation in dy - sum makes two
-// summation orders differ by more than an ulp. At fp16 512 keys both directions take one
-// vector per lane over a whole wave, one row per 64-thread workgroup (forward -2.6 to -3.2%
-// against two vectors over 32 lanes in 256 threads; backward -1 to -2% padded, within 1%
-// causal, against 128 threads), and the 128-key backward 64-thread workgroups (-3.6%); one
-// wave per workgroup elsewhere ties or loses up to 6%. The read-skipping forward keeps two
-// vectors over 32 lanes at 512 keys (one vector per lane made it 22% slower: it loads the
-// row's mask before its scores, so fewer loads per lane expose that latency), so there the
-// two forwards add a row's exponentials in different orders and agree to an fp16 ulp.
+// are the HW4 page's template list. Measured on MI355X, each plan against its neighbours in
+// one process (old and new library alternating, median of 7-9):
+//  * Up to 512 fp16 keys (256 fp32) both directions run best with a row on as few vectors
+//    per lane as fit a wave and one wave per workgroup: one 64-thread workgroup per row from
+//    256 fp16 keys, several rows per wave below. Against the earlier plans (two to four
+//    vectors per lane over 8-32 lanes in 256-thread workgroups): forward -2 to -4% at 64-512
+//    fp16 keys and -3 to -5% at 128-256 fp32 keys; backward -3.6% at 128 and 256 fp16 keys,
+//    -1 to -2% at 512 fp16 keys, -2 to -5% at 128-512 fp32 keys.
+//  * Longer rows keep two to four vectors per lane in 256-thread workgroups, except the
+//    2048-key forwards, where 64-thread workgroups win (-1% fp16, -4% fp32); one wave per
+//    workgroup loses 1-6% at 384-1024 fp16 keys and 384-768 fp32 keys, and up to 5% in the
+//    fp32 backward from 1024 keys. fp16 1024 keys take four vectors over 32 lanes in the
+//    backward (-4% against one vector per lane), fp16 2048 and fp32 1024 keys 256-thread
+//    workgroups (-4%, -5%).
+//  * fp32 512 keys over 32 lanes with four vectors in the backward was 1-4% faster but not
+//    taken: at fp32 storage the cancellation in dy - sum makes two summation orders differ by
+//    more than an ulp, and the read-skipping backward keeps two vectors over 64 lanes.
+// The read-skipping kernels have tables of their own: their forward loads a row's mask before
+// its scores, so one vector per lane exposes that latency (22% slower at 512 fp16 keys) and it
+// keeps several vectors per lane. Where the two forwards (or backwards) differ in lanes per
+// row or vectors per lane, they add a row's terms in different orders and agree to an ulp of
+// the storage type; elsewhere they agree exactly.
 // ------------------------------------------------------------------------------------------
 struct Plan {
     int bucket;  // longest row this instantiation takes; 0 = element-wise fallback
@@ -306,24 +306,24 @@ struct Plan {
 
 template <typename T> struct SoftmaxFwTable;
 template <> struct SoftmaxFwTable<f16> {   // V = 8
-    static constexpr Plan plans[] = {{32, 4, 1, 128},   {64, 8, 1, 128},   {128, 8, 2, 256},
-                                     {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 64, 1, 64},
-                                     {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
+    static constexpr Plan plans[] = {{32, 4, 1, 128},   {64, 8, 1, 64},    {128, 16, 1, 64},
+                                     {256, 32, 1, 64},  {384, 16, 3, 256}, {512, 64, 1, 64},
+                                     {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 64}};
 };
 template <> struct SoftmaxFwTable<float> { // V = 4
-    static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 8, 4, 256},
-                                     {256, 16, 4, 256}, {384, 32, 3, 256}, {512, 32, 4, 256},
-                                     {768, 64, 3, 256}, {1024, 64, 4, 256}, {2048, 64, 8, 256}};
+    static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 64},
+                                     {256, 64, 1, 64},  {384, 32, 3, 256}, {512, 32, 4, 256},
+                                     {768, 64, 3, 256}, {1024, 64, 4, 256}, {2048, 64, 8, 64}};
 };
 template <typename T> struct SoftmaxBwTable;
 template <> struct SoftmaxBwTable<f16> {
     static constexpr Plan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 64},
-                                     {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 64, 1, 64},
+                                     {256, 32, 1, 64},  {384, 16, 3, 256}, {512, 64, 1, 64},
                                      {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
 };
 template <> struct SoftmaxBwTable<float> {
-    static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 256},
-                                     {256, 64, 1, 128}, {384, 32, 3, 256}, {512, 64, 2, 128},
+    static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 64},
+                                     {256, 64, 1, 64},  {384, 32, 3, 256}, {512, 64, 2, 64},
                                      {768, 64, 3, 128}, {1024, 64, 4, 256}, {2048, 64, 8, 128}};
 };
 

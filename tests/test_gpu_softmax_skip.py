@@ -9,9 +9,11 @@ entries). Checked here:
   * equality with the dense entry points on the same inputs (a property of the design: the
     skipped runs contribute exactly 0 either way; equality is numeric, so -0 equals +0). Both
     directions are equal where the two use the same lanes per row and vectors per lane
-    (lnr_softmax_plan); where they do not (the backward at 256 fp16 keys, the forward at 512
-    fp16 keys), a row's sum adds the same terms in another order, and the two agree to one
-    unit in the last place of the storage type;
+    (lnr_softmax_plan). Where they do not, a row's sum adds the same terms in another order:
+    two such fp32 sums of Tk terms differ by at most 2(Tk - 1) u relative (u = 2^-24), so the
+    forward outputs (each term times the reciprocal sum) agree to (2 Tk + 4) u relative, or
+    one unit in the last place of the storage type where that is larger; the backward
+    outputs agree to one unit in the last place;
   * that skipped runs are really not read: NaN planted in them leaves the outputs finite and
     equal to the oracle's on clean inputs, where a read would poison the row (NaN + -inf and
     0 * NaN are NaN);
@@ -48,6 +50,21 @@ def assert_equal_or_one_ulp(a, b, what):
     assert not bad.any(), f"{what}: {int(bad.sum())} elements differ by more than one ulp"
 
 
+def assert_same_sum_reordered(a, b, Tk, what):
+    """a and b are the same softmax rows normalised by two fp32 sums of the same Tk terms in
+    different orders: |a - b| <= max(ulp(b), (2 Tk + 4) u |b|), u = 2^-24."""
+    if torch.equal(a, b):
+        return
+    an = a.detach().cpu().double().numpy()
+    bn = b.detach().cpu().numpy()
+    ulp = np.spacing(np.abs(bn)).astype(np.float64)
+    bound = np.maximum(ulp, (2 * Tk + 4) * 2.0 ** -24 * np.abs(bn.astype(np.float64)))
+    diff = np.abs(an - bn.astype(np.float64))
+    worst = float(np.max(diff / bound))
+    print(f"[parity] {what}: worst difference / bound {worst:.3f}", flush=True)
+    assert worst <= 1.0, f"{what}: {int((diff > bound).sum())} elements beyond the reordering bound"
+
+
 def same_plan(case, backward):
     """Whether the dense and the skipping kernel reduce a row of this case in the same order
     (the same lanes per row and vectors per lane)."""
@@ -73,7 +90,8 @@ def run_skip(case, check_chain=True):
     if same_plan(case, backward=False):
         assert torch.equal(y, y_dense), f"{case.name}: fw_skip differs from the dense forward"
     else:
-        assert_equal_or_one_ulp(y, y_dense, f"{case.name}: fw_skip against the dense forward")
+        assert_same_sum_reordered(y, y_dense, case.x.shape[-1],
+                                  f"{case.name}: fw_skip against the dense forward")
     del y_dense
 
     y_t = torch.from_numpy(y_ref).to(case.dtype)
