@@ -238,6 +238,10 @@ __global__ __launch_bounds__(WG) void softmax_bw_skip(T *dinp, const T *dout,
 
 // ------------------------------------------------------------------------------------------
 // Row-length buckets (G lanes per row, IT vectors per lane), the HW4 page's template list.
+// Measured on MI355X (fp16, old and new library alternating in one process): 64-thread
+// workgroups at 256-1024 keys in the forward and 256-512 in the backward (forward -2 to -5%,
+// backward -2 to -13%, the most on the 32 MiB GPT-2 shape); they lose at 2048 keys (+2-5%)
+// and in the 1024-key backward (+3%).
 // ------------------------------------------------------------------------------------------
 struct SkipPlan {
     int bucket;
@@ -249,8 +253,8 @@ struct SkipPlan {
 template <typename T> struct SkipFwTable;
 template <> struct SkipFwTable<f16> {
     static constexpr SkipPlan plans[] = {{32, 4, 1, 512},   {64, 8, 1, 512},   {128, 8, 2, 256},
-                                         {256, 8, 4, 256},  {384, 16, 3, 256}, {512, 32, 2, 256},
-                                         {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
+                                         {256, 8, 4, 64},   {384, 16, 3, 256}, {512, 32, 2, 64},
+                                         {768, 32, 3, 256}, {1024, 32, 4, 64}, {2048, 64, 4, 256}};
 };
 template <> struct SkipFwTable<float> {
     static constexpr SkipPlan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 8, 4, 256},
@@ -260,7 +264,7 @@ template <> struct SkipFwTable<float> {
 template <typename T> struct SkipBwTable;
 template <> struct SkipBwTable<f16> {
     static constexpr SkipPlan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 256},
-                                         {256, 32, 1, 256}, {384, 16, 3, 256}, {512, 64, 1, 128},
+                                         {256, 32, 1, 64},  {384, 16, 3, 256}, {512, 64, 1, 64},
                                          {768, 32, 3, 256}, {1024, 64, 2, 128}, {2048, 64, 4, 128}};
 };
 template <> struct SkipBwTable<float> {
