@@ -238,10 +238,11 @@ __global__ __launch_bounds__(WG) void softmax_bw_skip(T *dinp, const T *dout,
 
 // ------------------------------------------------------------------------------------------
 // Row-length buckets (G lanes per row, IT vectors per lane), the HW4 page's template list.
-// Measured on MI355X (fp16, old and new library alternating in one process): 64-thread
-// workgroups at 256-1024 keys in the forward and 256-512 in the backward (forward -2 to -5%,
-// backward -2 to -13%, the most on the 32 MiB GPT-2 shape); they lose at 2048 keys (+2-5%)
-// and in the 1024-key backward (+3%).
+// Measured on MI355X (old and new library alternating in one process): 64-thread workgroups
+// at fp16 256-1024 keys in the forward and 128-512 in the backward (forward -2 to -5%,
+// backward -2 to -13%, the most on the 32 MiB GPT-2 shape), fp32 128, 256 and 1024 keys in
+// the forward (-2 to -6%) and 256 in the backward (-3%); they lose or tie at 2048 keys
+// (+2-5%), in the fp16 1024-key backward (+3%) and at fp32 512 keys.
 // ------------------------------------------------------------------------------------------
 struct SkipPlan {
     int bucket;
@@ -257,19 +258,19 @@ template <> struct SkipFwTable<f16> {
                                          {768, 32, 3, 256}, {1024, 32, 4, 64}, {2048, 64, 4, 256}};
 };
 template <> struct SkipFwTable<float> {
-    static constexpr SkipPlan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 8, 4, 256},
-                                         {256, 16, 4, 256}, {384, 32, 3, 256}, {512, 32, 4, 256},
-                                         {768, 64, 3, 256}, {1024, 64, 4, 256}, {2048, 64, 8, 256}};
+    static constexpr SkipPlan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 8, 4, 64},
+                                         {256, 16, 4, 64},  {384, 32, 3, 256}, {512, 32, 4, 256},
+                                         {768, 64, 3, 256}, {1024, 64, 4, 64},  {2048, 64, 8, 256}};
 };
 template <typename T> struct SkipBwTable;
 template <> struct SkipBwTable<f16> {
-    static constexpr SkipPlan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 256},
+    static constexpr SkipPlan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 64},
                                          {256, 32, 1, 64},  {384, 16, 3, 256}, {512, 64, 1, 64},
                                          {768, 32, 3, 256}, {1024, 64, 2, 128}, {2048, 64, 4, 128}};
 };
 template <> struct SkipBwTable<float> {
     static constexpr SkipPlan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 256},
-                                         {256, 64, 1, 128}, {384, 32, 3, 256}, {512, 64, 2, 128},
+                                         {256, 64, 1, 64},  {384, 32, 3, 256}, {512, 64, 2, 128},
                                          {768, 64, 3, 128}, {1024, 64, 4, 128}, {2048, 64, 8, 128}};
 };
 
