@@ -279,9 +279,9 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 //  * Up to 512 fp16 keys (256 fp32) both directions run best with a row on as few vectors
 //    per lane as fit a wave and one wave per workgroup: one 64-thread workgroup per row from
 //    256 fp16 keys, several rows per wave below. Against the earlier plans (two to four
-//    vectors per lane over 8-32 lanes in 256-thread workgroups): forward -2 to -4% at 64-512
-//    fp16 keys and -3 to -5% at 128-256 fp32 keys; backward -3.6% at 128 and 256 fp16 keys,
-//    -1 to -2% at 512 fp16 keys, -2 to -5% at 128-512 fp32 keys.
+//    vectors per lane over 8-32 lanes, or 128-256-thread workgroups): forward -1 to -4% at
+//    32-512 fp16 keys and -1 to -5% at 32-256 fp32 keys; backward -3 to -4% at 32-256 fp16
+//    keys, -1 to -2% at 512 fp16 keys, -2 to -5% at 32-512 fp32 keys.
 //  * Longer rows keep two to four vectors per lane in 256-thread workgroups, except the
 //    2048-key forwards, where 64-thread workgroups win (-1% fp16, -4% fp32); one wave per
 //    workgroup loses 1-6% at 384-1024 fp16 keys and 384-768 fp32 keys, and up to 5% in the
@@ -306,23 +306,23 @@ struct Plan {
 
 template <typename T> struct SoftmaxFwTable;
 template <> struct SoftmaxFwTable<f16> {   // V = 8
-    static constexpr Plan plans[] = {{32, 4, 1, 128},   {64, 8, 1, 64},    {128, 16, 1, 64},
+    static constexpr Plan plans[] = {{32, 4, 1, 64},   {64, 8, 1, 64},    {128, 16, 1, 64},
                                      {256, 32, 1, 64},  {384, 16, 3, 256}, {512, 64, 1, 64},
                                      {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 64}};
 };
 template <> struct SoftmaxFwTable<float> { // V = 4
-    static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 64},
+    static constexpr Plan plans[] = {{32, 8, 1, 64},   {64, 16, 1, 256},  {128, 32, 1, 64},
                                      {256, 64, 1, 64},  {384, 32, 3, 256}, {512, 32, 4, 256},
                                      {768, 64, 3, 256}, {1024, 64, 4, 256}, {2048, 64, 8, 64}};
 };
 template <typename T> struct SoftmaxBwTable;
 template <> struct SoftmaxBwTable<f16> {
-    static constexpr Plan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 64},
+    static constexpr Plan plans[] = {{32, 4, 1, 64},   {64, 8, 1, 64},   {128, 16, 1, 64},
                                      {256, 32, 1, 64},  {384, 16, 3, 256}, {512, 64, 1, 64},
                                      {768, 32, 3, 256}, {1024, 32, 4, 256}, {2048, 64, 4, 256}};
 };
 template <> struct SoftmaxBwTable<float> {
-    static constexpr Plan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 32, 1, 64},
+    static constexpr Plan plans[] = {{32, 8, 1, 64},   {64, 16, 1, 64},  {128, 32, 1, 64},
                                      {256, 64, 1, 64},  {384, 32, 3, 256}, {512, 64, 2, 64},
                                      {768, 64, 3, 128}, {1024, 64, 4, 256}, {2048, 64, 8, 128}};
 };

@@ -239,7 +239,7 @@ __global__ __launch_bounds__(WG) void softmax_bw_skip(T *dinp, const T *dout,
 // ------------------------------------------------------------------------------------------
 // Row-length buckets (G lanes per row, IT vectors per lane), the HW4 page's template list.
 // Measured on MI355X (old and new library alternating in one process): 64-thread workgroups
-// at fp16 256-1024 keys in the forward and 128-512 in the backward (forward -2 to -5%,
+// at fp16 32-64 and 256-1024 keys in the forward and 32-512 in the backward (forward -2 to -6%,
 // backward -2 to -13%, the most on the 32 MiB GPT-2 shape), fp32 128, 256 and 1024 keys in
 // the forward (-2 to -6%) and 256 in the backward (-3%); they lose or tie at 2048 keys
 // (+2-5%), in the fp16 1024-key backward (+3%) and at fp32 512 keys.
@@ -253,7 +253,7 @@ struct SkipPlan {
 
 template <typename T> struct SkipFwTable;
 template <> struct SkipFwTable<f16> {
-    static constexpr SkipPlan plans[] = {{32, 4, 1, 512},   {64, 8, 1, 512},   {128, 8, 2, 256},
+    static constexpr SkipPlan plans[] = {{32, 4, 1, 64},   {64, 8, 1, 64},   {128, 8, 2, 256},
                                          {256, 8, 4, 64},   {384, 16, 3, 256}, {512, 32, 2, 64},
                                          {768, 32, 3, 256}, {1024, 32, 4, 64}, {2048, 64, 4, 256}};
 };
@@ -264,7 +264,7 @@ template <> struct SkipFwTable<float> {
 };
 template <typename T> struct SkipBwTable;
 template <> struct SkipBwTable<f16> {
-    static constexpr SkipPlan plans[] = {{32, 4, 1, 256},   {64, 8, 1, 256},   {128, 16, 1, 64},
+    static constexpr SkipPlan plans[] = {{32, 4, 1, 64},   {64, 8, 1, 64},   {128, 16, 1, 64},
                                          {256, 32, 1, 64},  {384, 16, 3, 256}, {512, 64, 1, 64},
                                          {768, 32, 3, 256}, {1024, 64, 2, 128}, {2048, 64, 4, 128}};
 };
