@@ -310,9 +310,10 @@ LNR_API int attn_softmax_bw_skip(void *dinp, const void *dout, const void *out_f
 
 /*
  * cross_entropy_fw_workspace_bytes -- device workspace cross_entropy_fw needs for (N, V,
- * dtype): per-chunk partial (max, sum) pairs when there are too few rows to fill the GPU and
- * each row is split over several workgroups; 0 when rows are not split (the common case of
- * thousands of rows) and for an invalid shape/dtype.
+ * dtype): per-chunk partial (max, sum) pairs when rows are longer than 256 KB (V above 65536
+ * fp32 or 131072 fp16 logits) and there are too few of them to fill the GPU, so that each row
+ * is split over several workgroups; 0 when rows are not split (every shorter row, and the
+ * common case of thousands of rows) and for an invalid shape/dtype.
  */
 LNR_API size_t cross_entropy_fw_workspace_bytes(int64_t N, int64_t V, lnr_dtype dtype);
 
