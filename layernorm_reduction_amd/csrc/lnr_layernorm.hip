@@ -13,9 +13,12 @@
 //     crossing waves through LDS with one barrier pair). 128-bit loads and stores.
 //   * Forward: one read of x, one write of y, per-row mean and rstd in fp32. The variance
 //     from the one-pass sums is clamped at 0 before eps is added.
-//   * Backward, fused: each workgroup walks every P-th row (P workgroups). Because a lane
-//     owns the same columns in every row, it accumulates dgamma/dbeta column partials in
-//     registers while it computes dx, so x and dy are read from HBM exactly once. At the
+//   * Backward, fused: P workgroups (one per CU) sweep the rows in bands of P*NG consecutive
+//     rows, each taking NG consecutive rows of every band (NG row groups per workgroup), with
+//     one or two rows fetched ahead. Because a lane owns the same columns in every row, it
+//     accumulates dgamma/dbeta column partials in registers while it computes dx, so x and
+//     dy are read from HBM exactly once. The launch plan depends on the width and, at 1024
+//     fp16 columns, on the row count. At the
 //     end the workgroup's row groups are combined through an LDS column tile, in group
 //     order, and one partial row per workgroup goes to the workspace. A second small kernel
 //     sums the partials in a fixed order. No atomics: results are bitwise reproducible.
