@@ -150,7 +150,8 @@ LNR_API size_t layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtyp
  *   dy, x   [N, C] dtype, read.  gamma [C] dtype, read.
  *   mean, rstd [N] float32, read: the values layernorm_fw wrote for this x.
  *   workspace  device buffer of at least layernorm_bw_workspace_bytes(N, C, dtype) bytes,
- *              8-byte aligned, owned by the caller; its contents on entry do not matter.
+ *              16-byte aligned (LNR_ERR_ALIGN otherwise: the partial sums are written as
+ *              16-byte vectors), owned by the caller; its contents on entry do not matter.
  *   Limits: 1 <= C <= LNR_LAYERNORM_MAX_C; N >= 0.
  */
 LNR_API int layernorm_bw(void *dx, void *dgamma, void *dbeta, const void *dy, const void *x,
@@ -221,7 +222,7 @@ LNR_API size_t rmsnorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype dtype)
  *   dy, x   [N, C] dtype, read.  gamma [C] dtype, read.
  *   rstd    [N] float32, read: the values rmsnorm_fw wrote for this x.
  *   workspace  device buffer of at least rmsnorm_bw_workspace_bytes(N, C, dtype) bytes,
- *              8-byte aligned, owned by the caller; its contents on entry do not matter.
+ *              16-byte aligned, owned by the caller; its contents on entry do not matter.
  *   Limits: 1 <= C <= LNR_LAYERNORM_MAX_C; N >= 0.
  */
 LNR_API int rmsnorm_bw(void *dx, void *dgamma, const void *dy, const void *x, const void *gamma,
@@ -270,7 +271,7 @@ LNR_API size_t bdr_layernorm_bw_workspace_bytes(int64_t N, int64_t C, lnr_dtype 
  *   overlaps nothing.  dgamma, dbeta, dbias [C] dtype, written.
  *   dy, s [N, C] dtype, read.  ds_extra [N, C] dtype, read, or NULL (no other path into s).
  *   keep_mask, p as in the forward.  gamma [C] dtype; mean, rstd [N] float32, read.
- *   workspace  bdr_layernorm_bw_workspace_bytes(N, C, dtype) bytes, 8-byte aligned, caller
+ *   workspace  bdr_layernorm_bw_workspace_bytes(N, C, dtype) bytes, 16-byte aligned, caller
  *   owned; contents on entry do not matter; must not overlap any other argument.
  *   Limits and the choice of kernel as in the forward.
  */

@@ -164,6 +164,7 @@ def test_layernorm_bw_validation(lib):
     assert lbw(lib, mean=None) == NULL
     assert lbw(lib, x=A + 2 ** 31 + 1) == ALIGN
     assert lbw(lib, ws=A + 2 ** 34 + 4) == ALIGN
+    assert lbw(lib, ws=A + 2 ** 34 + 8) == ALIGN             # partials are 16-byte vectors
     need = lib.layernorm_bw_workspace_bytes(64, 64, F16)
     assert need > 0
     assert lbw(lib, ws_bytes=need - 1) == WS
@@ -234,6 +235,7 @@ def test_rmsnorm_bw_validation(lib):
     assert rbw(lib, dg=None) == NULL
     assert rbw(lib, rstd=None) == NULL
     assert rbw(lib, x=A + 2 ** 31 + 1) == ALIGN
+    assert rbw(lib, ws=A + 2 ** 34 + 8) == ALIGN
     need = lib.rmsnorm_bw_workspace_bytes(64, 64, F16)
     assert need > 0
     assert rbw(lib, ws_bytes=need - 1) == WS
@@ -331,6 +333,7 @@ def test_bdr_layernorm_bw_validation(lib):
     need = lib.bdr_layernorm_bw_workspace_bytes(64, 64, F16)
     assert need > 0                                          # vector path only: 3 slots per partial row
     assert bbw(lib, ws_bytes=need - 1) == WS
+    assert bbw(lib, ws=A + 2 ** 34 + 8) == ALIGN
     assert bbw(lib, dx=A + 64) == ALIAS                      # dx over dresidual
     assert bbw(lib, dr=A + 2 ** 30 + 128) == ALIAS           # dresidual partially over dy
     assert bbw(lib, dbias=A + 2 ** 29 + 2) == ALIAS          # dbias over dgamma
