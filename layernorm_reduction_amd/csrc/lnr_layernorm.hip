@@ -258,7 +258,7 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
                     // s = r + (x + b) * scale for a kept element (one fma: one rounding), r
                     // exactly for a dropped one; the element-wise kernel forms it the same way.
                     d[k][e] = ((kc[k] >> e) & 1u) ? __builtin_fmaf(d[k][e] + bs[k][e], keep_scale, rf[e]) : rf[e];
-                store16_or_drop(s_out + wrow * static_cast<int64_t>(C), off_of(k), pack16<T>(d[k]));
+                store16_or_drop<kBufferDeviceStream>(s_out + wrow * static_cast<int64_t>(C), off_of(k), pack16<T>(d[k]));
             }
 #pragma unroll
             for (int e = 0; e < V; ++e) {
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(WG) void layernorm_fw_vec(T *y, float *__restrict__
                 if (live && c < nvec)
                     store_stream<T>(y + row * static_cast<int64_t>(C) + static_cast<int64_t>(c) * V, o);
             } else {
-                store16_or_drop(y + wrow * static_cast<int64_t>(C), off_of(k), pack16<T>(o));
+                store16_or_drop<kBufferDeviceStream>(y + wrow * static_cast<int64_t>(C), off_of(k), pack16<T>(o));
             }
         }
         // One lane per row stores its statistics (RMSNorm: no mean).

@@ -83,17 +83,21 @@ __device__ __forceinline__ void store_stream(T *p, const float (&in)[Vec16<T>::N
 constexpr uint32_t kDropOffset = 0xFFFFFFF0u;
 constexpr int32_t kBufferRange = 0x7FFFFFFF;    // valid offsets stay below it
 constexpr int32_t kBufferDword3 = 0x00020000;   // untyped 32-bit data (gfx9 family)
-constexpr int kBufferNonTemporal = 2;           // cache policy bits of a streaming store
+constexpr int kBufferNonTemporal = 2;           // cache policy bits of a streaming access
+// Streaming stores at device scope (sc1 and nt). Measured on MI355X with one-shot 16-byte
+// streams: read one tensor and write one at 512 MiB, 161.3 -> 159.1-159.6 us; read two and
+// write one unchanged (243 us), and in the backward kernels 0.2-2.5% slower. So the forward
+// kernels (one read stream, one write stream) store this way and the backward kernels do not.
+constexpr int kBufferDeviceStream = 18;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *wave_base, int32_t range = kBufferRange) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(wave_base), 0, range, kBufferDword3);
 }
-template <typename RV>
+template <int POLICY = kBufferNonTemporal, typename RV>
 __device__ __forceinline__ void store16_or_drop(const void *wave_base, uint32_t off, const RV &v) {
     static_assert(sizeof(RV) == 16, "16-byte vectors");
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), wave_rsrc(wave_base), off, 0,
-                                           kBufferNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), wave_rsrc(wave_base), off, 0, POLICY);
 }
 // A 16-byte vector through the same kind of descriptor, non-temporal: a lane whose offset is
 // beyond the range (kDropOffset) reads zeros and touches no memory.

@@ -48,6 +48,11 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
     const bool live = row < rows;
     const int nvec = Tk / V;
     const int64_t base = static_cast<int64_t>(live ? row : 0u) * Tk;
+    static_assert(G <= 64, "a wave holds whole rows");
+    // The wave's first row (clamped to row 0 when the whole wave is past the end, where every
+    // store is dropped): the base of the branch-free stores at the end.
+    const uint32_t wave_row0 = row - (threadIdx.x % 64) / G;
+    const uint32_t wrow = wave_row0 < rows ? wave_row0 : 0u;
 
     // Scores and mask are loaded as stored, every load unconditional (an idle lane reads its
     // row's first vector; a row past the end reads row 0), so no branch makes the compiler
@@ -126,15 +131,21 @@ __global__ __launch_bounds__(WG) void softmax_fw_vec(T *out, const T *inp,
     // the result is far inside the tolerance.
     const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
 
+    // Branch-free stores at device scope, through a descriptor at the wave's first row: a lane
+    // with nothing to store (a row past the end, a vector slot past the row) passes an offset
+    // beyond the range and is dropped. Offsets stay below 64 rows of 2048 fp32 keys.
+    T *wave_out = out + static_cast<int64_t>(wrow) * Tk;
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
-        if (live && c < nvec) {
-            float y[V];
+        float y[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) y[e] = z[k][e] * inv;
-            store_stream<T>(out + base + static_cast<int64_t>(c) * V, y);
-        }
+        for (int e = 0; e < V; ++e) y[e] = z[k][e] * inv;
+        const uint32_t off = (live && c < nvec)
+                                 ? ((row - wrow) * static_cast<uint32_t>(Tk) + static_cast<uint32_t>(c * V)) *
+                                       static_cast<uint32_t>(sizeof(T))
+                                 : kDropOffset;
+        store16_or_drop<kBufferDeviceStream>(wave_out, off, pack16<T>(y));
     }
 }
 
