@@ -150,15 +150,23 @@ __global__ __launch_bounds__(WG) void softmax_fw_skip(T *out, const T *inp,
     s = group_allreduce<G>(s, OpSum());
     const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
 
+    // Every vector of the row is written (zeros at skipped keys), as in the dense forward:
+    // branch-free stores at device scope from the wave's row base, idle lanes dropped.
+    // Measured on MI355X against stores under a branch with the plain streaming policy:
+    // -3% at 32-64 keys, -0.6% at [64,16,512,512], +0.3 to +0.8% on long causal rows (the
+    // same branch-free stores without device scope were slower everywhere).
+    T *wave_out = out + static_cast<int64_t>(wrow) * Tk;
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
         const int c = k * G + lane;
-        if (live && c < nvec) {
-            float y[V];
+        float y[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) y[e] = z[k][e] * inv;
-            store_stream<T>(out + base + static_cast<int64_t>(c) * V, y);
-        }
+        for (int e = 0; e < V; ++e) y[e] = z[k][e] * inv;
+        const uint32_t off = (live && c < nvec)
+                                 ? ((r - wrow) * static_cast<uint32_t>(Tk) + static_cast<uint32_t>(c * V)) *
+                                       static_cast<uint32_t>(sizeof(T))
+                                 : kDropOffset;
+        store16_or_drop<kBufferDeviceStream>(wave_out, off, pack16<T>(y));
     }
 }
 
