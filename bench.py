@@ -88,6 +88,9 @@ PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc
            "-d $OUT/pmc_{kind}_{w} -o {w} -- python3 $REPO/bench.py{args}")
 DOMINANT = "softmax_bw_vec"
 COPY = "copy16"
+# Work-items of the 1 GiB calibration copy (`lnr_copy` moves one 16-byte vector per thread);
+# the same kernel also times the same-size ceilings, so counters keep only this launch.
+CALIB_GRID = (1 << 30) // 16
 SKIP_PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc {ctr} -f csv "
                 "-d $OUT/pmc_{kind}_skip -o skip -- python3 $REPO/bench.py --skip-traffic")
 
@@ -148,7 +151,7 @@ def summarize_skip_traffic(root_dir: str):
     import csv
     import collections
 
-    calib_grid = str((1 << 30) // 64)
+    calib_grid = str(CALIB_GRID)
 
     def per_kernel(kind):
         path = os.path.join(root_dir, f"pmc_{kind}_skip", "skip_counter_collection.csv")
@@ -302,8 +305,7 @@ def summarize_profiles(root_dir: str, workload: str):
     with open(os.path.join(out_dir, f"{workload}_kernel_trace.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
-    # The 1 GiB calibration copy: 2^30 / 16 bytes per thread-vector / 4 vectors per thread.
-    calib_grid = str((1 << 30) // 64)
+    calib_grid = str(CALIB_GRID)
 
     def per_kernel(kind):
         path = os.path.join(root_dir, f"pmc_{kind}_{workload}", f"{workload}_counter_collection.csv")
