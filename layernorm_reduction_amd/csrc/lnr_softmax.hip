@@ -293,9 +293,13 @@ __global__ __launch_bounds__(kGenericWG) void softmax_bw_generic(T *dinp, const 
 //    vectors per lane over 8-32 lanes, or 128-256-thread workgroups): forward -1 to -4% at
 //    32-512 fp16 keys and -1 to -5% at 32-256 fp32 keys; backward -3 to -4% at 32-256 fp16
 //    keys, -1 to -2% at 512 fp16 keys, -2 to -5% at 32-512 fp32 keys.
+//  * The fp32 512-key forward takes one row per 64-thread workgroup with two vectors per
+//    lane: with the branch-free device-scope stores it runs 2-4.5% faster than four vectors
+//    over 32 lanes in 256-thread workgroups (before those stores the two tied).
 //  * Longer rows keep two to four vectors per lane in 256-thread workgroups, except the
 //    2048-key forwards, where 64-thread workgroups win (-1% fp16, -4% fp32); one wave per
-//    workgroup loses 1-6% at 384-1024 fp16 keys and 384-768 fp32 keys, and up to 5% in the
+//    workgroup loses 1-6% at 384-1024 fp16 keys and 384-768 fp32 keys (re-measured with the
+//    device-scope stores: +2 to +4%), and up to 5% in the
 //    fp32 backward from 1024 keys. fp16 1024 keys take four vectors over 32 lanes in the
 //    backward (-4% against one vector per lane), fp16 2048 and fp32 1024 keys 256-thread
 //    workgroups (-4%, -5%).
@@ -323,7 +327,7 @@ template <> struct SoftmaxFwTable<f16> {   // V = 8
 };
 template <> struct SoftmaxFwTable<float> { // V = 4
     static constexpr Plan plans[] = {{32, 8, 1, 64},   {64, 16, 1, 256},  {128, 32, 1, 64},
-                                     {256, 64, 1, 64},  {384, 32, 3, 256}, {512, 32, 4, 256},
+                                     {256, 64, 1, 64},  {384, 32, 3, 256}, {512, 64, 2, 64},
                                      {768, 64, 3, 256}, {1024, 64, 4, 256}, {2048, 64, 8, 64}};
 };
 template <typename T> struct SoftmaxBwTable;
