@@ -18,10 +18,10 @@
 //     one or two rows fetched ahead. Because a lane owns the same columns in every row, it
 //     accumulates dgamma/dbeta column partials in registers while it computes dx, so x and
 //     dy are read from HBM exactly once. The launch plan depends on the width and, at 1024
-//     fp16 columns, on the row count. At the
-//     end the workgroup's row groups are combined through an LDS column tile, in group
-//     order, and one partial row per workgroup goes to the workspace. A second small kernel
-//     sums the partials in a fixed order. No atomics: results are bitwise reproducible.
+//     fp16 columns, on the row count. At the end the workgroup's row groups are combined in
+//     group order (through LDS when there are several) into one partial row per workgroup,
+//     written to the workspace as 16-byte vectors. A second small kernel sums the partials
+//     in a fixed order. No atomics: results are bitwise reproducible.
 //     Partials are fp32 for fp16 storage and fp64 for fp32 storage, so the long column sums
 //     over tens of thousands of rows add no rounding beyond the per-element products.
 //   * RMSNorm ("FastTransformer: Breaking the Compiler Ceiling via Architectural
