@@ -81,7 +81,6 @@ __global__ __launch_bounds__(WG) void softmax_fw_skip(T *out, const T *inp,
     const bool live = row < rows;
     const uint32_t r = live ? row : 0u;
     const int nvec = Tk / V;
-    const int64_t base = static_cast<int64_t>(r) * Tk;
     // Keys [0, kend) may be attended to: all of them, or 0..query index when causal (Tq = Tk).
     const int qi = static_cast<int>(r - divu32(r, per_query) * per_query.d);
     const int kend = causal ? qi + 1 : Tk;
