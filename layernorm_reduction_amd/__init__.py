@@ -319,8 +319,8 @@ def layernorm_bw_workspace_bytes(N: int, C: int, dtype) -> int:
 def layernorm_bw(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None, workspace=None):
     """LayerNorm backward; returns (dx, dgamma, dbeta).
 
-    workspace: a uint8 GPU tensor of at least layernorm_bw_workspace_bytes(N, C, dtype) bytes;
-    allocated here when not given.
+    workspace: a uint8 GPU tensor of at least layernorm_bw_workspace_bytes(N, C, dtype) bytes,
+    16-byte aligned (a fresh allocation is); allocated here when not given.
     """
     torch = _torch()
     _dev(x, "x")
@@ -425,8 +425,8 @@ def rmsnorm_bw_workspace_bytes(N: int, C: int, dtype) -> int:
 def rmsnorm_bw(dy, x, gamma, rstd, dx=None, dgamma=None, workspace=None):
     """RMSNorm backward; returns (dx, dgamma).
 
-    workspace: a uint8 GPU tensor of at least rmsnorm_bw_workspace_bytes(N, C, dtype) bytes;
-    allocated here when not given.
+    workspace: a uint8 GPU tensor of at least rmsnorm_bw_workspace_bytes(N, C, dtype) bytes,
+    16-byte aligned; allocated here when not given.
     """
     torch = _torch()
     _dev(x, "x")
@@ -512,7 +512,9 @@ def bdr_layernorm_fw(x, residual, bias, keep_mask, p, gamma, beta, eps: float = 
 def bdr_layernorm_bw(dy, s, keep_mask, p, gamma, mean, rstd, ds_extra=None, dresidual=None,
                      dx=None, dgamma=None, dbeta=None, dbias=None, workspace=None):
     """Backward of bdr_layernorm_fw from the saved s, mean, rstd; ds_extra is a gradient
-    reaching s by another path (None: none). Returns (dresidual, dx, dgamma, dbeta, dbias)."""
+    reaching s by another path (None: none). Returns (dresidual, dx, dgamma, dbeta, dbias).
+    workspace: a uint8 GPU tensor of at least bdr_layernorm_bw_workspace_bytes(N, C, dtype)
+    bytes, 16-byte aligned; allocated here when not given."""
     torch = _torch()
     _dev(s, "s")
     if s.dim() != 2:
