@@ -248,8 +248,9 @@ __global__ __launch_bounds__(WG) void softmax_bw_skip(T *dinp, const T *dout,
 // Measured on MI355X (old and new library alternating in one process): 64-thread workgroups
 // at fp16 32-64 and 256-1024 keys in the forward and 32-512 in the backward (forward -2 to -6%,
 // backward -2 to -13%, the most on the 32 MiB GPT-2 shape), fp32 128, 256 and 1024 keys in
-// the forward (-2 to -6%) and 256 in the backward (-3%); they lose or tie at 2048 keys
-// (+2-5%), in the fp16 1024-key backward (+3%) and at fp32 512 keys.
+// the forward (-2 to -6%) and 256 in the backward (-3%), and fp32 512 keys in the forward once
+// its stores became branch-free at device scope (-1.2%); they lose or tie at 2048 keys
+// (+2-5%) and in the fp16 1024-key backward (+3%).
 // ------------------------------------------------------------------------------------------
 struct SkipPlan {
     int bucket;
@@ -266,7 +267,7 @@ template <> struct SkipFwTable<f16> {
 };
 template <> struct SkipFwTable<float> {
     static constexpr SkipPlan plans[] = {{32, 8, 1, 256},   {64, 16, 1, 256},  {128, 8, 4, 64},
-                                         {256, 16, 4, 64},  {384, 32, 3, 256}, {512, 32, 4, 256},
+                                         {256, 16, 4, 64},  {384, 32, 3, 256}, {512, 32, 4, 64},
                                          {768, 64, 3, 256}, {1024, 64, 4, 64},  {2048, 64, 8, 256}};
 };
 template <typename T> struct SkipBwTable;
