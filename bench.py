@@ -473,7 +473,8 @@ def table_cases():
 
 def run_table(match: str = "", warm: bool = False):
     """Back-to-back launches of each op over rotating buffers (>= 1 GiB footprint): average
-    per launch from one event pair around the batch, plus the kernel's own min / median / p90
+    per launch from one event pair around a batch (the median of five batches), plus the
+    kernel's own min / median / p90
     duration from events the kernel records (first kernel only for layernorm_bw).
 
     Beside each op, the same-size streaming ceiling: the library's 16-byte non-temporal copy
@@ -497,17 +498,25 @@ def run_table(match: str = "", warm: bool = False):
     g.manual_seed(1234)
     reps = 30
 
-    def timed(calls):
+    rounds = 5  # each back-to-back figure is the median of this many batches of `reps`
+
+    def b2b_median(calls):
         for c in calls[:3]:
             c()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(reps):
-            calls[i % len(calls)]()
-        b.record()
-        torch.cuda.synchronize()
-        b2b = a.elapsed_time(b) * 1e3 / reps
+        per = []
+        for _ in range(rounds):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                calls[i % len(calls)]()
+            b.record()
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / reps)
+        return statistics.median(per)
+
+    def timed(calls):
+        b2b = b2b_median(calls)
         ka, kb = hev.create(reps), hev.create(reps)
         for i in range(reps):
             hook(ka[i], kb[i])
@@ -528,18 +537,7 @@ def run_table(match: str = "", warm: bool = False):
         bufs = [[torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(3)] for _ in range(n)]
         cp = [(lambda b=b: lnr.copy_bytes(b[2], b[0])) for b in bufs]
         xr = [(lambda b=b: lnr.xor_bytes(b[2], b[0], b[1])) for b in bufs]
-        out = []
-        for calls in (cp, xr):
-            for c in calls[:3]:
-                c()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for i in range(reps):
-                calls[i % len(calls)]()
-            b.record()
-            torch.cuda.synchronize()
-            out.append(a.elapsed_time(b) * 1e3 / reps)
+        out = [b2b_median(calls) for calls in (cp, xr)]
         del bufs
         torch.cuda.empty_cache()
         return out
