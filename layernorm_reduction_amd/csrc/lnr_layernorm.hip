@@ -450,6 +450,12 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     constexpr bool DEFER = DEPTH == 1 && G <= 64 && IT <= 2 && !BDR;
     const int64_t iters = (rows_per_block + NG - 1) / NG;
     auto row_of = [&](int64_t it) { return (it * P + first_row) * NG + grp; };
+    // Statistics as scalar loads where a row covers whole waves and a row iteration carries
+    // enough work to cover their latency, which the next LDS wait exposes (scalar loads and
+    // LDS share one counter). Measured on MI355X, bitwise-equal outputs: fp32 8192 columns
+    // -6%, 2048 -4%, 1024 -1%, fp16 1024-8192 -0.3 to -1.5%; with one vector per lane and
+    // one row ahead (fp32 4096 columns, 16 waves per row) +2.5 to +4.5%, so not there.
+    constexpr bool kScalarStats = G >= 64 && (IT >= 2 || DEPTH == 2);
     auto fetch = [&](RowBuf &b, int64_t it) {
         const int64_t row = row_of(it);
         const bool live = it < iters && row < N;
@@ -481,11 +487,28 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
         // The stats come as loaded, with no select after the load: a select on a loaded value
         // makes the compiler wait for every memory operation in flight at that point. mean is
         // NULL in RMSNorm mode and is never dereferenced there.
-        b.rs = *(live ? rstd + row : reinterpret_cast<const float *>(zero16<T>(3)));
-        if constexpr (!RMS)
-            b.mu = *(live ? mean + row : reinterpret_cast<const float *>(zero16<T>(2)));
-        else
-            b.mu = 0.f;
+        if constexpr (kScalarStats) {
+            // A wave holds part of one row: its stats are read through the constant address
+            // space at a wave-uniform address, i.e. as scalar loads, which neither queue
+            // behind the row's vector loads nor hold its vector-memory waits.
+            using CF = const __attribute__((address_space(4))) float;
+            const int64_t urow = (it * P + first_row) * NG + __builtin_amdgcn_readfirstlane(grp);
+            const bool ulive = it < iters && urow < N;
+            const float *prs = ulive ? rstd + urow : reinterpret_cast<const float *>(zero16<T>(3));
+            b.rs = *reinterpret_cast<CF *>(reinterpret_cast<uintptr_t>(prs));
+            if constexpr (!RMS) {
+                const float *pmu = ulive ? mean + urow : reinterpret_cast<const float *>(zero16<T>(2));
+                b.mu = *reinterpret_cast<CF *>(reinterpret_cast<uintptr_t>(pmu));
+            } else {
+                b.mu = 0.f;
+            }
+        } else {
+            b.rs = *(live ? rstd + row : reinterpret_cast<const float *>(zero16<T>(3)));
+            if constexpr (!RMS)
+                b.mu = *(live ? mean + row : reinterpret_cast<const float *>(zero16<T>(2)));
+            else
+                b.mu = 0.f;
+        }
     };
     // Every store is branch-free (store16_or_drop): offsets count from the row of the wave's
     // first row group, and a lane with nothing to store (a row past the end, or a vector slot
