@@ -454,7 +454,7 @@ __global__ __launch_bounds__(WG) void layernorm_bw_vec(T *dx, typename Accum<T>:
     // enough work to cover their latency, which the next LDS wait exposes (scalar loads and
     // LDS share one counter). Measured on MI355X, bitwise-equal outputs: fp32 8192 columns
     // -6%, 2048 -4%, 1024 -1%, fp16 1024-8192 -0.3 to -1.5%; with one vector per lane and
-    // one row ahead (fp32 4096 columns, 16 waves per row) +2.5 to +4.5%, so not there.
+    // one row ahead (a plan of 16 waves per row at fp32 4096 columns) +2.5 to +4.5%.
     constexpr bool kScalarStats = G >= 64 && (IT >= 2 || DEPTH == 2);
     auto fetch = [&](RowBuf &b, int64_t it) {
         const int64_t row = row_of(it);
@@ -1098,7 +1098,9 @@ template <> struct LnFwTable<float> {  // V = 4
 // over four or eight waves likewise take two rows ahead in 512-thread workgroups instead of
 // one row ahead in 1024-thread ones: fp16 2048 columns -7 to -8%, fp32 1024 columns -4%,
 // fp32 2048 columns -5 to -6% (16384 and 32768 rows); at fp32 512 columns two waves with two
-// rows ahead lose (+4%) to the one-wave plan.
+// rows ahead lose (+4%) to the one-wave plan. fp32 4096 columns take two vectors per lane over
+// eight waves with one row ahead (-4 to -6% against one vector over sixteen waves in 1024
+// threads, -2 to -3% against two rows ahead); at 8192 two rows ahead spill (2.3x slower).
 template <typename T> struct LnBwTable;
 template <> struct LnBwTable<f16> {
     static constexpr LnPlan plans[] = {
@@ -1111,7 +1113,7 @@ template <> struct LnBwTable<float> {
     static constexpr LnPlan plans[] = {
         {64, 16, 1, 512, 1},     {128, 32, 1, 512, 1},    {256, 64, 1, 512, 1},
         {512, 64, 2, 512, 1},    {768, 64, 3, 512, 1},    {1024, 256, 1, 512, 2},
-        {2048, 512, 1, 512, 2},  {4096, 1024, 1, 1024, 1}, {8192, 1024, 2, 1024, 1}};
+        {2048, 512, 1, 512, 2},  {4096, 512, 2, 512, 1}, {8192, 1024, 2, 1024, 1}};
 };
 
 // Backward plans of the fused bias-dropout-residual LayerNorm. Its third column partial
