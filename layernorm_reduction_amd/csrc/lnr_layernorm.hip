@@ -17,8 +17,8 @@
 //     rows, each taking NG consecutive rows of every band (NG row groups per workgroup), with
 //     one or two rows fetched ahead. Because a lane owns the same columns in every row, it
 //     accumulates dgamma/dbeta column partials in registers while it computes dx, so x and
-//     dy are read from HBM exactly once. The launch plan depends on the width and, at 1024
-//     fp16 columns, on the row count. At the end the workgroup's row groups are combined in
+//     dy are read from HBM exactly once. The launch plan depends on the width (a plan may
+//     also require a minimum row count). At the end the workgroup's row groups are combined in
 //     group order (through LDS when there are several) into one partial row per workgroup,
 //     written to the workspace as 16-byte vectors. A second small kernel sums the partials
 //     in a fixed order. No atomics: results are bitwise reproducible.
@@ -1089,12 +1089,12 @@ template <> struct LnFwTable<float> {  // V = 4
 // The backward row kernel runs within 2-11% of a read-two-write-one stream of the same size
 // (N = 16384..32768). Up to 1024 columns (fp16) and 512 (fp32) a row sits inside one wave and
 // its dx stores are deferred (DEFER in the kernel): with that, two vectors per lane over 512
-// threads beat a row over two waves at fp16 1024 columns up to 16384 rows (-0.5 to -2.4%) and
+// threads beat a row over two waves at fp16 1024 columns (-0.5 to -2.4% up to 16384 rows) and
 // at fp32 512 columns (-9%). Four fp32 vectors per lane at 1024 columns spill and lose (+3%).
-// Longer fp16 launches at 1024 columns take a row over two waves with two rows fetched ahead:
-// each load instruction of the workgroup then covers four whole consecutive rows (8 KB), and
-// the deeper prefetch hides the cross-wave reduction (measured in one process against the
-// one-wave plan: 24576 rows -4.4%, 32768 -3.6%, 65536 -7.2%; 16384 +2.5%). Rows of 4-8 KB
+// A row over two waves with two rows ahead once won at 1024 fp16 columns from 24576 rows
+// (-3.6 to -7.2%); since the one-wave rows fetch aligned (a bare barrier per row) and read
+// their statistics as scalar loads, the one-wave plan is 1.1-1.4% faster at 24576-65536 rows
+// too, and no plan depends on the row count (min_rows stays available). Rows of 4-8 KB
 // over four or eight waves likewise take two rows ahead in 512-thread workgroups instead of
 // one row ahead in 1024-thread ones: fp16 2048 columns -7 to -8%, fp32 1024 columns -4%,
 // fp32 2048 columns -5 to -6% (16384 and 32768 rows); at fp32 512 columns two waves with two
@@ -1105,8 +1105,8 @@ template <typename T> struct LnBwTable;
 template <> struct LnBwTable<f16> {
     static constexpr LnPlan plans[] = {
         {64, 8, 1, 512, 1},      {128, 16, 1, 512, 1},    {256, 32, 1, 512, 1},
-        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 128, 1, 512, 2, 24576},
-        {1024, 64, 2, 512, 1},   {2048, 256, 1, 512, 2},  {4096, 256, 2, 512, 2},
+        {512, 64, 1, 512, 1},    {768, 32, 3, 512, 1},    {1024, 64, 2, 512, 1},
+        {2048, 256, 1, 512, 2},  {4096, 256, 2, 512, 2},
         {8192, 512, 2, 512, 2}};
 };
 template <> struct LnBwTable<float> {

@@ -155,10 +155,9 @@ def test_backward_odd_row_loop_trip_counts(N, C, dtype):
 
 
 @pytest.mark.parametrize("N,C", gpu_cases.NORM_LONG_F16)
-def test_long_launch_plan(N, C):
-    _, G, IT, _, _ = lnr.layernorm_plan(N, C, lnr.LNR_F16, backward=True)
-    _, G_short, _, _, _ = lnr.layernorm_plan(16384, C, lnr.LNR_F16, backward=True)
-    assert G > 64 >= G_short, (G, IT, G_short)   # a row over two waves, not inside one
+def test_long_ragged_launch(N, C):
+    """Long launches with a ragged row count (not whole row groups, a partial last band), at a
+    width with idle lanes and at the bucket's full width."""
     case = W.layernorm_case(f"long-N{N}-C{C}", N, C, dtype=torch.float16, seed_base=7900 + C,
                             row_offset_var=1.0)
     run_ln(case)

@@ -121,9 +121,8 @@ def test_backward_odd_row_loop_trip_counts(N, C, dtype):
 
 
 @pytest.mark.parametrize("N,C", gpu_cases.NORM_LONG_F16)
-def test_long_launch_plan(N, C):
-    """The backward's long-launch plan (a row over two waves, two rows fetched ahead) with
-    ragged row counts: see the LayerNorm test of the same name."""
+def test_long_ragged_launch(N, C):
+    """Long launches with ragged row counts: see the LayerNorm test of the same name."""
     case = W.layernorm_case(f"rms-long-N{N}-C{C}", N, C, dtype=torch.float16, seed_base=7950 + C,
                             row_offset_var=1.0, eps=W.RMS_EPS)
     run_rms(case)

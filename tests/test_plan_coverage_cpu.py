@@ -23,8 +23,9 @@ def norm_buckets(dtype, backward):
             for c in range(1, lnr.LAYERNORM_MAX_C + 1)} - {0}
 
 
-# Row counts at which a bucket's plan may change (the backward's long-launch plans start at
-# 24576 rows); every (bucket, lanes, vectors, workgroup) instantiation a launch can take.
+# Row counts at which a bucket's plan may change (a plan table may list plans taken only from
+# some launch length on); every (bucket, lanes, vectors, workgroup) instantiation a launch can
+# take.
 PLAN_ROWS = (64, 16384, 24576, 32768, 65536)
 
 
@@ -95,14 +96,16 @@ def test_norm_gpu_cases_reach_every_plan():
                 assert not missing, (name, dt, bw, sorted(missing))
 
 
-def test_long_launch_plans_exist_and_are_reached():
-    """The fp16 backward changes plan at 24576 rows at 1024 columns; the GPU's long-launch
-    cases sit above that row count and in that bucket."""
-    short = lnr.layernorm_plan(16384, 1024, F16, backward=True)[:4]
-    long = lnr.layernorm_plan(24576, 1024, F16, backward=True)[:4]
-    assert short != long and short[0] == long[0] == 1024
-    for n, c in gpu_cases.NORM_LONG_F16:
-        assert lnr.layernorm_plan(n, c, F16, backward=True)[:4] == long
+def test_row_count_dependent_plans_are_reached_by_long_cases():
+    """Where a bucket's backward plan changes with the row count (between PLAN_ROWS), the
+    GPU's long-launch cases reach the plan of the longest launches in that bucket."""
+    long_reached = reached_norm(gpu_cases.NORM_LONG_F16, F16, True)
+    for c in sorted(norm_buckets(F16, True)):
+        plans = [lnr.layernorm_plan(n, c, F16, backward=True)[:4] for n in PLAN_ROWS[1:]]
+        if len(set(plans)) > 1:
+            assert plans[-1] in long_reached, (c, plans)
+    for n, _ in gpu_cases.NORM_LONG_F16:
+        assert n > PLAN_ROWS[2], n
 
 
 def test_bdr_edge_widths_take_its_vector_path():
