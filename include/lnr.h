@@ -20,7 +20,9 @@
  *     is binary32. fp16 results are rounded to nearest even.
  *   - Tensors are dense, row-major, C-contiguous device buffers (hipMalloc'd or any
  *     device-accessible memory). The caller owns every buffer; the library allocates and
- *     frees nothing and keeps no state between calls, so calls are re-entrant.
+ *     frees nothing and keeps no state between calls, so calls are re-entrant. Two
+ *     exceptions, each described at its declaration: layernorm_bw_noalloc's fixed device
+ *     array (one per GPU, shared by its calls) and lnr_time_next_launch's per-thread request.
  *   - `stream` is a hipStream_t passed as void* (NULL means the default stream). Every call
  *     only enqueues work on that stream and returns; nothing synchronises.
  *   - Every argument is checked before anything is enqueued. A failed check returns a
@@ -32,10 +34,10 @@
  *   - Sizes of zero are legal and enqueue nothing, except the normalisation backwards
  *     (layernorm_bw, rmsnorm_bw, bdr_layernorm_bw), which still write zero parameter
  *     gradients when N == 0.
- *   - Any buffer may start at any address aligned to its element size. Rows whose byte
- *     length is a multiple of 16 and buffers aligned to 16 bytes take the 128-bit vector
- *     kernels; anything else takes a slower element-wise kernel with identical results
- *     up to rounding order.
+ *   - Any tensor may start at any address aligned to its element size (each workspace
+ *     states its own alignment). Rows whose byte length is a multiple of 16 and buffers
+ *     aligned to 16 bytes take the 128-bit vector kernels; anything else takes a slower
+ *     element-wise kernel with identical results up to rounding order.
  */
 #ifndef LNR_H
 #define LNR_H
@@ -58,9 +60,9 @@ typedef enum {
     LNR_ERR_SHAPE = 2,       /* a size is negative / zero where it may not be, or causal with Tq != Tk */
     LNR_ERR_UNSUPPORTED = 3, /* row length beyond LNR_SOFTMAX_MAX_TK or LNR_LAYERNORM_MAX_C */
     LNR_ERR_DTYPE = 4,       /* dtype is not an lnr_dtype value */
-    LNR_ERR_ALIGN = 5,       /* a pointer is not aligned to its element size */
+    LNR_ERR_ALIGN = 5,       /* a pointer below its element size's alignment, or a workspace below its stated one */
     LNR_ERR_ALIAS = 6,       /* buffers overlap in a way the operation forbids */
-    LNR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than layernorm_bw_workspace_bytes() */
+    LNR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the matching *_workspace_bytes() */
     LNR_ERR_HIP = 8,         /* the HIP runtime rejected a launch */
     LNR_ERR_SCRATCH = 9      /* the shape needs more than the library's fixed scratch array */
 } lnr_status;

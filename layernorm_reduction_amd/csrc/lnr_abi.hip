@@ -101,9 +101,9 @@ extern "C" const char *lnr_strerror(int status) {
         case LNR_ERR_SHAPE: return "invalid size (negative or zero where not allowed, or causal with Tq != Tk)";
         case LNR_ERR_UNSUPPORTED: return "row length or grid beyond the supported range";
         case LNR_ERR_DTYPE: return "dtype is not LNR_F32 or LNR_F16";
-        case LNR_ERR_ALIGN: return "pointer not aligned to its element size";
+        case LNR_ERR_ALIGN: return "pointer not aligned to its element size, or workspace not to its stated alignment";
         case LNR_ERR_ALIAS: return "buffers overlap in a way the operation forbids";
-        case LNR_ERR_WORKSPACE: return "workspace missing or smaller than layernorm_bw_workspace_bytes()";
+        case LNR_ERR_WORKSPACE: return "workspace missing or smaller than the matching *_workspace_bytes()";
         case LNR_ERR_HIP: return "the HIP runtime rejected a kernel launch";
         case LNR_ERR_SCRATCH: return "the shape needs more than the library's fixed scratch array (LNR_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
