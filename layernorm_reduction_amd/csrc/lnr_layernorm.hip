@@ -1071,14 +1071,21 @@ struct LnPlan {
 // 6-12% faster than one row; at 1024 fp16 columns one row is 3-8% faster than two). fp32 at
 // 1024 columns is a tie and keeps two. At 8192 fp16 columns the forward takes four vectors
 // per lane over four waves. At 1024 fp16 columns four rows per 256-thread workgroup beat two
-// per 128 threads by 1-2% (64, 512 and 1024 threads: tie, tie, 8% slower). The same plans
-// serve RMSNorm and the bias-dropout-residual LayerNorm.
+// per 128 threads by 1-2% (64, 512 and 1024 threads: tie, tie, 8% slower). At 4096 fp16
+// columns, launches of 24576 rows and more take two rows side by side in 512-thread
+// workgroups: same arithmetic per row (bitwise-equal outputs), LayerNorm 0.3-4.9% faster at
+// 24576-65536 rows and RMSNorm up to 10% at 65536, the bias-dropout-residual forward unchanged;
+// below 24576 rows it is 0.4-1.5% slower. The same doubling loses at 1024 and 8192 fp16
+// columns (+1-18%) and in every fp32 bucket; two waves per row with four vectors per lane
+// gains more for LayerNorm at 4096 but costs RMSNorm and the bias-dropout-residual forward
+// 6-7%. The same plans serve RMSNorm and the bias-dropout-residual LayerNorm.
 template <typename T> struct LnFwTable;
 template <> struct LnFwTable<f16> {  // V = 8
     static constexpr LnPlan plans[] = {
         {64, 8, 1, 256, 1},     {128, 16, 1, 256, 1},   {256, 16, 2, 256, 1},
         {512, 32, 2, 256, 1},   {768, 32, 3, 64, 1},    {1024, 64, 2, 256, 1},
-        {2048, 128, 2, 128, 1}, {4096, 256, 2, 256, 2}, {8192, 256, 4, 256, 2}};
+        {2048, 128, 2, 128, 1}, {4096, 256, 2, 512, 2, 24576}, {4096, 256, 2, 256, 2},
+        {8192, 256, 4, 256, 2}};
 };
 template <> struct LnFwTable<float> {  // V = 4
     static constexpr LnPlan plans[] = {
@@ -1094,7 +1101,7 @@ template <> struct LnFwTable<float> {  // V = 4
 // A row over two waves with two rows ahead once won at 1024 fp16 columns from 24576 rows
 // (-3.6 to -7.2%); since the one-wave rows fetch aligned (a bare barrier per row) and read
 // their statistics as scalar loads, the one-wave plan is 1.1-1.4% faster at 24576-65536 rows
-// too, and no plan depends on the row count (min_rows stays available). Rows of 4-8 KB
+// too, and no backward plan depends on the row count. Rows of 4-8 KB
 // over four or eight waves likewise take two rows ahead in 512-thread workgroups instead of
 // one row ahead in 1024-thread ones: fp16 2048 columns -7 to -8%, fp32 1024 columns -4%,
 // fp32 2048 columns -5 to -6% (16384 and 32768 rows); at fp32 512 columns two waves with two

@@ -9,8 +9,8 @@ NORM_EDGE_C = [1, 2, 8, 24, 64, 100, 128, 200, 264, 768, 1000, 1024, 1536, 2048,
 
 # Long launches (fp16, beyond 24576 rows, the row count from which a plan table may list
 # row-count-dependent plans): ragged row counts (not whole row groups, a partial last band) at
-# a width with idle lanes and at the bucket's full width.
-NORM_LONG_F16 = [(24577, 1000), (24579, 1024)]
+# widths with idle lanes and at a bucket's full width.
+NORM_LONG_F16 = [(24577, 1000), (24579, 1024), (24581, 4000)]
 
 # Softmax row lengths: every bucket of the template list at fp16 and fp32, its neighbours,
 # and odd lengths (element-wise kernel).

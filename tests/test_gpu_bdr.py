@@ -121,6 +121,13 @@ def test_hidden_sizes_fp16(C):
     run_bdr(W.bdr_case(f"bdr-16384x{C}-f16", 16384, C, dtype=torch.float16, seed_base=9100 + C))
 
 
+def test_long_ragged_launch():
+    """A long launch (beyond 24576 rows, where the forward's plan at 4096 fp16 columns changes)
+    with a ragged row count, at a width with idle lanes."""
+    run_bdr(W.bdr_case("bdr-long-24581x4000-f16", 24581, 4000, dtype=torch.float16, seed_base=9600),
+            chain=False)
+
+
 @pytest.mark.parametrize("C", [1024, 8192])
 def test_fp32(C):
     # C = 8192 fp32 is the plan whose backward spills part of its fp64 partials to scratch

@@ -77,9 +77,9 @@ def test_norm_gpu_cases_reach_every_plan():
     ln = {F16: edge | {(8192, 256)} | sweep | w5 | long16, F32: edge | {(64, 64)} | w5}
     # RMSNorm: the page's model shape [8192,256] (both), the sweep (fp16), [32768,1024] fp32
     rms = {F16: edge | {(8192, 256)} | sweep | long16, F32: edge | {(8192, 256), (32768, 1024)}}
-    # bias + dropout + residual: [8192,256] and [16384, 768/1024/4096] fp16, [8192,1024] and
-    # [2048,8192] fp32, its edge widths at 1, 7 and 1031 rows
-    bdr = {F16: {(8192, 256), (16384, 768), (16384, 1024), (16384, 4096)}
+    # bias + dropout + residual: [8192,256], [16384, 768/1024/4096] and the long [24581,4000]
+    # fp16, [8192,1024] and [2048,8192] fp32, its edge widths at 1, 7 and 1031 rows
+    bdr = {F16: {(8192, 256), (16384, 768), (16384, 1024), (16384, 4096), (24581, 4000)}
            | {(n, c) for d, c in gpu_cases.BDR_EDGE if d == "fp16" for n in (1, 7, 1031)},
            F32: {(8192, 1024), (2048, 8192)}
            | {(n, c) for d, c in gpu_cases.BDR_EDGE if d == "fp32" for n in (1, 7, 1031)}}
@@ -97,13 +97,15 @@ def test_norm_gpu_cases_reach_every_plan():
 
 
 def test_row_count_dependent_plans_are_reached_by_long_cases():
-    """Where a bucket's backward plan changes with the row count (between PLAN_ROWS), the
-    GPU's long-launch cases reach the plan of the longest launches in that bucket."""
-    long_reached = reached_norm(gpu_cases.NORM_LONG_F16, F16, True)
-    for c in sorted(norm_buckets(F16, True)):
-        plans = [lnr.layernorm_plan(n, c, F16, backward=True)[:4] for n in PLAN_ROWS[1:]]
-        if len(set(plans)) > 1:
-            assert plans[-1] in long_reached, (c, plans)
+    """Where a bucket's forward or backward plan changes with the row count (between
+    PLAN_ROWS), the GPU's long-launch cases reach the plan of the longest launches in that
+    bucket."""
+    for bw in (False, True):
+        long_reached = reached_norm(gpu_cases.NORM_LONG_F16, F16, bw)
+        for c in sorted(norm_buckets(F16, bw)):
+            plans = [lnr.layernorm_plan(n, c, F16, backward=bw)[:4] for n in PLAN_ROWS[1:]]
+            if len(set(plans)) > 1:
+                assert plans[-1] in long_reached, (bw, c, plans)
     for n, _ in gpu_cases.NORM_LONG_F16:
         assert n > PLAN_ROWS[2], n
 
