@@ -13,6 +13,9 @@ cast to the storage dtype; the oracle reads the cast values):
     per-row offset N(0,4) has standard deviation 2 and beta N(0,0.1) has std sqrt(0.1).
   * A valid length "U[a,b]" is an integer drawn uniformly from a..b inclusive, one per
     batch entry; key positions j >= L_b get an additive mask value of -inf, the rest 0.
+  * Tensors beyond 4 GiB (the large-tensor tests) are drawn on the GPU by ``device_normal`` /
+    ``device_uniform`` with a seeded device generator, directly in the storage dtype; the
+    oracle reads the sampled rows back from the same stored values.
 
 Shapes follow the pages' workloads: the GPT-2 training shapes B=32, T=256, C=256, H=8 of
 "FastTransformer: Breaking the Compiler Ceiling ..." (section 1), the row-length template
@@ -54,6 +57,21 @@ def normal(shape, seed: int, mean: float = 0.0, var: float = 1.0) -> torch.Tenso
     if mean != 0.0:
         t.add_(mean)
     return t
+
+
+def device_normal(shape, seed: int, dtype, device, std: float = 1.0) -> torch.Tensor:
+    """Seeded N(0, std^2) drawn on `device` in `dtype` (tensors too large to draw on the host)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device=device, dtype=dtype)
+    return t.mul_(std) if std != 1.0 else t
+
+
+def device_uniform(shape, seed: int, lo: float, hi: float, dtype, device) -> torch.Tensor:
+    """Seeded U[lo, hi) drawn on `device` in `dtype`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.rand(shape, generator=g, device=device, dtype=dtype).mul_(hi - lo).add_(lo)
 
 
 def uniform(shape, seed: int, lo: float, hi: float) -> torch.Tensor:
