@@ -13,8 +13,8 @@ cast to the storage dtype; the oracle reads the cast values):
     per-row offset N(0,4) has standard deviation 2 and beta N(0,0.1) has std sqrt(0.1).
   * A valid length "U[a,b]" is an integer drawn uniformly from a..b inclusive, one per
     batch entry; key positions j >= L_b get an additive mask value of -inf, the rest 0.
-  * Tensors beyond 4 GiB (the large-tensor tests) are drawn on the GPU by ``device_normal`` /
-    ``device_uniform`` with a seeded device generator, directly in the storage dtype; the
+  * Tensors beyond 4 GiB (the large-tensor tests) are drawn on the GPU by ``device_normal``,
+    ``device_uniform`` and ``device_bytes`` with a seeded device generator, directly in the storage dtype; the
     oracle reads the sampled rows back from the same stored values.
 
 Shapes follow the pages' workloads: the GPT-2 training shapes B=32, T=256, C=256, H=8 of
@@ -72,6 +72,13 @@ def device_uniform(shape, seed: int, lo: float, hi: float, dtype, device) -> tor
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return torch.rand(shape, generator=g, device=device, dtype=dtype).mul_(hi - lo).add_(lo)
+
+
+def device_bytes(shape, seed: int, device) -> torch.Tensor:
+    """Seeded uniform bytes drawn on `device` (keep-bit masks of the large-tensor tests)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.uint8)
 
 
 def uniform(shape, seed: int, lo: float, hi: float) -> torch.Tensor:

@@ -1,5 +1,6 @@
-"""GPU parity on tensors beyond 4 GiB (through the C ABI): the softmax, LayerNorm and
-cross-entropy kernels address rows past 2^31 elements and past 2^32 bytes.
+"""GPU parity on tensors beyond 4 GiB (through the C ABI): the softmax (dense and read-skipping),
+LayerNorm, bias-dropout-residual LayerNorm and cross-entropy kernels address rows past 2^31
+elements and past 2^32 bytes.
 
 Inputs are drawn on the GPU with seeded device generators (workloads.device_normal /
 device_uniform, in the storage dtype); the oracle runs on sampled rows read back from the
@@ -9,6 +10,7 @@ backward takes seeded inputs of its own (y for the softmax backward, mean/rstd f
 lse for cross-entropy; the formulas are definitions for any such input), so no oracle input
 comes from a GPU output. dgamma/dbeta (sums over every row) are checked on sampled columns.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -144,3 +146,85 @@ def test_cross_entropy_beyond_2_31_elements():
     assert_close(rows_of(dz, idx, V), ref, dtype, "xent dz beyond 2^31")
     del z, dz
     torch.cuda.empty_cache()
+
+
+def test_softmax_skip_beyond_4gib():
+    """The read-skipping forward and backward on the fp16 causal, padded case past 2^31
+    elements. The backward's y is zero wherever the forward's would be (masked keys and
+    future positions), the condition under which it equals the dense backward."""
+    dtype, B, H, T = torch.float16, 2, 260, 2048
+    rows = B * H * T
+    idx = sample_rows(rows, [2 ** 31 // T, H * T], SEED + 70)
+    say(f"skip softmax [{B},{H},{T},{T}]", "draw on device")
+    x = W.device_normal((B, H, T, T), SEED + 71, dtype, DEV, std=4.0)
+    lengths = W.valid_lengths(B, T // 2, T, SEED + 72)
+    mask = W.padding_mask(lengths, T, dtype)
+    y = lnr.attn_softmax_fw_skip(x, mask.to(DEV), True)
+    torch.cuda.synchronize()
+    x_rows, y_rows = rows_of(x, idx, T), rows_of(y, idx, T)
+    del x, y
+    m_rows = mask.double().numpy()[(idx // (H * T)).numpy()]
+    ref = oracle.softmax_fw_rows(x_rows, m_rows, (idx % T).numpy(), True)
+    assert_close(y_rows, ref, dtype, "skip softmax fw beyond 4 GiB")
+
+    say("GPU backward (skipping)")
+    yb = W.device_uniform((B, H, T, T), SEED + 73, 0.0, 1.0, dtype, DEV)
+    j = torch.arange(T, device=DEV)
+    yb.masked_fill_(j.view(1, 1, 1, T) >= lengths.to(DEV).view(B, 1, 1, 1), 0.0)
+    yb.masked_fill_(j.view(1, 1, 1, T) > j.view(1, 1, T, 1), 0.0)
+    dy = W.device_normal((B, H, T, T), SEED + 74, dtype, DEV)
+    dx = lnr.attn_softmax_bw_skip(dy, yb, mask.to(DEV), True)
+    torch.cuda.synchronize()
+    yb_rows, dy_rows, dx_rows = rows_of(yb, idx, T), rows_of(dy, idx, T), rows_of(dx, idx, T)
+    del yb, dy, dx
+    torch.cuda.empty_cache()
+    assert_close(dx_rows, oracle.softmax_bw(yb_rows, dy_rows), dtype, "skip softmax bw beyond 4 GiB")
+
+
+def test_bdr_layernorm_beyond_2_31_elements():
+    """Bias + dropout + residual LayerNorm past 2^31 elements: forward and backward rows, and
+    dgamma/dbeta on sampled columns (dbias, whose rows need full-row sums, is covered at the
+    smaller sizes of the bias-dropout-residual tests)."""
+    dtype, N, C, p = torch.float16, 262147, 8192, 0.1
+    idx = sample_rows(N, [2 ** 31 // C, N // 2], SEED + 80)
+    say(f"bdr layernorm [{N},{C}]", "draw on device")
+    x = W.device_normal((N, C), SEED + 81, dtype, DEV)
+    r = W.device_normal((N, C), SEED + 82, dtype, DEV)
+    keep = W.device_bytes((N, C // 8), SEED + 83, DEV)
+    bias = W.normal((C,), SEED + 84, var=0.1).to(dtype)
+    gamma = W.uniform((C,), SEED + 85, 0.5, 1.5).to(dtype)
+    beta = W.normal((C,), SEED + 86, var=0.1).to(dtype)
+    g64 = gamma.double().numpy()
+    s, y, mean, rstd = lnr.bdr_layernorm_fw(x, r, bias.to(DEV), keep, p, gamma.to(DEV), beta.to(DEV), W.LN_EPS)
+    torch.cuda.synchronize()
+    k_rows = keep.index_select(0, idx.to(DEV)).cpu().numpy()
+    s_ref, y_ref, mean_ref, rstd_ref = oracle.bdr_ln_fw(rows_of(x, idx, C), rows_of(r, idx, C),
+                                                        bias.double().numpy(), k_rows, p, g64,
+                                                        beta.double().numpy(), W.LN_EPS)
+    assert_close(rows_of(s, idx, C), s_ref, dtype, "bdr s beyond 2^31")
+    assert_close(rows_of(y, idx, C), y_ref, dtype, "bdr y beyond 2^31")
+    assert_close(to_host64(mean[idx.to(DEV)]), mean_ref, dtype, "bdr mean beyond 2^31")
+    assert_close(to_host64(rstd[idx.to(DEV)]), rstd_ref, dtype, "bdr rstd beyond 2^31")
+    del x, r, s, y, mean, rstd
+
+    say("GPU backward on a seeded s and statistics")
+    sb = W.device_normal((N, C), SEED + 87, dtype, DEV)
+    ms = W.device_normal((N,), SEED + 88, torch.float32, DEV, std=0.5)
+    rs = W.device_uniform((N,), SEED + 89, 0.5, 1.5, torch.float32, DEV)
+    dy = W.device_normal((N, C), SEED + 90, dtype, DEV)
+    dres, dx, dg, db, _ = lnr.bdr_layernorm_bw(dy, sb, keep, p, gamma.to(DEV), ms, rs)
+    torch.cuda.synchronize()
+    ms64, rs64 = to_host64(ms), to_host64(rs)
+    dres_ref, dx_ref, _, _, _ = oracle.bdr_ln_bw(rows_of(sb, idx, C), rows_of(dy, idx, C), None, k_rows, p,
+                                                 g64, ms64[idx.numpy()], rs64[idx.numpy()])
+    assert_close(rows_of(dres, idx, C), dres_ref, dtype, "bdr dresidual beyond 2^31")
+    assert_close(rows_of(dx, idx, C), dx_ref, dtype, "bdr dx beyond 2^31")
+    cols = torch.tensor([0, 1, 4095, 4096, 8190, 8191, 1234, 5678], dtype=torch.int64)
+    sc = to_host64(sb.index_select(1, cols.to(DEV)))
+    dyc = to_host64(dy.index_select(1, cols.to(DEV)))
+    del sb, dy, dres, dx, keep
+    torch.cuda.empty_cache()
+    ones = np.full((N, 1), 0xFF, np.uint8)     # dgamma and dbeta do not depend on the keep bits
+    _, _, dg_ref, db_ref, _ = oracle.bdr_ln_bw(sc, dyc, None, ones, p, g64[cols.numpy()], ms64, rs64)
+    assert_close(to_host64(dg)[cols.numpy()], dg_ref, dtype, "bdr dgamma beyond 2^31")
+    assert_close(to_host64(db)[cols.numpy()], db_ref, dtype, "bdr dbeta beyond 2^31")
